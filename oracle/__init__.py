@@ -1,0 +1,203 @@
+"""ctypes front end of the fp64 CPU oracle (``pa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this module; the product package never does.  It shares no
+code with the GPU library.  Every function takes host numpy arrays holding the exact bytes
+the GPU side uses (bf16 tensors as ``uint16`` bit patterns, fp32 as ``float32``) and
+returns fp64 results.
+
+Citations for what each function computes live in the header comment of ``pa_oracle.c``
+(aphrodite-engine "xformers.py" and vLLM "cpu_attn" pages of the reference).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "libpa_oracle.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile ``pa_oracle.c`` into ``libpa_oracle.so`` with gcc (plain -O2, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("alibi_slopes", ctypes.c_void_p),
+        ("sliding_window", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.orc_cache_write.argtypes = [ctypes.POINTER(_Layer), P, P, ctypes.c_int64, ctypes.c_int64, P, P]
+        lib.orc_cache_write.restype = ctypes.c_int
+        lib.orc_decode.argtypes = [ctypes.POINTER(_Layer), P, P, ctypes.c_int64, P, P, ctypes.c_int32,
+                                   P, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        lib.orc_decode.restype = ctypes.c_int
+        lib.orc_prefill.argtypes = [ctypes.POINTER(_Layer), P, P, ctypes.c_int64, P, P, ctypes.c_int64, P,
+                                    P, ctypes.c_int32, P, P, ctypes.c_int32, P, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_int)]
+        lib.orc_prefill.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+@dataclass
+class OracleLayer:
+    """Geometry of one attention layer, as the oracle needs it."""
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    num_blocks: int
+    dtype: int                       # DTYPE_F32 or DTYPE_BF16
+    scale: float
+    alibi_slopes: Optional[np.ndarray] = None   # float32 [num_heads]
+    sliding_window: int = 0
+
+    def _c(self):
+        slopes = None
+        if self.alibi_slopes is not None:
+            slopes = np.ascontiguousarray(self.alibi_slopes, dtype=np.float32)
+            assert slopes.shape == (self.num_heads,)
+        c = _Layer(self.num_heads, self.num_kv_heads, self.head_size, self.block_size,
+                   self.num_blocks, self.dtype, float(np.float32(self.scale)),
+                   slopes.ctypes.data if slopes is not None else None,
+                   int(self.sliding_window))
+        return c, slopes   # keep slopes alive while c is used
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise RuntimeError(f"oracle {what} failed with status {status}")
+
+
+def _elt_dtype(layer: OracleLayer):
+    return np.float32 if layer.dtype == DTYPE_F32 else np.uint16
+
+
+def cache_write(layer: OracleLayer, key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarray,
+                kv_cache: np.ndarray) -> None:
+    """In place: scatter key/value rows [T, Hkv*D] into kv_cache through slot_mapping."""
+    et = _elt_dtype(layer)
+    assert key.dtype == et and value.dtype == et and kv_cache.dtype == et
+    assert key.shape == value.shape and key.ndim == 2
+    if key.shape[0] == 0:
+        return
+    key = np.ascontiguousarray(key)
+    value = np.ascontiguousarray(value)
+    assert kv_cache.flags.c_contiguous
+    slot_mapping = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert slot_mapping.shape == (key.shape[0],)
+    c, keep = layer._c()
+    st = _load().orc_cache_write(ctypes.byref(c), _ptr(key), _ptr(value), key.shape[1],
+                                 key.shape[0], _ptr(slot_mapping), _ptr(kv_cache))
+    _check(st, "cache_write")
+
+
+def decode(layer: OracleLayer, query: np.ndarray, kv_cache: np.ndarray, block_tables: np.ndarray,
+           seq_lens: np.ndarray, num_threads: int = 0, return_threads: bool = False):
+    """fp64 [B, H, D] decode output (see ``orc_decode`` in pa_oracle.c)."""
+    et = _elt_dtype(layer)
+    assert query.dtype == et and kv_cache.dtype == et and kv_cache.flags.c_contiguous
+    assert query.ndim == 2
+    query = np.ascontiguousarray(query)
+    B = query.shape[0]
+    block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    assert block_tables.ndim == 2 and block_tables.shape[0] == B and seq_lens.shape == (B,)
+    out = np.empty((B, layer.num_heads, layer.head_size), dtype=np.float64)
+    c, keep = layer._c()
+    used = ctypes.c_int(0)
+    st = _load().orc_decode(ctypes.byref(c), _ptr(out), _ptr(query), query.shape[1],
+                            _ptr(kv_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B,
+                            num_threads, ctypes.byref(used))
+    _check(st, "decode")
+    return (out, used.value) if return_threads else out
+
+
+def prefill(layer: OracleLayer, query: np.ndarray, key: np.ndarray, value: np.ndarray,
+            kv_cache: Optional[np.ndarray], block_tables: Optional[np.ndarray],
+            context_lens: Optional[np.ndarray], cu_subquery: np.ndarray,
+            row_select: Optional[np.ndarray] = None, num_threads: int = 0,
+            return_threads: bool = False):
+    """fp64 [T, H, D] prefill output (see ``orc_prefill`` in pa_oracle.c).
+
+    Rows not selected by ``row_select`` (bool [T]) are returned as NaN.
+    """
+    et = _elt_dtype(layer)
+    assert query.dtype == et and key.dtype == et and value.dtype == et
+    assert query.ndim == 2 and key.ndim == 2 and key.shape == value.shape
+    query = np.ascontiguousarray(query)
+    key = np.ascontiguousarray(key)
+    value = np.ascontiguousarray(value)
+    T = query.shape[0]
+    assert key.shape[0] == T
+    cu = np.ascontiguousarray(cu_subquery, dtype=np.int32)
+    N = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T
+    if context_lens is not None:
+        context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+        assert context_lens.shape == (N,)
+    maxb = 0
+    if block_tables is not None:
+        block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+        assert block_tables.ndim == 2 and block_tables.shape[0] == N
+        maxb = block_tables.shape[1]
+    if kv_cache is not None:
+        assert kv_cache.dtype == et and kv_cache.flags.c_contiguous
+    sel = None
+    if row_select is not None:
+        sel = np.ascontiguousarray(row_select, dtype=np.uint8)
+        assert sel.shape == (T,)
+    out = np.full((T, layer.num_heads, layer.head_size), np.nan, dtype=np.float64)
+    c, keep = layer._c()
+    used = ctypes.c_int(0)
+    st = _load().orc_prefill(ctypes.byref(c), _ptr(out), _ptr(query), query.shape[1],
+                             _ptr(key), _ptr(value), key.shape[1], _ptr(kv_cache),
+                             _ptr(block_tables), maxb, _ptr(context_lens), _ptr(cu), N, _ptr(sel),
+                             num_threads, ctypes.byref(used))
+    _check(st, "prefill")
+    return (out, used.value) if return_threads else out
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

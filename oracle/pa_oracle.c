@@ -1,0 +1,338 @@
+/*
+ * pa_oracle.c -- plain, slow, fp64 CPU oracle for attention over a paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or calls this
+ * file; only the tests, the smoke check and the benchmark's CPU-baseline leg use it.  It
+ * shares no source, header, table or helper with the GPU library.
+ *
+ * What it computes, and where each step comes from (the three pages of the reference):
+ *
+ *  - Cache layout.  Both pages give the paged cache the shape
+ *    [2, num_blocks, block_size * num_kv_heads * head_size] (aphrodite-engine
+ *    "xformers.py", XFormersImpl.forward docstring; vLLM "cpu_attn",
+ *    TorchSDPABackendImpl.forward docstring).  Plane 0 holds keys, plane 1 values.  The
+ *    order of the elements inside one block is not printed anywhere; this oracle reads
+ *    the flat factor list literally, row-major [block_size][num_kv_heads][head_size].
+ *    That choice is a contract, not something the pages pin.
+ *
+ *  - Slot mapping.  A token's slot s lives in block s / block_size at offset
+ *    s % block_size (vLLM "cpu_attn", TorchSDPAMetadata.slot_mapping comment and its
+ *    worked example).  A negative slot marks a padded token that is not written.
+ *
+ *  - Block tables.  Row i maps logical block n of sequence i to a physical block
+ *    (vLLM "cpu_attn", TorchSDPAMetadata.decode_block_tables comment).
+ *
+ *  - Lengths.  In decode, the sequence length counts the new token, whose K/V is already
+ *    in the cache; in prefill, context_len counts only cached tokens before the new
+ *    subquery tokens (aphrodite-engine "xformers.py", XFormersMetadata NOTE/WARNING).
+ *
+ *  - Grouped-query heads: query head h reads KV head h / (H / Hkv)
+ *    (aphrodite-engine "xformers.py", _run_memory_efficient_xformers_forward view into
+ *    [Hkv, H/Hkv]; vLLM "cpu_attn", _run_sdpa_forward repeat_interleave).
+ *
+ *  - Scores: scale * <q, k_j>, plus slope_h * (j - pos) when ALiBi slopes are given
+ *    (aphrodite-engine "xformers.py", _make_alibi_bias: bias is key index minus query
+ *    index, times the head's slope, added to the scaled logits).  Key j is visible to
+ *    the query at absolute position pos when j <= pos (causal) and, with a sliding
+ *    window W > 0, when pos - j < W.  The pages never print the window helper; "W keys
+ *    including the query's own" is this oracle's reading.  ALiBi and the window are
+ *    both applied when both are given (the pages drop the window under ALiBi; the
+ *    built method takes both).
+ *
+ *  - Softmax attention in fp64: m = max s_j, p_j = exp(s_j - m), out = sum p_j v_j /
+ *    sum p_j (vLLM "cpu_attn", _run_sdpa_forward, scaled_dot_product_attention).
+ *
+ * Inputs are promoted exactly to double: fp32 directly, bf16 by placing its 16 bits in
+ * the high half of an fp32.  Outputs are double.  Element types: 0 = fp32, 1 = bf16.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_BAD_ARG 1
+#define ORC_BAD_INDEX 2
+#define ORC_NO_MEMORY 3
+
+typedef struct {
+    int32_t num_heads;      /* H */
+    int32_t num_kv_heads;   /* Hkv, divides H */
+    int32_t head_size;      /* D */
+    int32_t block_size;     /* tokens per cache block */
+    int64_t num_blocks;     /* physical blocks in each plane */
+    int32_t dtype;          /* 0 = fp32, 1 = bf16 */
+    float scale;            /* multiplies <q, k> */
+    const float *alibi_slopes; /* [H] or NULL */
+    int32_t sliding_window; /* <= 0: no window */
+} orc_layer;
+
+static int elt_bytes(int32_t dtype) { return dtype == 0 ? 4 : 2; }
+
+/* Exact promotion of one stored element to double. */
+static double elt_to_double(const void *base, int64_t idx, int32_t dtype)
+{
+    if (dtype == 0) {
+        return (double)((const float *)base)[idx];
+    } else {
+        uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+}
+
+/* Element offset, inside one cache plane, of (block, offset-in-block, kv head, dim). */
+static int64_t cache_index(const orc_layer *L, int64_t block, int64_t offset, int64_t g, int64_t d)
+{
+    return ((block * L->block_size + offset) * L->num_kv_heads + g) * L->head_size + d;
+}
+
+static int layer_ok(const orc_layer *L)
+{
+    if (!L || L->num_heads <= 0 || L->num_kv_heads <= 0 || L->head_size <= 0 || L->block_size <= 0)
+        return 0;
+    if (L->num_heads % L->num_kv_heads != 0) return 0;
+    if (L->dtype != 0 && L->dtype != 1) return 0;
+    if (L->num_blocks < 0) return 0;
+    return 1;
+}
+
+/*
+ * Cache write: for every token t whose slot s = slot_mapping[t] is >= 0, copy the bits of
+ * key row t into the key plane at (s / block_size, s % block_size) and the bits of value
+ * row t into the value plane at the same place.  key/value rows are num_kv_heads *
+ * head_size elements long and row_stride elements apart.
+ */
+int orc_cache_write(const orc_layer *L, const void *key, const void *value, int64_t row_stride,
+                    int64_t num_tokens, const int64_t *slot_mapping, void *kv_cache)
+{
+    if (!layer_ok(L) || num_tokens < 0) return ORC_BAD_ARG;
+    const int eb = elt_bytes(L->dtype);
+    const int64_t plane = L->num_blocks * L->block_size * L->num_kv_heads * L->head_size;
+    const int64_t row = (int64_t)L->num_kv_heads * L->head_size;
+    char *kc = (char *)kv_cache;
+    char *vc = kc + plane * eb;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        if (s < 0) continue;
+        int64_t block = s / L->block_size;
+        int64_t offset = s % L->block_size;
+        if (block >= L->num_blocks) return ORC_BAD_INDEX;
+        for (int64_t g = 0; g < L->num_kv_heads; ++g) {
+            for (int64_t d = 0; d < L->head_size; ++d) {
+                int64_t src = t * row_stride + g * L->head_size + d;
+                int64_t dst = cache_index(L, block, offset, g, d);
+                memcpy(kc + dst * eb, (const char *)key + src * eb, eb);
+                memcpy(vc + dst * eb, (const char *)value + src * eb, eb);
+            }
+        }
+    }
+    (void)row;
+    return ORC_OK;
+}
+
+/*
+ * Un-page the first n tokens of one sequence for KV head g: logical token j lives in
+ * physical block table_row[j / block_size] at offset j % block_size.  Writes n x D
+ * doubles to K and V.
+ */
+static int unpage(const orc_layer *L, const void *kv_cache, const int32_t *table_row, int64_t n,
+                  int64_t g, double *K, double *V)
+{
+    const int64_t plane = L->num_blocks * L->block_size * L->num_kv_heads * L->head_size;
+    const char *kc = (const char *)kv_cache;
+    const char *vc = kc + plane * elt_bytes(L->dtype);
+    for (int64_t j = 0; j < n; ++j) {
+        int64_t block = table_row[j / L->block_size];
+        int64_t offset = j % L->block_size;
+        if (block < 0 || block >= L->num_blocks) return ORC_BAD_INDEX;
+        for (int64_t d = 0; d < L->head_size; ++d) {
+            int64_t idx = cache_index(L, block, offset, g, d);
+            K[j * L->head_size + d] = elt_to_double(kc, idx, L->dtype);
+            V[j * L->head_size + d] = elt_to_double(vc, idx, L->dtype);
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * One query row of masked softmax attention.  K and V hold the sequence's keys and values
+ * for this KV head, indexed by absolute token position 0 .. pos.  q is D doubles.  Writes
+ * D doubles to out.
+ */
+static void attend_row(const orc_layer *L, const double *q, const double *K, const double *V,
+                       int64_t pos, double slope, int has_alibi, double *out)
+{
+    const int64_t D = L->head_size;
+    const int64_t W = L->sliding_window;
+    const int64_t first = (W > 0 && pos - W + 1 > 0) ? pos - W + 1 : 0;
+    const int64_t n = pos - first + 1;
+    double *s = (double *)malloc((size_t)n * sizeof(double));
+    /* scores */
+    double m = -INFINITY;
+    for (int64_t j = first; j <= pos; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += q[d] * K[j * D + d];
+        double sj = (double)L->scale * dot;
+        if (has_alibi) sj += slope * (double)(j - pos);
+        s[j - first] = sj;
+        if (sj > m) m = sj;
+    }
+    /* softmax-weighted sum of values */
+    double denom = 0.0;
+    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+    for (int64_t j = first; j <= pos; ++j) {
+        double p = exp(s[j - first] - m);
+        denom += p;
+        for (int64_t d = 0; d < D; ++d) out[d] += p * V[j * D + d];
+    }
+    for (int64_t d = 0; d < D; ++d) out[d] /= denom;
+    free(s);
+}
+
+static int set_threads(int num_threads)
+{
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+    return omp_get_max_threads();
+#else
+    (void)num_threads;
+    return 1;
+#endif
+}
+
+/*
+ * Single-token decode.  query row i ([H * D], row stride q_stride elements) attends to the
+ * first seq_lens[i] tokens of sequence i, the last of which is the query's own position.
+ * seq_lens[i] == 0 is a padded row and gives zeros.  out is [num_seqs, H, D] doubles.
+ * Returns ORC_OK or an error code; *threads_used gets the thread count.
+ */
+int orc_decode(const orc_layer *L, double *out, const void *query, int64_t q_stride,
+               const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+               const int32_t *seq_lens, int32_t num_seqs, int num_threads, int *threads_used)
+{
+    if (!layer_ok(L) || num_seqs < 0) return ORC_BAD_ARG;
+    int nt = set_threads(num_threads);
+    if (threads_used) *threads_used = nt;
+    const int64_t H = L->num_heads, Hkv = L->num_kv_heads, D = L->head_size;
+    const int64_t G = H / Hkv;
+    int status = ORC_OK;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        if (seq_lens[i] < 0 || (int64_t)seq_lens[i] > (int64_t)max_blocks_per_seq * L->block_size)
+            return ORC_BAD_INDEX;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t work = 0; work < (int64_t)num_seqs * Hkv; ++work) {
+        const int64_t i = work / Hkv, g = work % Hkv;
+        const int64_t n = seq_lens[i];
+        if (n == 0) {
+            for (int64_t h = g * G; h < (g + 1) * G; ++h)
+                for (int64_t d = 0; d < D; ++d) out[(i * H + h) * D + d] = 0.0;
+            continue;
+        }
+        double *K = (double *)malloc((size_t)(n * D) * sizeof(double));
+        double *V = (double *)malloc((size_t)(n * D) * sizeof(double));
+        double *q = (double *)malloc((size_t)D * sizeof(double));
+        if (!K || !V || !q) {
+#pragma omp atomic write
+            status = ORC_NO_MEMORY;
+            free(K); free(V); free(q);
+            continue;
+        }
+        int st = unpage(L, kv_cache, block_tables + i * max_blocks_per_seq, n, g, K, V);
+        if (st != ORC_OK) {
+#pragma omp atomic write
+            status = st;
+        } else {
+            for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                for (int64_t d = 0; d < D; ++d) q[d] = elt_to_double(query, i * q_stride + h * D + d, L->dtype);
+                double slope = L->alibi_slopes ? (double)L->alibi_slopes[h] : 0.0;
+                attend_row(L, q, K, V, n - 1, slope, L->alibi_slopes != NULL, out + (i * H + h) * D);
+            }
+        }
+        free(K); free(V); free(q);
+    }
+    return status;
+}
+
+/*
+ * Variable-length causal prefill with a cached context.  Sequence i has context_lens[i]
+ * cached tokens (reached through its block-table row) followed by the
+ * n_i = cu_subquery[i+1] - cu_subquery[i] new tokens whose query/key/value rows are
+ * cu_subquery[i] .. cu_subquery[i+1]-1 of the flattened inputs.  New token t of
+ * sequence i sits at position c_i + t and attends to positions 0 .. c_i + t; keys below
+ * c_i come from the cache, the rest from the key/value rows.  context_lens == NULL means
+ * no cached context.  out is [num_tokens, H, D] doubles.  If row_select is non-NULL, only
+ * rows with row_select[row] != 0 are computed (others are left untouched).
+ */
+int orc_prefill(const orc_layer *L, double *out, const void *query, int64_t q_stride,
+                const void *key, const void *value, int64_t kv_stride, const void *kv_cache,
+                const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *context_lens, const int32_t *cu_subquery, int32_t num_seqs,
+                const uint8_t *row_select, int num_threads, int *threads_used)
+{
+    if (!layer_ok(L) || num_seqs < 0) return ORC_BAD_ARG;
+    int nt = set_threads(num_threads);
+    if (threads_used) *threads_used = nt;
+    const int64_t H = L->num_heads, Hkv = L->num_kv_heads, D = L->head_size;
+    const int64_t G = H / Hkv;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        int64_t c = context_lens ? context_lens[i] : 0;
+        if (c < 0 || cu_subquery[i + 1] < cu_subquery[i]) return ORC_BAD_ARG;
+        if (c > 0 && (!block_tables || c > (int64_t)max_blocks_per_seq * L->block_size))
+            return ORC_BAD_INDEX;
+    }
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t work = 0; work < (int64_t)num_seqs * Hkv; ++work) {
+        const int64_t i = work / Hkv, g = work % Hkv;
+        const int64_t c = context_lens ? context_lens[i] : 0;
+        const int64_t start = cu_subquery[i];
+        const int64_t n_new = cu_subquery[i + 1] - start;
+        if (n_new == 0) continue;
+        int any = 0;
+        for (int64_t t = 0; t < n_new; ++t)
+            if (!row_select || row_select[start + t]) { any = 1; break; }
+        if (!any) continue;
+        const int64_t total = c + n_new;
+        double *K = (double *)malloc((size_t)(total * D) * sizeof(double));
+        double *V = (double *)malloc((size_t)(total * D) * sizeof(double));
+        double *q = (double *)malloc((size_t)D * sizeof(double));
+        if (!K || !V || !q) {
+#pragma omp atomic write
+            status = ORC_NO_MEMORY;
+            free(K); free(V); free(q);
+            continue;
+        }
+        int st = ORC_OK;
+        /* cached context, un-paged through the block table */
+        if (c > 0) st = unpage(L, kv_cache, block_tables + i * max_blocks_per_seq, c, g, K, V);
+        /* new tokens, straight from the key/value rows */
+        for (int64_t t = 0; t < n_new; ++t)
+            for (int64_t d = 0; d < D; ++d) {
+                K[(c + t) * D + d] = elt_to_double(key, (start + t) * kv_stride + g * D + d, L->dtype);
+                V[(c + t) * D + d] = elt_to_double(value, (start + t) * kv_stride + g * D + d, L->dtype);
+            }
+        if (st != ORC_OK) {
+#pragma omp atomic write
+            status = st;
+        } else {
+            for (int64_t t = 0; t < n_new; ++t) {
+                if (row_select && !row_select[start + t]) continue;
+                for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                    for (int64_t d = 0; d < D; ++d)
+                        q[d] = elt_to_double(query, (start + t) * q_stride + h * D + d, L->dtype);
+                    double slope = L->alibi_slopes ? (double)L->alibi_slopes[h] : 0.0;
+                    attend_row(L, q, K, V, c + t, slope, L->alibi_slopes != NULL,
+                               out + ((start + t) * H + h) * D);
+                }
+            }
+        }
+        free(K); free(V); free(q);
+    }
+    return status;
+}

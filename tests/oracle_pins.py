@@ -1,0 +1,389 @@
+"""Checks that pin the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with:
+  * a worked example printed on the reference pages (fixtures under tests/golden/),
+  * an independent library routine (torch's scaled_dot_product_attention in fp64, fed with
+    contiguous K/V rebuilt from the generator's rows -- never from the oracle's cache),
+  * a closed form (window of one key, a single key, a zero query), or
+  * an invariance the method must have (relabelled physical blocks, GQA as repeated KV
+    heads, decode as the last row of prefill, chunked prefill as rows of full prefill).
+
+``tests/test_oracle.py`` runs them against the real oracle; ``tests/test_oracle_mutants.py``
+runs them against copies of the oracle with planted mistakes and expects failures.
+"""
+from __future__ import annotations
+
+import dataclasses
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+# ------------------------------------------------------------------------------ helpers
+
+def oracle_layer(layer: wl.LayerSpec) -> oracle.OracleLayer:
+    return oracle.OracleLayer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size,
+                              layer.num_blocks, oracle.DTYPE_F32 if layer.dtype == wl.F32 else oracle.DTYPE_BF16,
+                              layer.scale, layer.alibi_slopes, layer.sliding_window)
+
+
+def nan_pool(layer: wl.LayerSpec) -> np.ndarray:
+    shape = (2, layer.num_blocks, layer.block_size * layer.num_kv_heads * layer.head_size)
+    if layer.dtype == wl.F32:
+        return np.full(shape, np.nan, dtype=np.float32)
+    return np.full(shape, NAN_BF16, dtype=np.uint16)
+
+
+def oracle_cache(batch: wl.PagedBatch) -> np.ndarray:
+    """The oracle's own pool: NaN everywhere, then context rows and new rows written by the
+    oracle's cache write (as the backends write new K/V before attending)."""
+    ol = oracle_layer(batch.layer)
+    pool = nan_pool(batch.layer)
+    oracle.cache_write(ol, wl.host_bits(batch.ctx_key), wl.host_bits(batch.ctx_value), batch.ctx_slots, pool)
+    oracle.cache_write(ol, wl.host_bits(batch.key), wl.host_bits(batch.value), batch.slot_mapping, pool)
+    return pool
+
+
+def f64(t: torch.Tensor) -> torch.Tensor:
+    return t.detach().to("cpu").to(torch.float64)
+
+
+def seq_rows(batch: wl.PagedBatch):
+    """Contiguous K/V [n, Hkv, D] (fp64 torch) and the new-token query rows of every
+    sequence, rebuilt from the generator's row tensors in the order the generator emits
+    them (prefill contexts, then decode contexts), without any cache."""
+    L = batch.layer
+    Hkv, D, H = L.num_kv_heads, L.head_size, L.num_heads
+    ck, cv = f64(batch.ctx_key), f64(batch.ctx_value)
+    k, v, q = f64(batch.key), f64(batch.value), f64(batch.query)
+    out = []
+    cpos = 0
+    for i in range(len(batch.prefill_context_lens)):
+        c = int(batch.prefill_context_lens[i])
+        s, e = int(batch.prefill_cu[i]), int(batch.prefill_cu[i + 1])
+        K = torch.cat([ck[cpos:cpos + c], k[s:e]]).view(-1, Hkv, D)
+        V = torch.cat([cv[cpos:cpos + c], v[s:e]]).view(-1, Hkv, D)
+        out.append(("prefill", i, c, K, V, q[s:e].view(-1, H, D), slice(s, e)))
+        cpos += c
+    tp = batch.num_prefill_tokens
+    for i in range(len(batch.decode_seq_lens)):
+        n = int(batch.decode_seq_lens[i])
+        if n == 0:
+            out.append(("decode", i, 0, None, None, q[tp + i:tp + i + 1].view(-1, H, D), slice(tp + i, tp + i + 1)))
+            continue
+        K = torch.cat([ck[cpos:cpos + n - 1], k[tp + i:tp + i + 1]]).view(-1, Hkv, D)
+        V = torch.cat([cv[cpos:cpos + n - 1], v[tp + i:tp + i + 1]]).view(-1, Hkv, D)
+        out.append(("decode", i, n - 1, K, V, q[tp + i:tp + i + 1].view(-1, H, D), slice(tp + i, tp + i + 1)))
+        cpos += n - 1
+    return out
+
+
+def sdpa_reference(layer: wl.LayerSpec, K, V, Q, first_pos: int, bias_form: str = "hf"):
+    """torch scaled_dot_product_attention in fp64 for query rows at positions
+    first_pos .. first_pos + len(Q) - 1 over keys 0 .. len(K) - 1.  GQA by repeat_interleave
+    of KV heads; ALiBi as an additive float mask in the row-constant-shifted form
+    slope * j ("hf") or slope * (j - i) ("paper"); window and causality as -inf."""
+    H = layer.num_heads
+    G = H // layer.num_kv_heads
+    n_q, n_k = Q.shape[0], K.shape[0]
+    Kr = K.permute(1, 0, 2).repeat_interleave(G, dim=0)        # [H, n_k, D]
+    Vr = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    Qr = Q.permute(1, 0, 2)                                     # [H, n_q, D]
+    pos = torch.arange(first_pos, first_pos + n_q, dtype=torch.float64)[:, None]
+    j = torch.arange(n_k, dtype=torch.float64)[None, :]
+    allowed = j <= pos
+    if layer.sliding_window and layer.sliding_window > 0:
+        allowed = allowed & (pos - j < layer.sliding_window)
+    mask = torch.zeros(H, n_q, n_k, dtype=torch.float64)
+    if layer.alibi_slopes is not None:
+        slopes = torch.tensor(layer.alibi_slopes.astype(np.float64))[:, None, None]
+        mask = mask + slopes * ((j - pos) if bias_form == "paper" else j)[None]
+    mask = mask.masked_fill(~allowed[None], float("-inf"))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        Qr[None], Kr[None], Vr[None], attn_mask=mask[None], dropout_p=0.0, scale=float(layer.scale))
+    return out[0].permute(1, 0, 2).numpy()                      # [n_q, H, D]
+
+
+def run_oracle(batch: wl.PagedBatch, pool=None):
+    """Oracle outputs for the whole batch: (prefill [Tp, H, D], decode [Bd, H, D])."""
+    ol = oracle_layer(batch.layer)
+    pool = oracle_cache(batch) if pool is None else pool
+    q = wl.host_bits(batch.query)
+    k = wl.host_bits(batch.key)
+    v = wl.host_bits(batch.value)
+    tp = batch.num_prefill_tokens
+    pre = dec = None
+    if len(batch.prefill_context_lens):
+        pre = oracle.prefill(ol, q[:tp], k[:tp], v[:tp], pool, batch.prefill_block_tables,
+                             batch.prefill_context_lens, batch.prefill_cu)
+    if len(batch.decode_seq_lens):
+        dec = oracle.decode(ol, q[tp:], pool, batch.decode_block_tables, batch.decode_seq_lens)
+    return pre, dec
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+def _layer(H, Hkv, D, bs, dtype=wl.F32, alibi=False, window=0, scale=None):
+    return wl.LayerSpec(H, Hkv, D, bs, 0, dtype, wl.fp32(scale if scale is not None else 1.0 / np.sqrt(D)),
+                        alibi_slopes=wl.alibi_slopes_geometric(H) if alibi else None, sliding_window=window)
+
+
+# ------------------------------------------------------------------------------ pins
+
+def pin_slot_worked_example():
+    """Slots [35, 2, 17] at block size 16 land in (block, offset) (2,3), (0,2), (1,1)."""
+    ex = json.load(open(os.path.join(GOLDEN, "slot_mapping_example.json")))
+    bs = ex["block_size"]
+    ol = oracle.OracleLayer(1, 1, 2, bs, 3, oracle.DTYPE_F32, 1.0)
+    key = np.array([[10.0, 11.0], [20.0, 21.0], [30.0, 31.0]], dtype=np.float32)
+    value = -key
+    pool = np.zeros((2, 3, bs * 2), dtype=np.float32)
+    oracle.cache_write(ol, key, value, np.array(ex["slot_mapping"]), pool)
+    written = np.argwhere(pool[0] != 0)
+    for t, (b, o) in enumerate(ex["expected_block_offset"]):
+        assert np.array_equal(pool[0, b, o * 2:o * 2 + 2], key[t]), f"token {t} key not at block {b} offset {o}"
+        assert np.array_equal(pool[1, b, o * 2:o * 2 + 2], value[t]), f"token {t} value not at block {b} offset {o}"
+    assert len(written) == 6, "cache write touched other slots"
+
+
+def pin_negative_slot_skipped():
+    ol = oracle.OracleLayer(1, 1, 2, 4, 2, oracle.DTYPE_F32, 1.0)
+    pool = np.zeros((2, 2, 8), dtype=np.float32)
+    key = np.ones((2, 2), dtype=np.float32)
+    oracle.cache_write(ol, key, key, np.array([-1, 5]), pool)
+    assert np.count_nonzero(pool) == 4 and np.all(pool[:, 1, 2:4] == 1.0)
+
+
+def pin_start_loc_worked_example():
+    """Start locations of lengths [4, 6] are [0, 4, 10], and a two-prompt flat batch with
+    those starts gives each prompt's own attention."""
+    ex = json.load(open(os.path.join(GOLDEN, "start_loc_example.json")))
+    cu = wl.cumulative_starts(ex["lengths"])
+    assert cu.tolist() == ex["expected_start_loc"]
+    layer = _layer(2, 1, 8, 4)
+    both = wl.make_batch(layer, seed=11, prefill=[(0, 4), (0, 6)])
+    assert both.prefill_cu.tolist() == ex["expected_start_loc"]
+    pre, _ = run_oracle(both)
+    for i, (s, e) in enumerate([(0, 4), (4, 10)]):
+        one = wl.make_batch(layer, seed=11, prefill=[(0, e - s)])
+        ol = oracle_layer(one.layer)
+        alone = oracle.prefill(ol, wl.host_bits(both.query[s:e]), wl.host_bits(both.key[s:e]),
+                               wl.host_bits(both.value[s:e]), None, None, None, np.array([0, e - s]))
+        _close(pre[s:e], alone, 0.0, f"prompt {i} alone vs in flat batch")
+
+
+def pin_identity_block_table():
+    """With the identity table [0, 1, 2] the paged sequence equals its contiguous rows:
+    decode over it matches SDPA over the contiguous rows."""
+    ex = json.load(open(os.path.join(GOLDEN, "block_table_example.json")))
+    bs = ex["block_size"]
+    n = len(ex["block_table"]) * bs
+    layer = _layer(4, 2, 8, bs)
+    layer = dataclasses.replace(layer, num_blocks=len(ex["block_table"]))
+    g = torch.Generator().manual_seed(5)
+    K = torch.randn(n, 2 * 8, generator=g)
+    V = torch.randn(n, 2 * 8, generator=g)
+    Q = torch.randn(1, 4 * 8, generator=g)
+    ol = oracle_layer(layer)
+    pool = np.zeros((2, layer.num_blocks, bs * 16), dtype=np.float32)
+    # contiguous storage: token p at slot p of the identity table
+    oracle.cache_write(ol, K.numpy(), V.numpy(), np.arange(n), pool)
+    out = oracle.decode(ol, Q.numpy(), pool, np.array([ex["block_table"]]), np.array([n]))
+    ref = sdpa_reference(layer, f64(K).view(n, 2, 8), f64(V).view(n, 2, 8), f64(Q).view(1, 4, 8), n - 1)
+    _close(out, ref, 1e-12, "identity block table vs contiguous SDPA")
+
+
+def _sdpa_batch_check(layer, prefill, decode, seed, tol=1e-12, bias_form="hf"):
+    batch = wl.make_batch(layer, seed=seed, prefill=prefill, decode=decode)
+    pre, dec = run_oracle(batch)
+    for kind, i, c, K, V, Q, rows in seq_rows(batch):
+        if K is None:
+            continue
+        ref = sdpa_reference(batch.layer, K, V, Q, c, bias_form)
+        got = pre[rows] if kind == "prefill" else dec[i:i + 1]
+        _close(got, ref, tol, f"{kind} seq {i} vs SDPA (H={layer.num_heads}, Hkv={layer.num_kv_heads}, "
+                              f"bs={layer.block_size}, alibi={layer.alibi_slopes is not None}, "
+                              f"W={layer.sliding_window})")
+
+
+def pin_sdpa_causal_gqa():
+    """Causal prefill and decode, GQA 4:1 and 2:1 and MHA, against fp64 SDPA."""
+    for (H, Hkv) in [(4, 4), (4, 2), (8, 2), (4, 1)]:
+        for bs in (1, 4, 16):
+            _sdpa_batch_check(_layer(H, Hkv, 8, bs), prefill=[(0, 7), (0, bs + 1)], decode=[1, bs, bs + 1, 3 * bs - 1],
+                              seed=100 + H * 10 + Hkv + bs)
+
+
+def pin_sdpa_chunked_context():
+    """Subquery rows over a cached context (chunked prefill), against SDPA over the whole
+    contiguous sequence."""
+    for bs in (2, 16):
+        _sdpa_batch_check(_layer(4, 2, 16, bs), prefill=[(5, 3), (bs, bs), (2 * bs + 1, 4), (0, 1)],
+                          decode=[], seed=200 + bs)
+
+
+def pin_sdpa_alibi():
+    """ALiBi: the oracle's slope * (j - pos) bias against SDPA with the shifted slope * j
+    mask (the two forms give the same attention) and with slope * (j - i)."""
+    for form in ("hf", "paper"):
+        _sdpa_batch_check(_layer(4, 2, 8, 4, alibi=True), prefill=[(0, 9), (6, 5)], decode=[1, 7, 13],
+                          seed=300, bias_form=form)
+    # large-magnitude slopes make a sign error visible even over few keys
+    layer = _layer(2, 1, 8, 4, alibi=True)
+    layer = dataclasses.replace(layer, alibi_slopes=np.array([1.5, 0.25], dtype=np.float32))
+    _sdpa_batch_check(layer, prefill=[(3, 6)], decode=[5, 11], seed=301)
+
+
+def pin_sdpa_window():
+    """Sliding window (W keys including the query's own), alone and with ALiBi."""
+    for W in (1, 2, 3, 5):
+        _sdpa_batch_check(_layer(4, 2, 8, 4, window=W), prefill=[(0, 9), (6, 5)], decode=[1, 4, 10], seed=400 + W)
+        _sdpa_batch_check(_layer(4, 4, 8, 2, window=W, alibi=True), prefill=[(3, 4)], decode=[7], seed=410 + W)
+
+
+def pin_window_one_closed_form():
+    """W = 1: each query sees only its own key, so out = v_pos exactly."""
+    layer = _layer(4, 2, 8, 4, window=1, alibi=True)
+    batch = wl.make_batch(layer, seed=500, prefill=[(3, 5)], decode=[6, 1])
+    pre, dec = run_oracle(batch)
+    H, G, D = 4, 2, 8
+    v = f64(batch.value).view(-1, 2, D).numpy()
+    for t in range(batch.num_prefill_tokens):
+        for h in range(H):
+            _close(pre[t, h], v[t, h // G], 0.0, "W=1 prefill")
+    tp = batch.num_prefill_tokens
+    for i in range(2):
+        for h in range(H):
+            _close(dec[i, h], v[tp + i, h // G], 0.0, "W=1 decode")
+
+
+def pin_single_key_closed_form():
+    """A sequence of one token: out = v_0 exactly (decode and prefill)."""
+    layer = _layer(4, 1, 8, 16, alibi=True)
+    batch = wl.make_batch(layer, seed=600, prefill=[(0, 1)], decode=[1])
+    pre, dec = run_oracle(batch)
+    v = f64(batch.value).view(-1, 1, 8).numpy()
+    for h in range(4):
+        _close(pre[0, h], v[0, 0], 0.0, "single-key prefill")
+        _close(dec[0, h], v[1, 0], 0.0, "single-key decode")
+
+
+def pin_zero_query_mean():
+    """q = 0 without ALiBi: every visible key has the same score, so out is the mean of the
+    visible values (window respected)."""
+    for W in (0, 3):
+        layer = _layer(2, 1, 8, 4, window=W)
+        batch = wl.make_batch(layer, seed=700 + W, prefill=[(5, 4)], decode=[9])
+        batch.query.zero_()
+        pre, dec = run_oracle(batch)
+        for kind, i, c, K, V, Q, rows in seq_rows(batch):
+            Vn = V.numpy()
+            n_q = Q.shape[0]
+            for t in range(n_q):
+                pos = c + t
+                lo = max(0, pos - W + 1) if W > 0 else 0
+                mean = Vn[lo:pos + 1, 0].mean(axis=0)
+                got = pre[rows][t] if kind == "prefill" else dec[i]
+                for h in range(2):
+                    _close(got[h], mean, 1e-14, f"zero-query mean ({kind}, W={W})")
+
+
+def pin_block_relabel_invariance():
+    """Relabelling physical blocks (permuting the pool and the tables alike) changes nothing."""
+    layer = _layer(4, 2, 8, 4, alibi=True, window=6)
+    batch = wl.make_batch(layer, seed=800, prefill=[(5, 3), (0, 4)], decode=[9, 2, 12], pool_blocks=20)
+    pool = oracle_cache(batch)
+    pre, dec = run_oracle(batch, pool)
+    perm = np.random.default_rng(3).permutation(batch.layer.num_blocks)   # old id -> new id
+    pool2 = np.empty_like(pool)
+    pool2[:, perm] = pool
+    b2 = dataclasses.replace(batch, prefill_block_tables=perm[batch.prefill_block_tables].astype(np.int32),
+                             decode_block_tables=perm[batch.decode_block_tables].astype(np.int32))
+    pre2, dec2 = run_oracle(b2, pool2)
+    _close(pre2, pre, 0.0, "relabelled blocks (prefill)")
+    _close(dec2, dec, 0.0, "relabelled blocks (decode)")
+
+
+def pin_gqa_equals_repeated_kv():
+    """GQA with G query heads per KV head equals MHA on KV heads repeated G times."""
+    H, Hkv, D, bs = 8, 2, 8, 4
+    G = H // Hkv
+    gqa = wl.make_batch(_layer(H, Hkv, D, bs, alibi=True), seed=900, prefill=[(3, 4)], decode=[6, 9])
+    rep = lambda t: t.view(-1, Hkv, D).repeat_interleave(G, dim=1).reshape(t.shape[0], H * D).contiguous()
+    mha_layer = _layer(H, H, D, bs, alibi=True)
+    mha = wl.make_batch(mha_layer, seed=900, prefill=[(3, 4)], decode=[6, 9])
+    mha = dataclasses.replace(mha, query=gqa.query, key=rep(gqa.key), value=rep(gqa.value),
+                              ctx_key=rep(gqa.ctx_key), ctx_value=rep(gqa.ctx_value),
+                              slot_mapping=gqa.slot_mapping, ctx_slots=gqa.ctx_slots,
+                              prefill_block_tables=gqa.prefill_block_tables,
+                              decode_block_tables=gqa.decode_block_tables,
+                              layer=dataclasses.replace(mha.layer, num_blocks=gqa.layer.num_blocks))
+    p1, d1 = run_oracle(gqa)
+    p2, d2 = run_oracle(mha)
+    _close(p1, p2, 0.0, "GQA vs repeated-KV MHA (prefill)")
+    _close(d1, d2, 0.0, "GQA vs repeated-KV MHA (decode)")
+
+
+def pin_decode_is_last_prefill_row():
+    """Decode of a length-L sequence equals the last row of causal prefill over the same L
+    tokens (here: prefill with the first L-1 tokens cached and one new token)."""
+    layer = _layer(4, 2, 8, 4, alibi=True, window=5)
+    for L in (1, 4, 5, 11):
+        dec_b = wl.make_batch(layer, seed=1000 + L, decode=[L])
+        pool = oracle_cache(dec_b)
+        ol = oracle_layer(dec_b.layer)
+        dec = oracle.decode(ol, wl.host_bits(dec_b.query), pool, dec_b.decode_block_tables, dec_b.decode_seq_lens)
+        pre = oracle.prefill(ol, wl.host_bits(dec_b.query), wl.host_bits(dec_b.key), wl.host_bits(dec_b.value),
+                             pool, dec_b.decode_block_tables, np.array([L - 1]), np.array([0, 1]))
+        _close(dec, pre, 0.0, f"decode vs last prefill row (L={L})")
+
+
+def pin_chunked_equals_full_rows():
+    """Chunked prefill (c cached + n new) gives the last n rows of a full prefill of c+n."""
+    layer = _layer(4, 2, 8, 4, alibi=True, window=7)
+    c, n = 9, 5
+    full = wl.make_batch(layer, seed=1100, prefill=[(0, c + n)])
+    ol = oracle_layer(full.layer)
+    pool = oracle_cache(full)
+    q, k, v = wl.host_bits(full.query), wl.host_bits(full.key), wl.host_bits(full.value)
+    whole = oracle.prefill(ol, q, k, v, pool, full.prefill_block_tables, np.array([0]), np.array([0, c + n]))
+    part = oracle.prefill(ol, q[c:], k[c:], v[c:], pool, full.prefill_block_tables, np.array([c]), np.array([0, n]))
+    _close(part, whole[c:], 0.0, "chunked vs full prefill rows")
+
+
+def pin_padded_decode_row():
+    layer = _layer(2, 1, 8, 4)
+    batch = wl.make_batch(layer, seed=1200, decode=[5, 0, 3])
+    _, dec = run_oracle(batch)
+    assert np.all(dec[1] == 0.0), "padded decode row must be zeros"
+    assert np.all(np.isfinite(dec))
+
+
+def pin_bf16_inputs():
+    """bf16 inputs are promoted exactly: the oracle on bf16 bit patterns equals SDPA on the
+    same values in fp64."""
+    _sdpa_batch_check(_layer(4, 2, 16, 4, dtype=wl.BF16, alibi=True, window=6), prefill=[(4, 6)], decode=[3, 9],
+                      seed=1300)
+
+
+PINS = [
+    pin_slot_worked_example, pin_negative_slot_skipped, pin_start_loc_worked_example, pin_identity_block_table,
+    pin_sdpa_causal_gqa, pin_sdpa_chunked_context, pin_sdpa_alibi, pin_sdpa_window, pin_window_one_closed_form,
+    pin_single_key_closed_form, pin_zero_query_mean, pin_block_relabel_invariance, pin_gqa_equals_repeated_kv,
+    pin_decode_is_last_prefill_row, pin_chunked_equals_full_rows, pin_padded_decode_row, pin_bf16_inputs,
+]

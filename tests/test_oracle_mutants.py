@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that the pins
+catch every one.  The real oracle is never modified: each mutant is a patched copy of
+pa_oracle.c compiled into a temporary library that replaces the loaded one only for the
+duration of one test."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "pa_oracle.c")
+
+# (name, text in pa_oracle.c, replacement)
+MUTANTS = [
+    ("alibi_sign", "sj += slope * (double)(j - pos);", "sj += slope * (double)(pos - j);"),
+    ("alibi_dropped", "if (has_alibi) sj += slope", "if (0) sj += slope"),
+    ("scale_dropped", "double sj = (double)L->scale * dot;", "double sj = dot;"),
+    ("window_off_by_one", "pos - W + 1 > 0) ? pos - W + 1 : 0;", "pos - W > 0) ? pos - W : 0;"),
+    ("slot_offset", "int64_t offset = s % L->block_size;", "int64_t offset = (s + 1) % L->block_size;"),
+    ("table_index", "table_row[j / L->block_size]", "table_row[j % L->block_size]"),
+    ("kv_head_in_unpage", "cache_index(L, block, offset, g, d);\n            K[", "cache_index(L, block, offset, 0, d);\n            K["),
+    ("gqa_map_decode", "for (int64_t h = g * G; h < (g + 1) * G; ++h) {\n                for (int64_t d = 0; d < D; ++d) q[d] = elt_to_double(query, i * q_stride + h * D + d",
+     "for (int64_t h = g * G; h < (g + 1) * G; ++h) {\n                for (int64_t d = 0; d < D; ++d) q[d] = elt_to_double(query, i * q_stride + ((h % Hkv) * G + h / Hkv) * D + d"),
+    ("prefill_local_position", "attend_row(L, q, K, V, c + t, slope", "attend_row(L, q, K, V, t + (c > 0 ? c - 1 : 0), slope"),
+    ("decode_position", "attend_row(L, q, K, V, n - 1, slope", "attend_row(L, q, K, V, n > 1 ? n - 2 : 0, slope"),
+    ("softmax_denominator", "out[d] /= denom;", "out[d] /= (denom + 1e-3);"),
+    ("bf16_promotion", "<< 16;\n        float f;", "<< 15;\n        float f;"),
+    ("value_plane", "const char *vc = kc + plane * elt_bytes(L->dtype);", "const char *vc = kc;"),
+]
+
+
+def _build_mutant(name, old, new, workdir):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutant {name}: anchor text must occur exactly once"
+    path = os.path.join(workdir, f"mut_{name}.c")
+    with open(path, "w") as f:
+        f.write(text.replace(old, new))
+    lib = os.path.join(workdir, f"libmut_{name}.so")
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", path, "-o", lib, "-lm"], check=True)
+    return lib
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(oracle_lib, name, old, new):
+    import ctypes
+    with tempfile.TemporaryDirectory() as d:
+        lib_path = _build_mutant(name, old, new, d)
+        saved_lib, saved_path = oracle._lib, oracle._LIB
+        try:
+            oracle._lib = None
+            oracle._LIB = lib_path
+            oracle._load()
+            caught = []
+            for pin in pins.PINS:
+                try:
+                    pin()
+                except (AssertionError, RuntimeError) as e:
+                    caught.append(pin.__name__)
+            assert caught, f"no pin caught mutant {name}"
+        finally:
+            oracle._lib, oracle._LIB = saved_lib, saved_path
