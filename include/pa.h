@@ -1,0 +1,181 @@
+/*
+ * pa.h -- attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * A plain C ABI: every argument is a scalar, a host pointer to a small struct, or a device
+ * pointer.  The library (libpa.so) never allocates device memory, never synchronizes the
+ * device and never reads device buffers on the host; all work is enqueued on the HIP stream
+ * the caller passes (NULL = the legacy default stream).  Calls are reentrant: the only
+ * global state is a per-device attribute cache and a thread-local error message.
+ *
+ * The problem statement follows the reference pages:
+ *   - query  [num_tokens, num_heads * head_size]
+ *   - key, value [num_tokens, num_kv_heads * head_size]
+ *   - kv_cache [2, num_blocks, block_size * num_kv_heads * head_size]
+ *     (aphrodite-engine "xformers.py", XFormersImpl.forward docstring; vLLM "cpu_attn",
+ *     TorchSDPABackendImpl.forward docstring).
+ *
+ * Cache layout (a contract of this library; the pages print only the flat size): plane 0
+ * holds keys, plane 1 values; inside a plane, element (block b, offset o, kv head g, dim d)
+ * is at ((b * block_size + o) * num_kv_heads + g) * head_size + d, i.e. each block is
+ * row-major [block_size][num_kv_heads][head_size] and one token's K (or V) is one
+ * contiguous row of num_kv_heads * head_size elements.
+ *
+ * Masking and bias, shared by decode and prefill: a query at absolute position pos of its
+ * sequence sees key j when j <= pos and, with sliding_window W > 0, pos - j < W (W keys
+ * including its own).  Scores are scale * <q, k_j>, plus alibi_slopes[h] * (j - pos) when
+ * slopes are given (aphrodite-engine "xformers.py", _make_alibi_bias).  ALiBi and the window
+ * compose.  Query head h reads KV head h / (num_heads / num_kv_heads) (grouped-query
+ * attention; aphrodite-engine "xformers.py", _run_memory_efficient_xformers_forward).
+ *
+ * Numerics: products and softmax in fp32; for bf16 layers the softmax weights are rounded to
+ * bf16 (nearest even) before they multiply V, and outputs are rounded to nearest even.
+ *
+ * Errors: every entry point returns a pa_status and launches nothing when it fails.  Only
+ * host-visible scalars and pointers are validated.  Device contents (slots, block ids,
+ * lengths, start locations) are preconditions; values out of range never cause an access
+ * outside the buffers described here (they are clamped or skipped), but the affected rows'
+ * results are unspecified.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARGUMENT = 1, /* a NULL pointer, a negative size, a misaligned buffer, a bad geometry */
+    PA_ERR_UNSUPPORTED = 2,      /* a head size, block size or dtype this build has no kernel for */
+    PA_ERR_WORKSPACE = 3,        /* decode workspace missing or smaller than pa_decode_workspace_size() */
+    PA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_DTYPE_F32 = 0,
+    PA_DTYPE_BF16 = 1
+} pa_dtype;
+
+/*
+ * Geometry of one attention layer; mirrors the backend constructor of the pages
+ * (num_heads, head_size, scale, num_kv_heads, alibi_slopes, sliding_window).
+ *   num_heads       H, > 0
+ *   num_kv_heads    Hkv, > 0, divides H
+ *   head_size       D: 64 or 128 (others: PA_ERR_UNSUPPORTED)
+ *   block_size      tokens per cache block: a power of two in [8, 256]
+ *   num_blocks      physical blocks per plane, > 0
+ *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16 (the cache, query, key, value and out)
+ *   scale           fp32 multiplier of <q, k>
+ *   alibi_slopes    device fp32 [H], or NULL for no ALiBi
+ *   sliding_window  W; <= 0 disables the window
+ */
+typedef struct pa_layer {
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t head_size;
+    int32_t block_size;
+    int64_t num_blocks;
+    int32_t dtype;
+    float scale;
+    const float *alibi_slopes;
+    int32_t sliding_window;
+} pa_layer;
+
+/*
+ * Cache write: for every token t in [0, num_tokens) with s = slot_mapping[t] >= 0, copy
+ * key row t into the key plane at block s / block_size, offset s % block_size, and value row
+ * t into the value plane at the same place; bits are copied unchanged.  A negative slot is a
+ * padded token and is skipped; a slot >= num_blocks * block_size is skipped too.  Duplicate
+ * slots in one call leave an unspecified one of the rows.
+ * (vLLM "cpu_attn", TorchSDPAMetadata.slot_mapping comment and worked example;
+ * aphrodite-engine "xformers.py", XFormersImpl.forward, write_to_paged_cache.)
+ *   key, value       device [num_tokens, num_kv_heads * head_size], rows kv_row_stride
+ *                    elements apart (>= num_kv_heads * head_size); 16-byte aligned base
+ *                    and row stride
+ *   slot_mapping     device int64 [num_tokens]
+ *   kv_cache         device, the whole [2, num_blocks, ...] cache, 16-byte aligned; mutated
+ *                    in place
+ * num_tokens == 0 returns PA_OK and launches nothing.
+ */
+pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *value, int64_t kv_row_stride,
+                         int64_t num_tokens, const int64_t *slot_mapping, void *kv_cache, void *stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for this batch shape (0 when every sequence
+ * fits one split-KV partition).  Depends only on the layer's head counts, num_seqs and
+ * max_seq_len.  Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len);
+
+/*
+ * Single-token decode.  Row i of query attends, through block_tables row i, to the first
+ * seq_lens[i] tokens of sequence i; seq_lens counts the new token, whose K/V must already be
+ * in the cache, so the query's position is seq_lens[i] - 1.
+ * (aphrodite-engine "xformers.py", XFormersMetadata NOTE on context_len and
+ * XFormersImpl.forward, forward_decode; vLLM "cpu_attn", TorchSDPAMetadata.decode_seq_lens
+ * and decode_block_tables comments.)
+ *   out              device [num_seqs, num_heads * head_size], contiguous, written
+ *   query            device [num_seqs, num_heads * head_size], rows q_row_stride elements
+ *                    apart; 16-byte aligned
+ *   kv_cache         device cache as above, read only
+ *   block_tables     device int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens         device int32 [num_seqs]; 0 marks a padded row, whose output is zeros
+ *   max_seq_len      host upper bound of seq_lens (sizes the split-KV grid; a larger device
+ *                    value is clamped to it and to max_blocks_per_seq * block_size)
+ *   workspace        device scratch of pa_decode_workspace_size() bytes (may be NULL when
+ *                    that is 0); 256-byte aligned; overwritten
+ * Long sequences are cut into partitions processed in parallel; a second kernel merges the
+ * partitions' (max, sum, weighted-V) triples with the log-sum-exp rule.
+ */
+pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                    const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * Variable-length causal prefill with an optional cached context (chunked prefill).
+ * Sequence i owns query/key/value rows cu_subquery[i] .. cu_subquery[i+1]-1 (its subquery
+ * tokens) and has context_lens[i] tokens already in the cache before them.  Subquery token
+ * t sits at position context_lens[i] + t and attends to positions 0 .. that position: keys
+ * below context_lens[i] are read from the cache through block_tables row i, the others from
+ * the key/value rows.
+ * (aphrodite-engine "xformers.py", XFormersMetadata NOTE on context_len / subquery_len /
+ * seqlen and subquery_start_loc, XFormersImpl.forward, forward_prefix and
+ * _run_memory_efficient_xformers_forward; vLLM "cpu_attn", flash_attn_varlen_func call.)
+ *   out              device [num_tokens, num_heads * head_size], contiguous, written
+ *   query            device [num_tokens, ...], rows q_row_stride elements apart
+ *   key, value       device [num_tokens, num_kv_heads * head_size], rows kv_row_stride apart
+ *   kv_cache         device cache, read only; may be NULL when max_context_len == 0
+ *   block_tables     device int32 [num_seqs, max_blocks_per_seq]; may be NULL when
+ *                    max_context_len == 0
+ *   context_lens     device int32 [num_seqs], or NULL for no cached context
+ *   cu_subquery      device int32 [num_seqs + 1]: 0, then cumulative subquery lengths
+ *                    (e.g. lengths [4, 6] give [0, 4, 10]); cu_subquery[num_seqs] == num_tokens
+ *   max_subquery_len host upper bound of the subquery lengths (sizes the grid)
+ *   max_context_len  host upper bound of context_lens (0 when there is no context)
+ * All device pointers 16-byte aligned, row strides multiples of 8 elements.
+ */
+pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                            const void *key, const void *value, int64_t kv_row_stride, const void *kv_cache,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *cu_subquery, int32_t num_seqs,
+                            int64_t num_tokens, int32_t max_subquery_len, int32_t max_context_len,
+                            void *stream);
+
+/* Static text for a status code. */
+const char *pa_status_string(pa_status status);
+
+/* Detail of the last failure on the calling thread ("" when none). */
+const char *pa_last_error_message(void);
+
+/* Library version string. */
+const char *pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,243 @@
+// C ABI of libpa: argument validation, dispatch to the kernels, status codes and messages.
+// Nothing here allocates device memory, synchronizes, or reads device buffers.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pa.h"
+#include "pa_kernels.h"
+
+#define PA_VERSION_STRING "pa 0.1.0 (gfx950)"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+pa_status ok() {
+    g_last_error[0] = '\0';
+    return PA_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int log2_exact(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return (1 << s) == x ? s : -1;
+}
+
+int elt_bytes(int32_t dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+pa_status check_layer(const pa_layer *L, const char *fn) {
+    if (!L) return fail(PA_ERR_INVALID_ARGUMENT, "%s: layer is NULL", fn);
+    if (L->num_heads <= 0 || L->num_kv_heads <= 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_heads (%d) and num_kv_heads (%d) must be positive", fn,
+                    L->num_heads, L->num_kv_heads);
+    if (L->num_heads % L->num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_kv_heads (%d) must divide num_heads (%d)", fn, L->num_kv_heads,
+                    L->num_heads);
+    if (L->dtype != PA_DTYPE_F32 && L->dtype != PA_DTYPE_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (fp32 = 0, bf16 = 1)", fn, L->dtype);
+    if (L->head_size != 64 && L->head_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "%s: head size %d is not supported; supported head sizes are 64 and 128", fn,
+                    L->head_size);
+    const int bs_shift = log2_exact(L->block_size);
+    if (L->block_size < 8 || L->block_size > 256 || bs_shift < 0)
+        return fail(PA_ERR_UNSUPPORTED, "%s: block size %d is not supported (powers of two from 8 to 256)", fn,
+                    L->block_size);
+    if (L->num_blocks <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_blocks must be positive", fn);
+    if (L->num_blocks > (int64_t(1) << 31))
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_blocks %lld exceeds int32 block ids", fn,
+                    (long long)L->num_blocks);
+    if (!(L->scale == L->scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_version(void) { return PA_VERSION_STRING; }
+
+const char *pa_last_error_message(void) { return g_last_error; }
+
+const char *pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+    }
+    return "PA_ERR_UNKNOWN";
+}
+
+pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *value, int64_t kv_row_stride,
+                         int64_t num_tokens, const int64_t *slot_mapping, void *kv_cache, void *stream) {
+    const char *fn = "pa_cache_write";
+    pa_status st = check_layer(layer, fn);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_tokens is negative", fn);
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !slot_mapping || !kv_cache)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: key, value, slot_mapping and kv_cache must be non-NULL", fn);
+    const int eb = elt_bytes(layer->dtype);
+    const int64_t row = int64_t(layer->num_kv_heads) * layer->head_size;
+    if (kv_row_stride < row)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: kv_row_stride %lld < num_kv_heads * head_size %lld", fn,
+                    (long long)kv_row_stride, (long long)row);
+    if (!aligned16(key) || !aligned16(value) || !aligned16(kv_cache) || (kv_row_stride * eb) % 16 != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: key/value/kv_cache must be 16-byte aligned with 16-byte row strides",
+                    fn);
+    pa::CacheWriteParams p;
+    p.key = static_cast<const char *>(key);
+    p.value = static_cast<const char *>(value);
+    p.kv_stride_bytes = kv_row_stride * eb;
+    p.num_tokens = num_tokens;
+    p.slot_mapping = slot_mapping;
+    p.kv_cache = static_cast<char *>(kv_cache);
+    p.num_slots = layer->num_blocks * layer->block_size;
+    p.row_bytes = int32_t(row * eb);
+    p.plane_bytes = p.num_slots * p.row_bytes;
+    hipError_t e = pa::launch_cache_write(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len) {
+    if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0) return 0;
+    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, num_seqs, max_seq_len)
+        .workspace_bytes;
+}
+
+pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride, const void *kv_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                    int32_t num_seqs, int32_t max_seq_len, void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "pa_decode";
+    pa_status st = check_layer(layer, fn);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_seqs, max_seq_len and max_blocks_per_seq must be >= 0", fn);
+    if (num_seqs == 0) return ok();
+    if (!out || !query || !kv_cache || !block_tables || !seq_lens)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: out, query, kv_cache, block_tables and seq_lens must be non-NULL",
+                    fn);
+    if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: max_blocks_per_seq must be positive", fn);
+    const int eb = elt_bytes(layer->dtype);
+    const int64_t qrow = int64_t(layer->num_heads) * layer->head_size;
+    if (q_row_stride < qrow)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: q_row_stride %lld < num_heads * head_size %lld", fn,
+                    (long long)q_row_stride, (long long)qrow);
+    if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache) || (q_row_stride * eb) % 16 != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: out/query/kv_cache must be 16-byte aligned with 16-byte row strides",
+                    fn);
+    const pa::DecodePlan plan =
+        pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, num_seqs, max_seq_len);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes)
+            return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", fn, plan.workspace_bytes,
+                        workspace ? workspace_bytes : size_t(0));
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(PA_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
+    }
+    pa::DecodeParams p;
+    p.out = out;
+    p.query = query;
+    p.q_stride = q_row_stride;
+    p.k_cache = kv_cache;
+    p.v_cache = static_cast<const char *>(kv_cache) +
+                layer->num_blocks * layer->block_size * int64_t(layer->num_kv_heads) * layer->head_size * eb;
+    p.block_tables = block_tables;
+    p.max_blocks = max_blocks_per_seq;
+    p.seq_lens = seq_lens;
+    p.num_seqs = num_seqs;
+    p.num_heads = layer->num_heads;
+    p.num_kv_heads = layer->num_kv_heads;
+    p.block_shift = log2_exact(layer->block_size);
+    p.num_blocks = layer->num_blocks;
+    p.scale = layer->scale;
+    p.alibi_slopes = layer->alibi_slopes;
+    p.window = layer->sliding_window;
+    p.ws_acc = nullptr;
+    p.ws_ml = nullptr;
+    if (plan.workspace_bytes > 0) {
+        const size_t slots = size_t(num_seqs) * layer->num_heads * plan.num_parts;
+        const size_t acc = (slots * layer->head_size * sizeof(float) + 255) / 256 * 256;
+        p.ws_acc = static_cast<float *>(workspace);
+        p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc);
+    }
+    hipError_t e = pa::launch_decode(p, plan, layer->dtype, layer->head_size, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                            const void *key, const void *value, int64_t kv_row_stride, const void *kv_cache,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            const int32_t *cu_subquery, int32_t num_seqs, int64_t num_tokens,
+                            int32_t max_subquery_len, int32_t max_context_len, void *stream) {
+    const char *fn = "pa_prefill_varlen";
+    pa_status st = check_layer(layer, fn);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_tokens < 0 || max_subquery_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: sizes must be >= 0", fn);
+    if (num_seqs == 0 || num_tokens == 0) return ok();
+    if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_tokens exceeds int32", fn);
+    if (!out || !query || !key || !value || !cu_subquery)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: out, query, key, value and cu_subquery must be non-NULL", fn);
+    if (max_context_len > 0 && (!kv_cache || !block_tables || !context_lens || max_blocks_per_seq == 0))
+        return fail(PA_ERR_INVALID_ARGUMENT,
+                    "%s: a cached context (max_context_len > 0) needs kv_cache, block_tables, context_lens and "
+                    "max_blocks_per_seq > 0",
+                    fn);
+    const int eb = elt_bytes(layer->dtype);
+    const int64_t qrow = int64_t(layer->num_heads) * layer->head_size;
+    const int64_t kvrow = int64_t(layer->num_kv_heads) * layer->head_size;
+    if (q_row_stride < qrow || kv_row_stride < kvrow)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: row strides smaller than the rows", fn);
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key) || !aligned16(value) ||
+        (kv_cache && !aligned16(kv_cache)) || (q_row_stride * eb) % 16 != 0 || (kv_row_stride * eb) % 16 != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: buffers must be 16-byte aligned with 16-byte row strides", fn);
+    if (max_subquery_len == 0) return ok();
+    pa::PrefillParams p;
+    p.out = out;
+    p.query = query;
+    p.q_stride = q_row_stride;
+    p.key = key;
+    p.value = value;
+    p.kv_stride = kv_row_stride;
+    p.k_cache = kv_cache;
+    p.v_cache = kv_cache ? static_cast<const char *>(kv_cache) +
+                               layer->num_blocks * layer->block_size * kvrow * eb
+                         : nullptr;
+    const bool has_ctx = max_context_len > 0;
+    p.block_tables = has_ctx ? block_tables : nullptr;
+    p.max_blocks = has_ctx ? max_blocks_per_seq : 0;
+    p.context_lens = has_ctx ? context_lens : nullptr;
+    p.cu_subquery = cu_subquery;
+    p.num_seqs = num_seqs;
+    p.num_tokens = num_tokens;
+    p.num_heads = layer->num_heads;
+    p.num_kv_heads = layer->num_kv_heads;
+    p.block_shift = log2_exact(layer->block_size);
+    p.num_blocks = layer->num_blocks;
+    p.scale = layer->scale;
+    p.alibi_slopes = layer->alibi_slopes;
+    p.window = layer->sliding_window;
+    p.max_subquery_len = max_subquery_len;
+    p.max_context_len = max_context_len;
+    hipError_t e = pa::launch_prefill(p, layer->dtype, layer->head_size, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

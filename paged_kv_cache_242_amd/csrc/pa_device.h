@@ -1,0 +1,106 @@
+// Device-side helpers shared by the gfx950 kernels of libpa (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// bf16 values travel as raw 16-bit patterns; arithmetic is done in fp32.
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float floatx4_v __attribute__((ext_vector_type(4)));
+typedef float floatx16_v __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+    __bf16 b = static_cast<__bf16>(x);
+    return __builtin_bit_cast(bf16_t, b);
+}
+
+// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// c + a.lo * b.lo + a.hi * b.hi with bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c,
+                                           false);
+}
+
+// Byte permute: result byte k = byte sel[k] of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// From two bf16 pairs a = (a0, a1) and b = (b0, b1): (a0, b0) and (a1, b1).
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
+
+// DPP lane moves inside a row of 16 lanes.
+enum : int {
+    kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]: lane ^ 1
+    kDppQuadXor3 = 0x1B,      // quad_perm [3,2,1,0]: lane ^ 3
+    kDppHalfMirror = 0x141,   // lane ^ 7 inside each 8 lanes
+    kDppMirror = 0x140,       // lane ^ 15 inside each 16 lanes
+    kDppRowRor8 = 0x128,      // (lane + 8) mod 16: lane ^ 8 inside each 16 lanes
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Value of lane (lane ^ mask) for masks of the form 2^k - 1 (k = 1..6) or 2^k.
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float x) {
+    if constexpr (MASK == 1) return dpp_move<kDppQuadXor1>(x);
+    else if constexpr (MASK == 3) return dpp_move<kDppQuadXor3>(x);
+    else if constexpr (MASK == 7) return dpp_move<kDppHalfMirror>(x);
+    else if constexpr (MASK == 15) return dpp_move<kDppMirror>(x);
+    else if constexpr (MASK == 8) return dpp_move<kDppRowRor8>(x);
+    else return __shfl_xor(x, MASK, 64);
+}
+
+// Sum / max over the lanes lane ^ M, lane ^ 2M, ... (M a power of two): combines the row groups
+// of a wavefront whose rows are M lanes wide.
+template <int M>
+__device__ __forceinline__ float xor_sum_from(float x) {
+    if constexpr (M < 64) {
+        x += lane_xor<M>(x);
+        return xor_sum_from<M * 2>(x);
+    } else {
+        return x;
+    }
+}
+template <int M>
+__device__ __forceinline__ float xor_max_from(float x) {
+    if constexpr (M < 64) {
+        x = fmaxf(x, lane_xor<M>(x));
+        return xor_max_from<M * 2>(x);
+    } else {
+        return x;
+    }
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Compiler barrier for LDS traffic that stays inside one wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace pa

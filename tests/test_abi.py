@@ -1,0 +1,113 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point include/pa.h
+declares, and rejects bad host arguments before touching the GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import paged_kv_cache_242_amd as pa
+    return pa
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["pa_cache_write", "pa_decode", "pa_decode_workspace_size",
+                                           "pa_prefill_varlen", "pa_status_string", "pa_last_error_message",
+                                           "pa_version"])
+
+
+def test_library_exports_every_declared_symbol(pa):
+    lib = pa.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libpa.so does not export {name}"
+    assert set(pa.EXPORTED) == set(declared_functions())
+
+
+def test_version_and_status_strings(pa):
+    assert "gfx950" in pa.version()
+    lib = pa.library()
+    assert lib.pa_status_string(0) == b"PA_OK"
+    assert lib.pa_status_string(2) == b"PA_ERR_UNSUPPORTED"
+    assert lib.pa_status_string(99) == b"PA_ERR_UNKNOWN"
+
+
+def _layer(pa, **kw):
+    base = dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=4, dtype=1, scale=0.1,
+                alibi_slopes=None, sliding_window=0)
+    base.update(kw)
+    return pa._CLayer(*base.values())
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(head_size=96), 2, "head size 96"),
+    (dict(num_heads=6, num_kv_heads=4), 1, "must divide"),
+    (dict(block_size=12), 2, "block size 12"),
+    (dict(block_size=4), 2, "block size 4"),
+    (dict(dtype=7), 2, "dtype 7"),
+    (dict(num_blocks=0), 1, "num_blocks"),
+])
+def test_layer_validation(pa, kw, status, needle):
+    lib = pa.library()
+    c = _layer(pa, **kw)
+    st = lib.pa_cache_write(ctypes.byref(c), 16, 16, 1024, 1, 16, 16, None)
+    assert st == status
+    assert needle in lib.pa_last_error_message().decode()
+
+
+def test_zero_sizes_are_noops(pa):
+    lib = pa.library()
+    c = _layer(pa)
+    assert lib.pa_cache_write(ctypes.byref(c), None, None, 256, 0, None, None, None) == 0
+    assert lib.pa_decode(ctypes.byref(c), None, None, 1024, None, None, 1, None, 0, 0, None, 0, None) == 0
+    assert lib.pa_prefill_varlen(ctypes.byref(c), None, None, 1024, None, None, 256, None, None, 0, None, None, 0, 0,
+                                 0, 0, None) == 0
+    assert lib.pa_last_error_message() == b""
+
+
+def test_bad_pointers_and_alignment(pa):
+    lib = pa.library()
+    c = _layer(pa)
+    assert lib.pa_cache_write(ctypes.byref(c), None, 16, 256, 3, 16, 16, None) == 1
+    assert lib.pa_cache_write(ctypes.byref(c), 8, 16, 256, 3, 16, 16, None) == 1      # misaligned key
+    assert "aligned" in lib.pa_last_error_message().decode()
+    assert lib.pa_cache_write(ctypes.byref(c), 16, 16, 100, 3, 16, 16, None) == 1     # stride < row
+    # decode: workspace required for a long context
+    need = lib.pa_decode_workspace_size(ctypes.byref(c), 4, 100000)
+    assert need > 0
+    st = lib.pa_decode(ctypes.byref(c), 256, 256, 1024, 256, 256, 7000, 256, 4, 100000, None, 0, None)
+    assert st == 3 and "workspace" in lib.pa_last_error_message().decode()
+    st = lib.pa_decode(ctypes.byref(c), 256, 256, 1024, 256, 256, 7000, 256, 4, 100000, 256, need - 1, None)
+    assert st == 3
+    st = lib.pa_decode(ctypes.byref(c), 256, 256, 1024, 256, 256, 7000, 256, 4, 100000, 128, need, None)
+    assert st == 1 and "256-byte" in lib.pa_last_error_message().decode()
+    # prefill: a cached context needs tables
+    st = lib.pa_prefill_varlen(ctypes.byref(c), 256, 256, 1024, 256, 256, 256, 256, None, 4, 256, 256, 2, 10, 5, 7,
+                               None)
+    assert st == 1 and "cached context" in lib.pa_last_error_message().decode()
+
+
+def test_workspace_size_short_context_is_zero(pa):
+    lib = pa.library()
+    c = _layer(pa)
+    assert lib.pa_decode_workspace_size(ctypes.byref(c), 8, 100) == 0
+    assert lib.pa_decode_workspace_size(ctypes.byref(c), 0, 100) == 0
+
+
+def test_python_binding_rejects_cpu_tensors(pa):
+    import torch
+    layer = pa.Layer(8, 2, 128, 16, 4, torch.bfloat16, 0.1)
+    k = torch.zeros(3, 256, dtype=torch.bfloat16)
+    with pytest.raises(pa.PaError):
+        pa.cache_write(k, k, torch.zeros(2, 4, 16 * 256, dtype=torch.bfloat16), torch.zeros(3, dtype=torch.int64),
+                       layer)

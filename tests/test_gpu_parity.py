@@ -1,0 +1,261 @@
+"""GPU parity: libpa (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Cache write: bit-exact over the whole pool (unused slots keep their NaN fill).  Attention:
+bf16 max-abs <= 2e-2 and mean-abs <= 2e-3, fp32 max-abs <= 1e-4.  Small grids are compared
+element by element; the five full-size workloads run in the same launch configuration the
+benchmark times and are compared on sampled sequences / rows (the oracle computes those one by
+one)."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as gh
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _layer(H, Hkv, D, bs, dtype=wl.BF16, alibi=False, window=0, scale=None):
+    return wl.LayerSpec(H, Hkv, D, bs, 0, dtype, wl.fp32(scale if scale is not None else 1.0 / math.sqrt(D)),
+                        alibi_slopes=wl.alibi_slopes_geometric(H) if alibi else None, sliding_window=window)
+
+
+def _check_full(batch, what):
+    """Run everything on the GPU and compare everything against the oracle."""
+    _say(f"[{what}] gpu run")
+    cache, pre, dec = gh.gpu_run(batch)
+    _say(f"[{what}] oracle")
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(gh.wl.host_bits(cache).view(np.uint8), pool.view(np.uint8)), f"{what}: cache differs"
+    if pre is not None:
+        ref = gh.oracle_prefill(batch, pool)
+        gh.assert_close(gh.to_f64(pre), ref, batch.layer, f"{what} prefill")
+    if dec is not None:
+        ref, _ = gh.oracle_decode(batch, pool)
+        gh.assert_close(gh.to_f64(dec), ref, batch.layer, f"{what} decode")
+
+
+# ------------------------------------------------------------------------------ cache write
+
+@pytest.mark.parametrize("H,Hkv,D,bs,dtype", [
+    (8, 8, 64, 16, wl.F32), (32, 8, 128, 16, wl.BF16), (64, 8, 128, 32, wl.BF16), (4, 1, 64, 8, wl.BF16),
+    (6, 3, 128, 256, wl.F32),
+])
+def test_cache_write_bit_exact(H, Hkv, D, bs, dtype):
+    layer = _layer(H, Hkv, D, bs, dtype)
+    batch = wl.make_batch(layer, seed=31, prefill=[(3, 5), (0, 40)], decode=[1, 17, 0, 2 * bs + 3],
+                          device=gh.device(), pool_blocks=None)
+    _say(f"cache write H={H} Hkv={Hkv} D={D} bs={bs} {dtype}")
+    cache = gh.gpu_pool(batch)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8))
+
+
+def test_cache_write_strided_rows_and_padding():
+    """key/value as column slices of a wider [T, 3 * Hkv * D] tensor; slot -1 rows are skipped."""
+    layer = _layer(8, 2, 128, 16)
+    batch = wl.make_batch(layer, seed=32, decode=[5, 0, 9, 0, 33], device=gh.device())
+    T, W = batch.key.shape
+    wide = torch.zeros(T, 3 * W, dtype=torch.bfloat16, device=gh.device())
+    wide[:, W:2 * W] = batch.key
+    wide[:, 2 * W:] = batch.value
+    strided = dataclasses.replace(batch, key=wide[:, W:2 * W], value=wide[:, 2 * W:])
+    assert strided.key.stride(0) == 3 * W
+    cache = gh.gpu_pool(strided)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8))
+
+
+# ------------------------------------------------------------------------------ decode grid
+
+DECODE_LAYERS = [
+    _layer(8, 8, 64, 16, wl.F32, scale=0.125),
+    _layer(32, 8, 128, 16),
+    _layer(64, 8, 128, 32),
+    _layer(32, 32, 128, 16, alibi=True, window=100),
+    _layer(16, 2, 64, 8),
+    _layer(12, 2, 128, 64),                 # 6 heads per KV head: padded group
+    _layer(32, 2, 128, 16, window=300),     # 16 heads per KV head: two head groups
+    _layer(4, 4, 128, 32, wl.F32, alibi=True, window=37),
+    _layer(6, 3, 64, 256, alibi=True),
+]
+DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
+
+
+@pytest.mark.parametrize("li", range(len(DECODE_LAYERS)))
+def test_decode_grid(li):
+    layer = DECODE_LAYERS[li]
+    _say(f"decode grid layer {li}: {layer}")
+    batch = wl.make_batch(layer, seed=40 + li, decode=DECODE_LENS, device=gh.device())
+    _check_full(batch, f"decode layer {li}")
+
+
+def test_decode_strided_query_and_determinism():
+    layer = _layer(32, 8, 128, 16)
+    batch = wl.make_batch(layer, seed=50, decode=[700, 3000, 1, 64], device=gh.device())
+    pl = gh.player(batch.layer)
+    cache = gh.gpu_pool(batch, pl)
+    wide = torch.zeros(4, 3 * 32 * 128, dtype=torch.bfloat16, device=gh.device())
+    wide[:, 128:128 + 4096] = batch.query
+    q = wide[:, 128:128 + 4096]
+    bt, sl = gh.i32(batch.decode_block_tables), gh.i32(batch.decode_seq_lens)
+    a = gh.pa().decode(q, cache, bt, sl, pl, 3000)
+    b = gh.pa().decode(batch.query, cache, bt, sl, pl, 3000)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "decode is not deterministic"
+    pool = gh.oracle_pool(batch)
+    ref, _ = gh.oracle_decode(batch, pool)
+    gh.assert_close(gh.to_f64(a), ref, batch.layer, "strided-query decode")
+
+
+def test_decode_workspace_errors():
+    layer = _layer(32, 8, 128, 16)
+    batch = wl.make_batch(layer, seed=51, decode=[3000, 2000], device=gh.device())
+    pl = gh.player(batch.layer)
+    cache = gh.gpu_pool(batch, pl)
+    need = gh.pa().decode_workspace_size(pl, 2, 3000)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device=gh.device())
+    with pytest.raises(gh.pa().PaError) as e:
+        gh.pa().decode(batch.query, cache, gh.i32(batch.decode_block_tables), gh.i32(batch.decode_seq_lens), pl,
+                       3000, workspace=small)
+    assert e.value.status == gh.pa().PA_ERR_WORKSPACE
+
+
+def test_unsupported_head_size_raises():
+    pl = gh.pa().Layer(4, 4, 96, 16, 4, torch.bfloat16, 0.1)
+    q = torch.zeros(1, 4 * 96, dtype=torch.bfloat16, device=gh.device())
+    cache = torch.zeros(2, 4, 16 * 4 * 96, dtype=torch.bfloat16, device=gh.device())
+    with pytest.raises(gh.pa().PaError) as e:
+        gh.pa().decode(q, cache, gh.i32(np.zeros((1, 1))), gh.i32(np.ones(1)), pl, 1)
+    assert e.value.status == gh.pa().PA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------------------ prefill grid
+
+PREFILL_LAYERS = [
+    _layer(32, 8, 128, 16),
+    _layer(32, 32, 128, 16, alibi=True, window=100),
+    _layer(8, 2, 64, 32),
+    _layer(8, 8, 64, 16, wl.F32),
+    _layer(12, 4, 128, 16, window=64),
+    _layer(4, 1, 128, 8, alibi=True),
+    _layer(4, 2, 128, 16, wl.F32, alibi=True, window=50),
+]
+PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
+                (1000, 257), (63, 1), (64, 64), (0, 0)]
+
+
+@pytest.mark.parametrize("li", range(len(PREFILL_LAYERS)))
+def test_prefill_grid(li):
+    layer = PREFILL_LAYERS[li]
+    _say(f"prefill grid layer {li}: {layer}")
+    batch = wl.make_batch(layer, seed=60 + li, prefill=PREFILL_SEQS, device=gh.device())
+    _check_full(batch, f"prefill layer {li}")
+
+
+def test_prefill_without_context_arguments():
+    """No cached context: kv_cache, block_tables and context_lens may all be omitted."""
+    layer = _layer(32, 8, 128, 16)
+    batch = wl.make_batch(layer, seed=70, prefill=[(0, 200), (0, 7), (0, 129)], device=gh.device())
+    pl = gh.player(batch.layer)
+    out = gh.pa().prefill_varlen(batch.query, batch.key, batch.value, None, None, None, gh.i32(batch.prefill_cu),
+                                 pl, 200, 0)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    ref = gh.oracle_prefill(batch, pool)
+    gh.assert_close(gh.to_f64(out), ref, batch.layer, "context-free prefill")
+
+
+def test_mixed_batch_small():
+    layer = _layer(16, 4, 128, 16, alibi=True, window=200)
+    batch = wl.make_batch(layer, seed=71, prefill=[(100, 150), (0, 90), (333, 1)], decode=[1, 250, 700, 0],
+                          device=gh.device())
+    _check_full(batch, "mixed small")
+
+
+# ------------------------------------------------------------------------------ full-size workloads
+
+def _sample(n, k, rng, must=()):
+    pick = set(int(x) for x in must)
+    pick.update(int(x) for x in rng.choice(n, size=min(k, n), replace=False))
+    return sorted(pick)
+
+
+def test_workload1_full():
+    W = wl.workload(1)
+    _say(W.description)
+    batch = W.batch(gh.device())
+    _check_full(batch, W.name)
+
+
+def test_workload2_full_cache_and_sampled_rows():
+    W = wl.workload(2)
+    _say(W.description)
+    batch = W.batch(gh.device())
+    cache, pre, _ = gh.gpu_run(batch)
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8)), "cache write differs"
+    T = batch.num_prefill_tokens
+    sel = np.zeros(T, dtype=bool)
+    sel[::11] = True
+    sel[batch.prefill_cu[:-1]] = True
+    sel[batch.prefill_cu[1:] - 1] = True
+    ref = gh.oracle_prefill(batch, pool, row_select=sel)
+    gh.assert_close(gh.to_f64(pre)[sel], ref[sel].reshape(int(sel.sum()), -1), batch.layer, W.name)
+
+
+def test_workload3_sampled_sequences():
+    W = wl.workload(3)
+    _say(W.description)
+    batch = W.batch(gh.device())
+    _, _, dec = gh.gpu_run(batch)
+    rng = np.random.default_rng(3)
+    lens = batch.decode_seq_lens
+    seqs = _sample(len(lens), 12, rng, must=(int(np.argmax(lens)), int(np.argmin(lens))))
+    pool = gh.oracle_pool(batch, decode_seqs=seqs)
+    ref, idx = gh.oracle_decode(batch, pool, seqs)
+    gh.assert_close(gh.to_f64(dec).reshape(len(lens), -1)[idx], ref.reshape(len(idx), -1), batch.layer, W.name)
+
+
+def test_workload4_sampled():
+    W = wl.workload(4)
+    _say(W.description)
+    batch = W.batch(gh.device())
+    _, pre, dec = gh.gpu_run(batch)
+    rng = np.random.default_rng(4)
+    lens = batch.decode_seq_lens
+    seqs = _sample(len(lens), 10, rng, must=(int(np.argmax(lens)), int(np.argmin(lens))))
+    pool = gh.oracle_pool(batch, prefill_seqs=range(len(batch.prefill_context_lens)), decode_seqs=seqs)
+    ref, idx = gh.oracle_decode(batch, pool, seqs)
+    gh.assert_close(gh.to_f64(dec).reshape(len(lens), -1)[idx], ref.reshape(len(idx), -1), batch.layer,
+                    W.name + " decode")
+    T = batch.num_prefill_tokens
+    sel = np.zeros(T, dtype=bool)
+    sel[::13] = True
+    sel[batch.prefill_cu[1:] - 1] = True
+    ref = gh.oracle_prefill(batch, pool, row_select=sel)
+    gh.assert_close(gh.to_f64(pre)[sel], ref[sel].reshape(int(sel.sum()), -1), batch.layer, W.name + " prefill")
+
+
+def test_workload5_sampled_sequences():
+    W = wl.workload(5)
+    _say(W.description)
+    batch = W.batch(gh.device())
+    _, _, dec = gh.gpu_run(batch)
+    lens = batch.decode_seq_lens
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7})
+    pool = gh.oracle_pool(batch, decode_seqs=seqs)
+    ref, idx = gh.oracle_decode(batch, pool, seqs)
+    gh.assert_close(gh.to_f64(dec).reshape(len(lens), -1)[idx], ref.reshape(len(idx), -1), batch.layer, W.name)
+    del batch, dec
+    torch.cuda.empty_cache()
