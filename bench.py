@@ -1,0 +1,267 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one synthetic batch, all inputs resident in HBM:
+pa_cache_write of the step's new K/V rows, pa_prefill_varlen over the prefill rows and pa_decode
+over the decode rows (a workload without prefill or decode rows skips that call).  The default
+workload is the chunked-prefill mixed batch (4 chunks of 512 new tokens on contexts U[1024, 4096],
+plus 128 decode sequences with L ~ U[256, 4096], 32 query = 32 KV heads, head size 128, block
+size 16, ALiBi, window 4096, bf16), the one workload that exercises every step of the path.
+
+Each call is bracketed by HIP events on the stream it runs on (torch's current stream), so the
+per-call times are kernel times; the K timed steps are bracketed by torch.cuda.synchronize().
+
+Prints ONE JSON line:
+  value         decode KV-read throughput, GB/s = visible K+V bytes / decode time
+  secondary     prefill attention TFLOP/s (4 * head_size flops per visible (row, key, head)),
+                cache-write GB/s (bytes read + written), each with its fraction of peak
+  roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample of the same
+                workload (decode sequences), in the same GB/s unit
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "decode KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(batch: wl.PagedBatch) -> int:
+    L = batch.layer
+    W = L.sliding_window
+    lens = batch.decode_seq_lens.astype(np.int64)
+    vis = np.minimum(lens, W) if W and W > 0 else lens
+    return int(vis.sum()) * L.num_kv_heads * L.head_size * 2 * L.elt_bytes
+
+
+def prefill_flops(batch: wl.PagedBatch) -> int:
+    L = batch.layer
+    W = L.sliding_window
+    total = 0
+    for c, n in zip(batch.prefill_context_lens.astype(np.int64), batch.prefill_query_lens.astype(np.int64)):
+        pos = c + np.arange(n, dtype=np.int64)
+        vis = np.minimum(pos + 1, W) if W and W > 0 else pos + 1
+        total += int(vis.sum())
+    return total * L.num_heads * 4 * L.head_size
+
+
+def cache_write_bytes(batch: wl.PagedBatch) -> int:
+    L = batch.layer
+    rows = int((batch.slot_mapping >= 0).sum())
+    return rows * L.row_elems * L.elt_bytes * 2 * 2      # K and V, read + written
+
+
+def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20.0):
+    """Time the oracle's decode on the GPU machine's host cores over a bounded sample of the
+    decode sequences of the same batch (longest-first is not used: a seeded random subset)."""
+    import oracle
+    L = batch.layer
+    ol = oracle.OracleLayer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks,
+                            oracle.DTYPE_F32 if L.dtype == wl.F32 else oracle.DTYPE_BF16, L.scale,
+                            L.alibi_slopes, L.sliding_window)
+    pool = wl.host_bits(cache)                                  # exact bytes the GPU used
+    tp = batch.num_prefill_tokens
+    q = wl.host_bits(batch.query[tp:])
+    lens = batch.decode_seq_lens
+    order = np.random.default_rng(batch.seed).permutation(len(lens))
+    # calibrate on a small slice, then size the sample for ~budget_s of CPU work
+    per_byte = None
+    done_bytes = 0
+    done_time = 0.0
+    used = 0
+    taken = []
+    start = 0
+    chunk = 4
+    while start < len(order):
+        idx = order[start:start + chunk]
+        t0 = time.perf_counter()
+        _, used = oracle.decode(ol, q[idx], pool, batch.decode_block_tables[idx], lens[idx], return_threads=True)
+        dt = time.perf_counter() - t0
+        vis = np.minimum(lens[idx], L.sliding_window) if L.sliding_window > 0 else lens[idx]
+        nbytes = int(vis.astype(np.int64).sum()) * L.num_kv_heads * L.head_size * 2 * L.elt_bytes
+        done_bytes += nbytes
+        done_time += dt
+        taken.extend(int(i) for i in idx)
+        start += chunk
+        per_byte = done_time / max(done_bytes, 1)
+        remaining = budget_s - done_time
+        if remaining <= 0:
+            break
+        chunk = max(1, min(len(order) - start, int(remaining / max(per_byte * nbytes / len(idx), 1e-9))))
+    return {
+        "value": done_bytes / done_time / 1e9,
+        "unit": "GB/s",
+        "cores": int(used),
+        "kind": "oracle",
+        "sample": f"fp64 oracle decode of {len(taken)} of {len(lens)} decode sequences of the same batch "
+                  f"({done_bytes / 1e9:.2f} GB of visible K+V, {done_time:.1f} s), cpu "
+                  f"{platform.processor() or platform.machine()}",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import paged_kv_cache_242_amd as pa
+
+    dev = torch.device("cuda:0")
+    W = wl.workload(args.workload)
+    log(f"workload {args.workload}: {W.description}")
+    t0 = time.perf_counter()
+    batch = W.batch(dev)
+    L = batch.layer
+    slopes = torch.tensor(L.alibi_slopes, device=dev) if L.alibi_slopes is not None else None
+    layer = pa.Layer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks, L.torch_dtype, L.scale,
+                     slopes, L.sliding_window)
+    cache = torch.full((2, L.num_blocks, L.block_size * L.row_elems), float("nan"), dtype=L.torch_dtype, device=dev)
+    if batch.ctx_key.shape[0]:
+        pa.cache_write(batch.ctx_key, batch.ctx_value, cache, torch.as_tensor(batch.ctx_slots, device=dev), layer)
+    batch.ctx_key = batch.ctx_value = None                       # context is in the cache now
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"setup {time.perf_counter() - t0:.1f} s; pool {cache.numel() * cache.element_size() / 1e9:.2f} GB")
+
+    i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
+    slots = torch.as_tensor(batch.slot_mapping, device=dev)
+    tp = batch.num_prefill_tokens
+    has_pre = len(batch.prefill_context_lens) > 0
+    has_dec = len(batch.decode_seq_lens) > 0
+    if has_pre:
+        p_bt, p_ctx, p_cu = i32(batch.prefill_block_tables), i32(batch.prefill_context_lens), i32(batch.prefill_cu)
+        p_maxq, p_maxc = int(batch.prefill_query_lens.max()), int(batch.prefill_context_lens.max())
+        q_pre, k_pre, v_pre = batch.query[:tp], batch.key[:tp], batch.value[:tp]
+        out_pre = torch.empty_like(q_pre)
+    if has_dec:
+        d_bt, d_sl = i32(batch.decode_block_tables), i32(batch.decode_seq_lens)
+        d_max = int(batch.decode_seq_lens.max())
+        q_dec = batch.query[tp:]
+        out_dec = torch.empty_like(q_dec)
+        ws_bytes = pa.decode_workspace_size(layer, len(batch.decode_seq_lens), d_max)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+    n_ev = 2 * (args.steps + args.warmup)
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("cw", "pre", "dec")}
+
+    def step(s):
+        ev["cw"][2 * s].record(stream)
+        pa.cache_write(batch.key, batch.value, cache, slots, layer)
+        ev["cw"][2 * s + 1].record(stream)
+        if has_pre:
+            ev["pre"][2 * s].record(stream)
+            pa.prefill_varlen(q_pre, k_pre, v_pre, cache, p_bt, p_ctx, p_cu, layer, p_maxq, p_maxc, out=out_pre)
+            ev["pre"][2 * s + 1].record(stream)
+        if has_dec:
+            ev["dec"][2 * s].record(stream)
+            pa.decode(q_dec, cache, d_bt, d_sl, layer, d_max, out=out_dec, workspace=ws)
+            ev["dec"][2 * s + 1].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+
+    def avg_ms(key):
+        ts = [ev[key][2 * s].elapsed_time(ev[key][2 * s + 1]) for s in range(args.warmup, args.warmup + args.steps)]
+        return float(np.mean(ts)), float(np.min(ts))
+
+    cw_ms, _ = avg_ms("cw")
+    cw_gbps = cache_write_bytes(batch) / (cw_ms * 1e-3) / 1e9
+    secondary = {"cache_write": {"ms": cw_ms, "GB_per_s": cw_gbps, "frac_hbm_peak": cw_gbps / HBM_PEAK_GBPS}}
+    value = None
+    unit = "GB/s"
+    roofline = None
+    if has_pre:
+        pre_ms, pre_min = avg_ms("pre")
+        flops = prefill_flops(batch)
+        tflops = flops / (pre_ms * 1e-3) / 1e12
+        secondary["prefill"] = {"ms": pre_ms, "ms_min": pre_min, "gflop_per_call": flops / 1e9, "TFLOP_per_s": tflops,
+                                "frac_mfma_peak": tflops / MFMA_BF16_PEAK_TFLOPS}
+    if has_dec:
+        dec_ms, dec_min = avg_ms("dec")
+        nbytes = decode_bytes(batch)
+        gbps = nbytes / (dec_ms * 1e-3) / 1e9
+        value = gbps
+        secondary["decode"] = {"ms": dec_ms, "ms_min": dec_min, "gb_per_call": nbytes / 1e9, "GB_per_s": gbps,
+                               "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
+        roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                    "kernel": "decode_partition_kernel (+ decode_merge_kernel when split)",
+                    "algorithmic_bytes_per_launch": nbytes}
+    else:
+        value = secondary["prefill"]["TFLOP_per_s"]
+        unit = "TFLOP/s"
+        roofline = {"bound": "mfma", "achieved": value, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": value / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_bf16_kernel",
+                    "algorithmic_flops_per_launch": prefill_flops(batch)}
+
+    cpu = None
+    if not args.no_cpu_baseline and has_dec:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(batch, cache, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": L.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{W.name} (config {W.index}): {W.description}", "seed": W.seed,
+                   "num_tokens": batch.num_tokens, "prefill_rows": tp,
+                   "decode_seqs": int(len(batch.decode_seq_lens)),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
