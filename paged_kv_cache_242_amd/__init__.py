@@ -52,11 +52,11 @@ class _CLayer(ctypes.Structure):
     ]
 
 
-def _load_library():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libpa.so is not built ({LIB_PATH} missing); run `python -m paged_kv_cache_242_amd.build` "
+def _load_library(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"libpa.so is not built ({path} missing); run `python -m paged_kv_cache_242_amd.build` "
                           "or __graft_entry__.build()")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     LP = ctypes.POINTER(_CLayer)
     lib.pa_cache_write.argtypes = [LP, P, P, I64, I64, P, P, P]

@@ -115,7 +115,8 @@ pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *val
 
 size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len) {
     if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0) return 0;
-    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, num_seqs, max_seq_len)
+    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, num_seqs,
+                           max_seq_len)
         .workspace_bytes;
 }
 
@@ -141,7 +142,8 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: out/query/kv_cache must be 16-byte aligned with 16-byte row strides",
                     fn);
     const pa::DecodePlan plan =
-        pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, num_seqs, max_seq_len);
+        pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, num_seqs,
+                           max_seq_len);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes)
             return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", fn, plan.workspace_bytes,

@@ -25,12 +25,12 @@ struct DecodePlan {
     int32_t head_groups;      // query heads of one KV head are processed in this many groups
     int32_t heads_per_group;  // real heads per group (<= 8)
     int32_t padded_group;     // heads_per_group rounded up to 1, 2, 4 or 8
-    int32_t part_size;        // keys per split-KV partition (multiple of 128)
+    int32_t part_size;        // keys per split-KV partition (multiple of 256, <= 128 blocks)
     int32_t num_parts;        // partitions of the longest sequence
     size_t workspace_bytes;   // 0 when num_parts == 1
 };
-DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t num_seqs,
-                       int32_t max_seq_len);
+DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                       int32_t num_seqs, int32_t max_seq_len);
 
 struct DecodeParams {
     void *out;                // [B, H*D]
