@@ -16,7 +16,9 @@ Prints ONE JSON line:
   value         decode KV-read throughput, GB/s = visible K+V bytes / decode time
   secondary     prefill attention TFLOP/s (4 * head_size flops per visible (row, key, head)),
                 cache-write GB/s (bytes read + written), each with its fraction of peak
-  roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s
+  roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s;
+                traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
+                (profiles/decode_traffic.json), null when the decode source changed since
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample of the same
                 workload (decode sequences), in the same GB/s unit
 """
@@ -39,6 +41,8 @@ if ROOT not in sys.path:
 import workloads as wl  # noqa: E402
 
 METRIC = "decode KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SOURCES = ("paged_kv_cache_242_amd/csrc/decode.hip", "paged_kv_cache_242_amd/csrc/pa_device.h")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 
@@ -70,6 +74,44 @@ def cache_write_bytes(batch: wl.PagedBatch) -> int:
     L = batch.layer
     rows = int((batch.slot_mapping >= 0).sum())
     return rows * L.row_elems * L.elt_bytes * 2 * 2      # K and V, read + written
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: int):
+    """HBM bytes per decode call (partition + merge kernels) from the committed rocprofv3 counter
+    summary, or None when there is none for this workload or the decode kernel source changed
+    since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("decode_source_sha256") != decode_source_hash():
+        return None
+    entry = data.get("workloads", {}).get(str(workload))
+    return None if entry is None else entry.get("hbm_bytes_per_call")
+
+
+def copy_probe(gib: float):
+    """A plain device copy of a known size (for calibrating the FETCH_SIZE / WRITE_SIZE counters)."""
+    dev = torch.device("cuda:0")
+    n = int(gib * (1 << 30))
+    x = torch.ones(n, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "calls": 3}), flush=True)
+    return 0
 
 
 def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20.0):
@@ -128,6 +170,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device copy of GIB GiB (counter calibration) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -135,6 +179,8 @@ def main(argv=None):
               file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe > 0:
+        return copy_probe(args.copy_probe)
     import paged_kv_cache_242_amd as pa
 
     dev = torch.device("cuda:0")
@@ -223,7 +269,7 @@ def main(argv=None):
         secondary["decode"] = {"ms": dec_ms, "ms_min": dec_min, "gb_per_call": nbytes / 1e9, "GB_per_s": gbps,
                                "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
         roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                    "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
                     "kernel": "decode_partition_kernel (+ decode_merge_kernel when split)",
                     "algorithmic_bytes_per_launch": nbytes}
     else:
