@@ -66,6 +66,14 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # hipcc's host pass can drop a kernel's launch stub without an error (e.g. when a device
+    # builtin gets an argument type the host target rejects); the library would then fail only
+    # when loaded.  Refuse to install such a library.
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], check=True, capture_output=True, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the host code:\n  " + "\n  ".join(missing))
     os.replace(tmp, OUT)
     return OUT
 

@@ -36,8 +36,6 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 32;          // keys per wavefront tile
 constexpr int kMaxGroup = 8;       // query heads per work unit
 #ifndef PA_DECODE_MIN_UNITS

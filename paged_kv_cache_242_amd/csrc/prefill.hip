@@ -57,12 +57,7 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams &p, int seq) {
     return s;
 }
 
-// Element offset of key/value row j of a sequence, and which source it comes from.
-struct RowSrc {
-    const bf16_t *k;
-    const bf16_t *v;
-};
-
+// Key and value rows j of a sequence: cached (through the block table) or new.
 template <typename T>
 __device__ __forceinline__ void row_ptrs(const PrefillParams &p, const SeqInfo &s, int seq, int g, int D, int j,
                                          const T *&kptr, const T *&vptr) {
@@ -80,18 +75,6 @@ __device__ __forceinline__ void row_ptrs(const PrefillParams &p, const SeqInfo &
     }
 }
 
-// Position of key kp' (0..63) of a tile in the transposed V tile, for key index k (0..63):
-// k = 32 kc + 16 hh + 4 g + ii  ->  32 kc + 8 g + 4 hh + ii.
-__device__ __forceinline__ int vt_key_pos(int k) {
-    const int kc = k >> 5, hh = (k >> 4) & 1, g = (k >> 2) & 3, ii = k & 3;
-    return 32 * kc + 8 * g + 4 * hh + ii;
-}
-// Element index inside Vt[D][64] of (d, permuted key position kp), with 16-byte units swizzled.
-__device__ __forceinline__ int vt_index(int d, int kp) {
-    const int f = (d ^ (d >> 3)) & 7;
-    return d * kBN + (((kp >> 3) ^ f) << 3) + (kp & 7);
-}
-
 // Grid of the bf16 kernel.  Workgroups that read the same K/V -- the G query heads of one KV head
 // and `qtiles_per_group` neighbouring query tiles of one sequence -- form a group.  Workgroups
 // are dealt to the 8 XCDs round-robin by index, so the index is built as
@@ -106,16 +89,48 @@ struct PrefillGrid {
     int num_groups;        // num_qblocks * num_seqs * num_kv_heads
 };
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// One 16-byte-per-lane global -> LDS copy: lane l reads base + lane_off (bytes) and fills
+// 16-byte unit l of the 1 KB stretch at lds_dst.  base must be wave-uniform; it goes into a raw
+// buffer descriptor (kept in scalar registers) and the lane offset into the vector offset.
+__device__ __forceinline__ void dma16(const char *base, uint32_t lane_off, bf16_t *lds_dst) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, lane_off, 0, 0, 0);
+}
+
+// The same copy from a per-lane address.
+__device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
+    __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)lds_dst, 16, 0, 0);
+}
+
+// Tile staging.  K and V tiles (64 keys x D) are copied global -> LDS by the load-to-LDS path
+// (buffer/global_load_lds_dwordx4: lane l of an instruction fills 16-byte unit l of a 1 KB LDS
+// stretch), so they never pass through registers.  Swizzles are applied by choosing, per lane,
+// which 16-byte chunk of the source row to fetch:
+//   K: row-major [64][D], chunk c of row r stored at chunk c ^ (r % CH); the S^T operand read
+//      (16 rows, same chunk) then hits distinct banks.
+//   V: row-major [64][D], 32-byte unit u of key k stored at unit u ^ (k % 4); the transposing
+//      operand read (ds_read_b64_tr_b16: 4 keys x 32 bytes per 16 lanes) then hits distinct
+//      banks.
+// Each wavefront copies 16 keys (rows 16 w .. 16 w + 15) of each tile, so one or two block ids
+// per wavefront and tile suffice; they are scalar loads issued two tiles ahead.
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams p, PrefillGrid grid) {
     constexpr int CH = D / 8;        // 16-byte chunks per row
     constexpr int DC = D / 32;       // k-chunks of S^T
     constexpr int DB = D / 16;       // d-blocks of O^T
-    constexpr int KPT = CH / 4;      // K chunks per thread (one row per thread, 4 threads per row)
-    constexpr int V_THREADS = 16 * CH;
-    // two stages of K (row-major) and V (transposed)
-    __shared__ __align__(16) bf16_t Ks[2][kBN * D];
-    __shared__ __align__(16) bf16_t Vt[2][D * kBN];
+    constexpr int NJ = CH / 4;       // DMA instructions per wavefront per operand per tile
+    constexpr int ROWB = D * 2;      // bytes per tile row
+    __shared__ __align__(16) bf16_t Ks0[kBN * D];
+    __shared__ __align__(16) bf16_t Vs0[kBN * D];
+    __shared__ __align__(16) bf16_t Ks1[kBN * D];
+    __shared__ __align__(16) bf16_t Vs1[kBN * D];
 
     // ---- workgroup -> (sequence, KV head, query head, query tile)
     const int b = blockIdx.x;
@@ -161,219 +176,282 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const float slope2 = p.alibi_slopes ? p.alibi_slopes[h] * kLog2e : 0.f;
     const bool has_alibi = p.alibi_slopes != nullptr;
 
-    // ---- tile loaders.  Each thread loads one K row (KPT chunks) and, if it is a V thread, four
-    // consecutive keys of one 16-byte column; both lie in one cache block, whose id is fetched two
-    // tiles ahead.
-    const int k_row = tid >> 2;
-    const int k_ch0 = (tid & 3) * KPT;
-    const int v_quad = tid & 15, v_ch = tid >> 4;
-    const int64_t kv_head_off = int64_t(g) * D;
-    const int64_t cache_row_elems = int64_t(p.num_kv_heads) * D;
-    auto block_id = [&](int key) -> int {
-        if (key >= si.c) return 0;
-        int64_t blk = p.block_tables[int64_t(seq) * p.max_blocks + (key >> p.block_shift)];
-        return int(blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk));
+    // ---- DMA addressing.  Wavefront w, instruction j copies tile rows (NJ w + j) * (64 / CH) ..;
+    // lane l lands in 16-byte unit l of that 1 KB stretch: row (NJ w + j) * (64 / CH) + l / CH,
+    // physical chunk l % CH, which holds logical chunk kchunk (K) / vchunk (V).
+    constexpr int ROWS_PER_INST = 64 / CH;                  // 4 (D = 128) or 8 (D = 64)
+    const char *kc_bytes = reinterpret_cast<const char *>(p.k_cache);
+    const char *vc_bytes = reinterpret_cast<const char *>(p.v_cache);
+    const char *kn_bytes = reinterpret_cast<const char *>(p.key);
+    const char *vn_bytes = reinterpret_cast<const char *>(p.value);
+    const int64_t head_off = int64_t(g) * ROWB;
+    const int64_t cache_row_bytes = int64_t(p.num_kv_heads) * ROWB;
+    const int64_t new_row_bytes = int64_t(p.kv_stride) * 2;
+    const int64_t block_bytes = cache_row_bytes << p.block_shift;
+    const int bmask = (1 << p.block_shift) - 1;
+    // Lane terms of the copy addresses: the lane's row among its instruction's rows and the
+    // logical chunk its physical LDS unit holds (the residues of the row mod CH and mod 4 depend
+    // only on j and the lane).  They are rebuilt from the lane id at every copy -- a few ALU ops --
+    // rather than held in registers across the loop.
+    auto lane_terms = [&](int &lrow, int &pc) {
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        lrow = l / CH;
+        pc = l % CH;
     };
-    auto clampk = [&](int key) { return min(max(key, key_lo), key_hi); };
-    auto row_ptr = [&](const void *cache, const void *rows, int key, int blk) -> const bf16_t * {
-        if (key < si.c) {
-            const int64_t off = ((int64_t(blk) << p.block_shift) + (key & ((1 << p.block_shift) - 1))) * cache_row_elems +
-                                kv_head_off;
-            return reinterpret_cast<const bf16_t *>(cache) + off;
+    auto k_chunk = [&](int lrow, int pc, int j) -> uint32_t {
+        return uint32_t(pc ^ ((j * ROWS_PER_INST + lrow) % CH)) * 16;
+    };
+    auto v_chunk = [&](int lrow, int pc) -> uint32_t {
+        return uint32_t((((pc >> 1) ^ (lrow & 3)) * 2 + (pc & 1)) * 16);
+    };
+    const int wrow0 = 16 * wave;                            // first tile row this wavefront copies
+    // Block ids of this wavefront's 16 rows of tile kt: lane 0 gets the first row's block, lane 1
+    // the last (cached) row's.  A vector load, so the wait at the end of the tile covers it.
+    auto fetch_ids = [&](int kt) -> int {
+        const int r0 = kt * kBN + wrow0;
+        int id = 0;
+        if (r0 < si.c) {
+            const int r = (lane & 1) ? min(r0 + 15, si.c - 1) : r0;
+            id = p.block_tables[int64_t(seq) * p.max_blocks + (r >> p.block_shift)];
         }
-        return reinterpret_cast<const bf16_t *>(rows) + int64_t(si.start + (key - si.c)) * p.kv_stride + kv_head_off;
+        return id;
     };
-    int kid_a = 0, vid_a = 0, kid_b = 0, vid_b = 0;   // block ids of tiles kt+1 (a) and kt+2 (b)
-    auto fetch_ids = [&](int kt, int &kid, int &vid) {
-        kid = block_id(clampk(kt * kBN + k_row));
-        vid = block_id(clampk(kt * kBN + 4 * v_quad));
+    auto clamp_block = [&](int64_t b) -> int64_t {
+        return b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
     };
-    uint4 kreg[KPT], vreg[4];
-    auto load_tile = [&](int kt, int kid, int vid) {
-        const int kk = clampk(kt * kBN + k_row);
-        const bf16_t *kp = row_ptr(p.k_cache, p.key, kk, kid);
+    // Copy this wavefront's 16 rows of tile kt into (kdst, vdst).  The rows are all cached, all
+    // new and at or below key_hi (each instruction then has a uniform base address and a 32-bit
+    // lane offset), or -- at most twice per sequence -- mixed, which takes a per-lane path.  Rows
+    // past key_hi re-read row key_hi; every query row of the tile masks them.
+    auto copy_tile = [&](int kt, int ids, bf16_t *kdst, bf16_t *vdst) {
+        const int w0 = kt * kBN + wrow0;                  // first key of this wavefront (uniform)
+        int lrow, pc;
+        lane_terms(lrow, pc);
+        if (w0 + 15 < si.c) {
+            const int64_t id0 = clamp_block(__builtin_amdgcn_readlane(ids, 0));
+            const int64_t id1 = clamp_block(__builtin_amdgcn_readlane(ids, 1));
+            const uint32_t lrow_cache = uint32_t(lrow) * uint32_t(cache_row_bytes);
+            const uint32_t v_lane = lrow_cache + v_chunk(lrow, pc);
 #pragma unroll
-        for (int c = 0; c < KPT; ++c) kreg[c] = *reinterpret_cast<const uint4 *>(kp + 8 * (k_ch0 + c));
-        if (tid < V_THREADS) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                // the four keys of a quad share a block (block sizes are multiples of 8)
-                const int kv = clampk(kt * kBN + 4 * v_quad + ii);
-                const int vb = (kv >> p.block_shift) == ((kt * kBN + 4 * v_quad) >> p.block_shift) ? vid : block_id(kv);
-                vreg[ii] = *reinterpret_cast<const uint4 *>(row_ptr(p.v_cache, p.value, kv, vb) + 8 * v_ch);
+            for (int j = 0; j < NJ; ++j) {
+                const int r0 = w0 + j * ROWS_PER_INST;
+                const int64_t blk = ((r0 >> p.block_shift) == (w0 >> p.block_shift)) ? id0 : id1;
+                const int64_t base = blk * block_bytes + head_off + int64_t(r0 & bmask) * cache_row_bytes;
+                dma16(kc_bytes + base, lrow_cache + k_chunk(lrow, pc, j), kdst + (NJ * wave + j) * 512);
+                dma16(vc_bytes + base, v_lane, vdst + (NJ * wave + j) * 512);
             }
-        }
-    };
-    auto store_tile = [&](int stage) {
+        } else if (w0 >= si.c && w0 + 15 <= key_hi) {
+            const uint32_t lrow_new = uint32_t(lrow) * uint32_t(new_row_bytes);
+            const uint32_t v_lane = lrow_new + v_chunk(lrow, pc);
 #pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-            const int ch = k_ch0 + c;
-            *reinterpret_cast<uint4 *>(&Ks[stage][k_row * D + ((ch ^ (k_row % CH)) << 3)]) = kreg[c];
-        }
-        if (tid < V_THREADS) {
-            const int kp0 = vt_key_pos(4 * v_quad);
-            const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-            const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-            const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-            const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+            for (int j = 0; j < NJ; ++j) {
+                const int r0 = w0 + j * ROWS_PER_INST;
+                const int64_t base = int64_t(si.start + (r0 - si.c)) * new_row_bytes + head_off;
+                dma16(kn_bytes + base, lrow_new + k_chunk(lrow, pc, j), kdst + (NJ * wave + j) * 512);
+                dma16(vn_bytes + base, v_lane, vdst + (NJ * wave + j) * 512);
+            }
+        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int wv = e >> 1;
-                uint2 pk;
-                if (e & 1) {
-                    pk.x = interleave_hi(w0[wv], w1[wv]);
-                    pk.y = interleave_hi(w2[wv], w3[wv]);
+            for (int j = 0; j < NJ; ++j) {
+                const int kk = min(w0 + j * ROWS_PER_INST + lrow, key_hi);
+                int64_t off;
+                const char *kb_, *vb_;
+                if (kk < si.c) {
+                    int64_t blk = p.block_tables[int64_t(seq) * p.max_blocks + (kk >> p.block_shift)];
+                    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+                    off = blk * block_bytes + int64_t(kk & bmask) * cache_row_bytes + head_off;
+                    kb_ = kc_bytes;
+                    vb_ = vc_bytes;
                 } else {
-                    pk.x = interleave_lo(w0[wv], w1[wv]);
-                    pk.y = interleave_lo(w2[wv], w3[wv]);
+                    off = int64_t(si.start + (kk - si.c)) * new_row_bytes + head_off;
+                    kb_ = kn_bytes;
+                    vb_ = vn_bytes;
                 }
-                *reinterpret_cast<uint2 *>(&Vt[stage][vt_index(8 * v_ch + e, kp0)]) = pk;
+                dma16_lane(kb_ + off + k_chunk(lrow, pc, j), kdst + (NJ * wave + j) * 512);
+                dma16_lane(vb_ + off + v_chunk(lrow, pc), vdst + (NJ * wave + j) * 512);
             }
         }
     };
 
+    // ---- operand read offsets (elements), fixed for the whole loop.  Row 16 kb + l16 of K has
+    // row % CH == l16 % CH, so the swizzle depends on the lane only and kb adds a constant.
+    int k_off[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) k_off[dc] = l16 * D + (((4 * dc + lg) ^ (l16 % CH)) << 3);
+    // V^T operand for (d-block db, key chunk kc, half hh): lane l16 = 4 a + c of group lg reads,
+    // through the transposing load, key 32 kc + 16 hh + 4 lg + a at d = 16 db + 4 c.  That key is
+    // == a (mod 4), so its 32-byte unit db sits at db ^ a: the low two bits of db pick one of four
+    // lane offsets and the rest of db, kc and hh add constants.
+    const int va = l16 >> 2;
+    int v_off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v_off[u] = (4 * lg + va) * D + ((u ^ va) << 4) + 4 * (l16 & 3);
     float m_run[2] = {-INFINITY, -INFINITY};   // row max (base 2), uniform over the row's 4 lanes
-    float l_run[2] = {0.f, 0.f};               // this lane's part of the row sum
     floatx4_v o[2][DB];
+    // Row sums of the rounded weights, accumulated by the MFMA unit: an all-ones block times P^T
+    // gives sum_k P[q][k] in every element of lane (q, .).
+    floatx4_v lsum[2];
+#pragma unroll
+    for (int qbk = 0; qbk < 2; ++qbk) {
+        lsum[qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[qbk][db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+    }
+    const bf16x8_v ones = __builtin_bit_cast(bf16x8_v, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const bool pos_scale = qk_scale > 0.f;
+    const int wlim = p.window > 0 ? p.window : 0x7fffffff;   // keys with x - rel >= wlim are outside the window
+
+    // One 64-key tile, taken as two 32-key halves (key chunk kc): S^T for the half, its visible
+    // logits and running max, P, then O^T += V^T P^T.  Halving keeps the live score and weight
+    // registers small enough for two workgroups per CU.
+    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) {
+        // x = pos - (kt * kBN + 4 lg): key 16 kb + i of this lane is visible iff 16 kb + i <= x
+        // and x - (16 kb + i) < W.  Interior tiles without ALiBi keep the raw MFMA values (the
+        // scale is folded into the exponent); other tiles get scale, bias and mask in place.
+        const bool full =
+            kt * kBN + kBN - 1 <= si.c + t0 && (p.window <= 0 || si.c + t0 + 31 - kt * kBN < p.window);
+        const bool simple = full && !has_alibi && pos_scale;            // uniform
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            // ---- S^T = K Q^T: s[kk][qbk] holds keys 32 kc + 16 kk + 4 lg + i of row 16 qbk + l16
+            floatx4_v s[2][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8_v a = *reinterpret_cast<const bf16x8_v *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
+#pragma unroll
+                    for (int qbk = 0; qbk < 2; ++qbk)
+                        s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qbk][dc], s[kk][qbk], 0, 0, 0);
+                }
+            }
+
+            float tmax[2];
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk) {
+                if (simple) {
+                    float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), fmaxf(s[0][qbk][2], s[0][qbk][3]));
+                    mx = fmaxf(mx, fmaxf(fmaxf(s[1][qbk][0], s[1][qbk][1]), fmaxf(s[1][qbk][2], s[1][qbk][3])));
+                    tmax[qbk] = mx * qk_scale;
+                } else {
+                    const int x = si.c + t0 + 16 * qbk + l16 - (kt * kBN + 4 * lg);
+                    const float bias0 = -slope2 * float(x);     // slope2 == 0 without ALiBi
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rel = 32 * kc + 16 * kk + i;
+                            const float v = fmaf(s[kk][qbk][i], qk_scale, fmaf(slope2, float(rel), bias0));
+                            const bool vis = (rel <= x) & (x - rel < wlim);
+                            s[kk][qbk][i] = vis ? v : -INFINITY;
+                            mx = fmaxf(mx, s[kk][qbk][i]);
+                        }
+                    tmax[qbk] = mx;
+                }
+            }
+            const bool raise = tmax[0] > m_run[0] + kRescaleSlack || tmax[1] > m_run[1] + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+                for (int qbk = 0; qbk < 2; ++qbk) {
+                    float r = fmaxf(tmax[qbk], lane_xor<16>(tmax[qbk]));
+                    r = fmaxf(r, lane_xor<32>(r));
+                    const float m_new = fmaxf(m_run[qbk], r);
+                    const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
+                    m_run[qbk] = m_new;
+                    lsum[qbk] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
+                }
+            }
+
+            // ---- P (bf16) as the B operand of O^T = V^T P^T: slots 0-3 are keys 32 kc + 4 lg + i,
+            // slots 4-7 keys 32 kc + 16 + 4 lg + i.  A row whose max is still -inf has seen no
+            // visible key; its weights are exp2(-inf) = 0 against a finite stand-in max.
+            bf16x8_v pb[2];
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk) {
+                const float m = m_run[qbk] == -INFINITY ? 0.f : m_run[qbk];
+                uint32_t pk[2][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    float pf[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pf[i] = simple ? fast_exp2(fmaf(s[kk][qbk][i], qk_scale, -m)) : fast_exp2(s[kk][qbk][i] - m);
+                    pk[kk][0] = pack_bf16x2(pf[0], pf[1]);
+                    pk[kk][1] = pack_bf16x2(pf[2], pf[3]);
+                }
+                pb[qbk] = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+            }
+
+            // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile), row sums += 1^T P^T
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16_t *vb = vs + v_off[db & 3] + ((db & ~3) << 4) + 32 * kc * D;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
+                const v4i16 both[2] = {lo, hi};
+                const bf16x8_v a = __builtin_bit_cast(bf16x8_v, both);
+#pragma unroll
+                for (int qbk = 0; qbk < 2; ++qbk)
+                    o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qbk], o[qbk][db], 0, 0, 0);
+            }
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk)
+                lsum[qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qbk], lsum[qbk], 0, 0, 0);
+        }
+    };
+
+    // ---- pipeline: while tile kt is computed from one LDS stage, tile kt + 1 streams into the
+    // other; block ids run two tiles ahead.  The loop is unrolled by two so each stage is a
+    // distinct LDS object.
+    // The explicit vmcnt(0) waits cover every global load of the loop (copies, ids); passing the
+    // loaded registers through an empty asm after them keeps the compiler from adding waits of
+    // its own further down, which would also wait for the copies in flight.
+    int ids = fetch_ids(kt_lo);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" : "+v"(ids));
+    copy_tile(kt_lo, ids, Ks0, Vs0);
+    ids = fetch_ids(kt_lo + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wavefront's copies, ids and Q landed
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[qbk][db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
-
-    // ---- prologue: tile kt_lo into stage 0; ids of the next two tiles in flight
-    {
-        int kid, vid;
-        fetch_ids(kt_lo, kid, vid);
-        load_tile(kt_lo, kid, vid);
-        fetch_ids(kt_lo + 1, kid_a, vid_a);
-        fetch_ids(kt_lo + 2, kid_b, vid_b);
-        store_tile(0);
+        for (int dc = 0; dc < DC; ++dc) asm volatile("" : "+v"(qf[qbk][dc]));
+    asm volatile("" : "+v"(ids));
+    __syncthreads();
+    for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+        if (kt < kt_hi) {
+            copy_tile(kt + 1, ids, Ks1, Vs1);
+            ids = fetch_ids(kt + 2);
+        }
+        compute_tile(kt, Ks0, Vs0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" : "+v"(ids));
         __syncthreads();
-    }
-
-    int stage = 0;
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-        const bool more = kt < kt_hi;
-        if (more) {
-            load_tile(kt + 1, kid_a, vid_a);     // data of the next tile in flight during this one
-            kid_a = kid_b;
-            vid_a = vid_b;
-            fetch_ids(kt + 3, kid_b, vid_b);
+        if (kt + 1 > kt_hi) break;
+        if (kt + 1 < kt_hi) {
+            copy_tile(kt + 2, ids, Ks0, Vs0);
+            ids = fetch_ids(kt + 3);
         }
-
-        // ---- S^T = K Q^T: s[kb][qbk] holds keys 16 kb + 4 lg + i of row 16 qbk + l16
-        floatx4_v s[4][2];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int qbk = 0; qbk < 2; ++qbk) s[kb][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
-        const bf16_t *ks = Ks[stage];
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int row = 16 * kb + l16;
-                const bf16x8_v a = *reinterpret_cast<const bf16x8_v *>(&ks[row * D + (((4 * dc + lg) ^ (row % CH)) << 3)]);
-#pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk)
-                    s[kb][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qbk][dc], s[kb][qbk], 0, 0, 0);
-            }
-        }
-
-        // ---- scale, bias, mask (edge tiles only), lazily raised row max
-        const int kbase = kt * kBN + 4 * lg;
-        const bool full = kt * kBN + kBN - 1 <= si.c + t0 && (p.window <= 0 || si.c + t0 + 31 - kt * kBN < p.window);
-        float tmax[2];
-#pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-            const int pos = si.c + t0 + 16 * qbk + l16;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = s[kb][qbk][i] * qk_scale;
-                    if (has_alibi) v += slope2 * float(kbase + 16 * kb + i - pos);
-                    if (!full) {
-                        const int key = kbase + 16 * kb + i;
-                        const bool vis = key <= pos && (p.window <= 0 || pos - key < p.window);
-                        v = vis ? v : -INFINITY;
-                    }
-                    s[kb][qbk][i] = v;
-                    mx = fmaxf(mx, v);
-                }
-            tmax[qbk] = mx;
-        }
-        const bool raise = tmax[0] > m_run[0] + kRescaleSlack || tmax[1] > m_run[1] + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-#pragma unroll
-            for (int qbk = 0; qbk < 2; ++qbk) {
-                float r = fmaxf(tmax[qbk], lane_xor<16>(tmax[qbk]));
-                r = fmaxf(r, lane_xor<32>(r));
-                const float m_new = fmaxf(m_run[qbk], r);
-                const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
-                l_run[qbk] *= alpha;
-                m_run[qbk] = m_new;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
-            }
-        }
-
-        // ---- P (bf16) as the B operand of O^T = V^T P^T
-        bf16x8_v pb[2][2];
-#pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-            const float m = m_run[qbk];
-            float psum = 0.f;
-            uint32_t pk[4][2];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                float pf[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = s[kb][qbk][i];
-                    pf[i] = (x == -INFINITY) ? 0.f : fast_exp2(x - m);
-                }
-                pk[kb][0] = pack_bf16x2(pf[0], pf[1]);
-                pk[kb][1] = pack_bf16x2(pf[2], pf[3]);
-                psum += bf16_lo(pk[kb][0]) + bf16_hi(pk[kb][0]) + bf16_lo(pk[kb][1]) + bf16_hi(pk[kb][1]);
-            }
-            l_run[qbk] += psum;
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const uint4 w = make_uint4(pk[2 * kc][0], pk[2 * kc][1], pk[2 * kc + 1][0], pk[2 * kc + 1][1]);
-                pb[qbk][kc] = __builtin_bit_cast(bf16x8_v, w);
-            }
-        }
-
-        // ---- O^T += V^T P^T
-        const bf16_t *vt = Vt[stage];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = 16 * db + l16;
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const bf16x8_v a = *reinterpret_cast<const bf16x8_v *>(&vt[vt_index(d, 32 * kc + 8 * lg)]);
-#pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk)
-                    o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qbk][kc], o[qbk][db], 0, 0, 0);
-            }
-        }
-
-        if (more) store_tile(stage ^ 1);
+        compute_tile(kt + 1, Ks1, Vs1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" : "+v"(ids));
         __syncthreads();
-        stage ^= 1;
     }
 
     // ---- epilogue: O = O^T / l, rounded to bf16; lane holds d = 16 db + 4 lg + i of its row
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
-        float l = l_run[qbk];
-        l += lane_xor<16>(l);
-        l += lane_xor<32>(l);
         const int trow = t0 + 16 * qbk + l16;
         if (trow < si.n) {
-            const float inv = 1.f / l;
+            const float inv = 1.f / lsum[qbk][0];
             bf16_t *orow = reinterpret_cast<bf16_t *>(p.out) + int64_t(si.start + trow) * p.num_heads * D +
                            int64_t(h) * D + 4 * lg;
 #pragma unroll
