@@ -25,9 +25,11 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
     return __builtin_bit_cast(bf16_t, b);
 }
 
-// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    typedef float float2_v __attribute__((ext_vector_type(2)));
+    const float2_v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
 
 // c + a.lo * b.lo + a.hi * b.hi with bf16 pairs (v_dot2_f32_bf16).

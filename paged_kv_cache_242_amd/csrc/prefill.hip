@@ -94,13 +94,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// One 16-byte-per-lane global -> LDS copy: lane l reads base + lane_off (bytes) and fills
-// 16-byte unit l of the 1 KB stretch at lds_dst.  base must be wave-uniform; it goes into a raw
-// buffer descriptor (kept in scalar registers) and the lane offset into the vector offset.
-__device__ __forceinline__ void dma16(const char *base, uint32_t lane_off, bf16_t *lds_dst) {
+// One 16-byte-per-lane global -> LDS copy: lane l reads base + soff + lane_off (bytes) and fills
+// 16-byte unit l of the 1 KB stretch at lds_dst.  base and soff must be wave-uniform; base goes
+// into a raw buffer descriptor (scalar registers), soff into the scalar offset and the lane
+// offset into the vector offset.
+__device__ __forceinline__ void dma16(const char *base, uint32_t lane_off, uint32_t soff, bf16_t *lds_dst) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, lane_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, lane_off, soff, 0, 0);
 }
 
 // The same copy from a per-lane address.
@@ -117,15 +118,25 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 //   V: row-major [64][D], 32-byte unit u of key k stored at unit u ^ (k % 4); the transposing
 //      operand read (ds_read_b64_tr_b16: 4 keys x 32 bytes per 16 lanes) then hits distinct
 //      banks.
-// Each wavefront copies 16 keys (rows 16 w .. 16 w + 15) of each tile, so one or two block ids
-// per wavefront and tile suffice; they are scalar loads issued two tiles ahead.
+// Each wavefront copies 16 keys (rows 16 w .. 16 w + 15) of each tile, which lie in one cache
+// block (two for 8-token blocks), so one descriptor per block and tile serves all its copies.
+//
+// Scores.  A wavefront's 32 rows meet a tile in two 32-key halves.  Per half the scores are
+// kept in raw units s (q.k, plus for ALiBi the in-half key offset times slope / |scale|, added
+// by one rank-1 MFMA per score block); the base-2 logit is s * |scale| log2(e) + c_row with a
+// per-row constant c_row (the ALiBi term of the half's first key, else 0).  A half is
+//   * empty for the wavefront when every (row, key) pair is masked -- skipped entirely;
+//   * full when none is -- no per-score work besides the max and the exponent;
+//   * partial otherwise -- masked scores are set to -inf.
+// A negative scale is folded into a sign flip of Q (exact in bf16), a zero scale into Q = 0.
 
-template <int D>
+template <int D, bool ALIBI>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams p, PrefillGrid grid) {
     constexpr int CH = D / 8;        // 16-byte chunks per row
     constexpr int DC = D / 32;       // k-chunks of S^T
     constexpr int DB = D / 16;       // d-blocks of O^T
-    constexpr int NJ = CH / 4;       // DMA instructions per wavefront per operand per tile
+    constexpr int RPI = 64 / CH;     // tile rows per copy instruction (4 or 8)
+    constexpr int NJ = 16 / RPI;     // copy instructions per wavefront per operand per tile
     constexpr int ROWB = D * 2;      // bytes per tile row
     __shared__ __align__(16) bf16_t Ks0[kBN * D];
     __shared__ __align__(16) bf16_t Vs0[kBN * D];
@@ -154,9 +165,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int lg = lane >> 4;
-    const int t0 = qt * kBM + wave * 32;
+    const int t0 = qt * kBM + wave * 32;     // first subquery row of this wavefront
+    const int p0 = si.c + t0;                // its position
 
-    // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qb + l16), d = 32 dc + 8 lg .. +7.
+    const float qk_scale = p.scale * kLog2e;
+    const float qk_eff = qk_scale > 0.f ? qk_scale : (qk_scale < 0.f ? -qk_scale : 1.f);
+    const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // bf16 sign flips
+    const uint32_t qand = qk_scale == 0.f ? 0u : 0xffffffffu;
+
+    // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qbk + l16), d = 32 dc + 8 lg .. +7.
     bf16x8_v qf[2][DC];
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
@@ -164,7 +181,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         const bf16_t *qrow = reinterpret_cast<const bf16_t *>(p.query) + int64_t(si.start + trow) * p.q_stride +
                              int64_t(h) * D + 8 * lg;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) qf[qbk][dc] = *reinterpret_cast<const bf16x8_v *>(qrow + 32 * dc);
+        for (int dc = 0; dc < DC; ++dc) {
+            uint4 w = *reinterpret_cast<const uint4 *>(qrow + 32 * dc);
+            w.x = (w.x ^ qxor) & qand;
+            w.y = (w.y ^ qxor) & qand;
+            w.z = (w.z ^ qxor) & qand;
+            w.w = (w.w ^ qxor) & qand;
+            qf[qbk][dc] = __builtin_bit_cast(bf16x8_v, w);
+        }
     }
 
     const int row_hi = min(qt * kBM + kBM, si.n) - 1;
@@ -172,14 +196,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const int key_hi = si.c + row_hi;
     const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
     const int kt_lo = key_lo / kBN, kt_hi = key_hi / kBN;
-    const float qk_scale = p.scale * kLog2e;
-    const float slope2 = p.alibi_slopes ? p.alibi_slopes[h] * kLog2e : 0.f;
-    const bool has_alibi = p.alibi_slopes != nullptr;
 
-    // ---- DMA addressing.  Wavefront w, instruction j copies tile rows (NJ w + j) * (64 / CH) ..;
-    // lane l lands in 16-byte unit l of that 1 KB stretch: row (NJ w + j) * (64 / CH) + l / CH,
-    // physical chunk l % CH, which holds logical chunk kchunk (K) / vchunk (V).
-    constexpr int ROWS_PER_INST = 64 / CH;                  // 4 (D = 128) or 8 (D = 64)
+    // ALiBi: slope in base-2 units; the rank-1 MFMA term adds (key - half start) * slope2 / qk_eff
+    // to the raw scores, with the factor split into a bf16 high and low part (k slots 0 and 1).
+    float slope2 = 0.f;
+    bf16x8_v bslope = {}, arel[2] = {};
+    if constexpr (ALIBI) {
+        slope2 = p.alibi_slopes[h] * kLog2e;
+        const float ratio = slope2 / qk_eff;
+        const bf16_t hi = f32_to_bf16(ratio);
+        const bf16_t lo = f32_to_bf16(ratio - bf16_to_f32(hi));
+        const uint32_t hl = lane < 16 ? (uint32_t(hi) | (uint32_t(lo) << 16)) : 0u;
+        bslope = __builtin_bit_cast(bf16x8_v, make_uint4(hl, 0u, 0u, 0u));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16_t r = f32_to_bf16(float(16 * kk + l16));
+            const uint32_t rr = lane < 16 ? (uint32_t(r) | (uint32_t(r) << 16)) : 0u;
+            arel[kk] = __builtin_bit_cast(bf16x8_v, make_uint4(rr, 0u, 0u, 0u));
+        }
+    }
+
+    // ---- copies
     const char *kc_bytes = reinterpret_cast<const char *>(p.k_cache);
     const char *vc_bytes = reinterpret_cast<const char *>(p.v_cache);
     const char *kn_bytes = reinterpret_cast<const char *>(p.key);
@@ -189,26 +226,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const int64_t new_row_bytes = int64_t(p.kv_stride) * 2;
     const int64_t block_bytes = cache_row_bytes << p.block_shift;
     const int bmask = (1 << p.block_shift) - 1;
+    const int wrow0 = 16 * wave;                            // first tile row this wavefront copies
     // Lane terms of the copy addresses: the lane's row among its instruction's rows and the
     // logical chunk its physical LDS unit holds (the residues of the row mod CH and mod 4 depend
     // only on j and the lane).  They are rebuilt from the lane id at every copy -- a few ALU ops --
     // rather than held in registers across the loop.
-    auto lane_terms = [&](int &lrow, int &pc) {
+    auto lane_terms = [&](int &lrow, int &pc) __attribute__((always_inline)) {
         int l;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
         lrow = l / CH;
         pc = l % CH;
     };
-    auto k_chunk = [&](int lrow, int pc, int j) -> uint32_t {
-        return uint32_t(pc ^ ((j * ROWS_PER_INST + lrow) % CH)) * 16;
+    auto k_chunk = [&](int lrow, int pc, int j) __attribute__((always_inline)) -> uint32_t {
+        return uint32_t(pc ^ ((j * RPI + lrow) % CH)) * 16;
     };
-    auto v_chunk = [&](int lrow, int pc) -> uint32_t {
+    auto v_chunk = [&](int lrow, int pc) __attribute__((always_inline)) -> uint32_t {
         return uint32_t((((pc >> 1) ^ (lrow & 3)) * 2 + (pc & 1)) * 16);
     };
-    const int wrow0 = 16 * wave;                            // first tile row this wavefront copies
+    auto clamp_block = [&](int64_t bl) __attribute__((always_inline)) -> int64_t {
+        return bl < 0 ? 0 : (bl >= p.num_blocks ? p.num_blocks - 1 : bl);
+    };
     // Block ids of this wavefront's 16 rows of tile kt: lane 0 gets the first row's block, lane 1
     // the last (cached) row's.  A vector load, so the wait at the end of the tile covers it.
-    auto fetch_ids = [&](int kt) -> int {
+    auto fetch_ids = [&](int kt) __attribute__((always_inline)) -> int {
         const int r0 = kt * kBN + wrow0;
         int id = 0;
         if (r0 < si.c) {
@@ -217,59 +257,58 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         }
         return id;
     };
-    auto clamp_block = [&](int64_t b) -> int64_t {
-        return b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
-    };
-    // Copy this wavefront's 16 rows of tile kt into (kdst, vdst).  The rows are all cached, all
-    // new and at or below key_hi (each instruction then has a uniform base address and a 32-bit
-    // lane offset), or -- at most twice per sequence -- mixed, which takes a per-lane path.  Rows
-    // past key_hi re-read row key_hi; every query row of the tile masks them.
-    auto copy_tile = [&](int kt, int ids, bf16_t *kdst, bf16_t *vdst) {
+    // Copy this wavefront's 16 rows of tile kt into (kdst, vdst); id0 / id1 are the blocks of its
+    // first and last cached row (wave-uniform).  The rows are all cached, all new and at or below
+    // key_hi (one descriptor per block, scalar offsets per instruction), or -- at most twice per
+    // sequence -- mixed, which takes a per-lane path.  Rows past key_hi re-read row key_hi; every
+    // query row masks them.
+    auto copy_tile = [&](int kt, int id0_raw, int id1_raw, bf16_t *kdst, bf16_t *vdst) __attribute__((always_inline)) {
         const int w0 = kt * kBN + wrow0;                  // first key of this wavefront (uniform)
         int lrow, pc;
         lane_terms(lrow, pc);
         if (w0 + 15 < si.c) {
-            const int64_t id0 = clamp_block(__builtin_amdgcn_readlane(ids, 0));
-            const int64_t id1 = clamp_block(__builtin_amdgcn_readlane(ids, 1));
-            const uint32_t lrow_cache = uint32_t(lrow) * uint32_t(cache_row_bytes);
-            const uint32_t v_lane = lrow_cache + v_chunk(lrow, pc);
+            const int64_t off0 = clamp_block(id0_raw) * block_bytes + head_off + int64_t(w0 & bmask) * cache_row_bytes;
+            const int64_t off1 = clamp_block(id1_raw) * block_bytes + head_off;
+            const uint32_t lro = uint32_t(lrow) * uint32_t(cache_row_bytes);
+            const uint32_t vl = lro + v_chunk(lrow, pc);
+            const bool one_block = (1 << p.block_shift) >= 16;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int r0 = w0 + j * ROWS_PER_INST;
-                const int64_t blk = ((r0 >> p.block_shift) == (w0 >> p.block_shift)) ? id0 : id1;
-                const int64_t base = blk * block_bytes + head_off + int64_t(r0 & bmask) * cache_row_bytes;
-                dma16(kc_bytes + base, lrow_cache + k_chunk(lrow, pc, j), kdst + (NJ * wave + j) * 512);
-                dma16(vc_bytes + base, v_lane, vdst + (NJ * wave + j) * 512);
+                const bool second = !one_block && j >= NJ / 2;
+                const int64_t off = second ? off1 : off0;
+                const uint32_t soff = uint32_t((second ? j - NJ / 2 : j) * RPI) * uint32_t(cache_row_bytes);
+                dma16(kc_bytes + off, lro + k_chunk(lrow, pc, j), soff, kdst + (NJ * wave + j) * 512);
+                dma16(vc_bytes + off, vl, soff, vdst + (NJ * wave + j) * 512);
             }
         } else if (w0 >= si.c && w0 + 15 <= key_hi) {
-            const uint32_t lrow_new = uint32_t(lrow) * uint32_t(new_row_bytes);
-            const uint32_t v_lane = lrow_new + v_chunk(lrow, pc);
+            const int64_t off = int64_t(si.start + (w0 - si.c)) * new_row_bytes + head_off;
+            const uint32_t lro = uint32_t(lrow) * uint32_t(new_row_bytes);
+            const uint32_t vl = lro + v_chunk(lrow, pc);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int r0 = w0 + j * ROWS_PER_INST;
-                const int64_t base = int64_t(si.start + (r0 - si.c)) * new_row_bytes + head_off;
-                dma16(kn_bytes + base, lrow_new + k_chunk(lrow, pc, j), kdst + (NJ * wave + j) * 512);
-                dma16(vn_bytes + base, v_lane, vdst + (NJ * wave + j) * 512);
+                const uint32_t soff = uint32_t(j * RPI) * uint32_t(new_row_bytes);
+                dma16(kn_bytes + off, lro + k_chunk(lrow, pc, j), soff, kdst + (NJ * wave + j) * 512);
+                dma16(vn_bytes + off, vl, soff, vdst + (NJ * wave + j) * 512);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int kk = min(w0 + j * ROWS_PER_INST + lrow, key_hi);
-                int64_t off;
-                const char *kb_, *vb_;
-                if (kk < si.c) {
-                    int64_t blk = p.block_tables[int64_t(seq) * p.max_blocks + (kk >> p.block_shift)];
-                    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
-                    off = blk * block_bytes + int64_t(kk & bmask) * cache_row_bytes + head_off;
-                    kb_ = kc_bytes;
-                    vb_ = vc_bytes;
+                const int kk = min(w0 + j * RPI + lrow, key_hi);
+                const bool cached = kk < si.c;
+                const int64_t bl = clamp_block(
+                    p.block_tables[int64_t(seq) * p.max_blocks + (min(kk, max(si.c - 1, 0)) >> p.block_shift)]);
+                const int64_t off = cached ? bl * block_bytes + int64_t(kk & bmask) * cache_row_bytes + head_off
+                                           : int64_t(si.start + (kk - si.c)) * new_row_bytes + head_off;
+                bf16_t *kd = kdst + (NJ * wave + j) * 512;
+                bf16_t *vd = vdst + (NJ * wave + j) * 512;
+                // (a branch rather than a select of the two bases keeps the bases in scalar registers)
+                if (cached) {
+                    dma16_lane(kc_bytes + off + k_chunk(lrow, pc, j), kd);
+                    dma16_lane(vc_bytes + off + v_chunk(lrow, pc), vd);
                 } else {
-                    off = int64_t(si.start + (kk - si.c)) * new_row_bytes + head_off;
-                    kb_ = kn_bytes;
-                    vb_ = vn_bytes;
+                    dma16_lane(kn_bytes + off + k_chunk(lrow, pc, j), kd);
+                    dma16_lane(vn_bytes + off + v_chunk(lrow, pc), vd);
                 }
-                dma16_lane(kb_ + off + k_chunk(lrow, pc, j), kdst + (NJ * wave + j) * 512);
-                dma16_lane(vb_ + off + v_chunk(lrow, pc), vdst + (NJ * wave + j) * 512);
             }
         }
     };
@@ -287,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     int v_off[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v_off[u] = (4 * lg + va) * D + ((u ^ va) << 4) + 4 * (l16 & 3);
+
     float m_run[2] = {-INFINITY, -INFINITY};   // row max (base 2), uniform over the row's 4 lanes
     floatx4_v o[2][DB];
     // Row sums of the rounded weights, accumulated by the MFMA unit: an all-ones block times P^T
@@ -299,126 +339,144 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         for (int db = 0; db < DB; ++db) o[qbk][db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
     }
     const bf16x8_v ones = __builtin_bit_cast(bf16x8_v, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-    const bool pos_scale = qk_scale > 0.f;
-    const int wlim = p.window > 0 ? p.window : 0x7fffffff;   // keys with x - rel >= wlim are outside the window
 
-    // One 64-key tile, taken as two 32-key halves (key chunk kc): S^T for the half, its visible
-    // logits and running max, P, then O^T += V^T P^T.  Halving keeps the live score and weight
-    // registers small enough for two workgroups per CU.
-    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) {
-        // x = pos - (kt * kBN + 4 lg): key 16 kb + i of this lane is visible iff 16 kb + i <= x
-        // and x - (16 kb + i) < W.  Interior tiles without ALiBi keep the raw MFMA values (the
-        // scale is folded into the exponent); other tiles get scale, bias and mask in place.
-        const bool full =
-            kt * kBN + kBN - 1 <= si.c + t0 && (p.window <= 0 || si.c + t0 + 31 - kt * kBN < p.window);
-        const bool simple = full && !has_alibi && pos_scale;            // uniform
+    // One 32-key half (keys k0h .. k0h + 31, key chunk kc of the tile in (ks, vs)).
+    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
+        // wavefront rows are positions p0 .. p0 + 31; a key is visible from pos iff
+        // pos - W < key <= pos
+        const bool empty = k0h > p0 + 31 || (p.window > 0 && k0h + 31 <= p0 - p.window);
+        if (empty) return;
+        const bool full = k0h + 31 <= p0 && (p.window <= 0 || k0h > p0 + 31 - p.window);
+
+        // ---- S^T = K Q^T (+ ALiBi term): s[kk][qbk] holds keys k0h + 16 kk + 4 lg + i of row 16 qbk + l16
+        floatx4_v s[2][2];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            // ---- S^T = K Q^T: s[kk][qbk] holds keys 32 kc + 16 kk + 4 lg + i of row 16 qbk + l16
-            floatx4_v s[2][2];
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8_v a = *reinterpret_cast<const bf16x8_v *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
+#pragma unroll
+                for (int qbk = 0; qbk < 2; ++qbk)
+                    s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qbk][dc], s[kk][qbk], 0, 0, 0);
+            }
+        }
+        if constexpr (ALIBI) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8_v a = *reinterpret_cast<const bf16x8_v *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
-#pragma unroll
-                    for (int qbk = 0; qbk < 2; ++qbk)
-                        s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qbk][dc], s[kk][qbk], 0, 0, 0);
-                }
-            }
+                for (int qbk = 0; qbk < 2; ++qbk)
+                    s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arel[kk], bslope, s[kk][qbk], 0, 0, 0);
+        }
 
-            float tmax[2];
+        // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
+        // 16 kk + i <= x and x - (16 kk + i) < W, x = pos - k0h - 4 lg.
+        if (!full) {
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) {
-                if (simple) {
-                    float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), fmaxf(s[0][qbk][2], s[0][qbk][3]));
-                    mx = fmaxf(mx, fmaxf(fmaxf(s[1][qbk][0], s[1][qbk][1]), fmaxf(s[1][qbk][2], s[1][qbk][3])));
-                    tmax[qbk] = mx * qk_scale;
-                } else {
-                    const int x = si.c + t0 + 16 * qbk + l16 - (kt * kBN + 4 * lg);
-                    const float bias0 = -slope2 * float(x);     // slope2 == 0 without ALiBi
-                    float mx = -INFINITY;
+                const int x = p0 + 16 * qbk + l16 - k0h - 4 * lg;
+                if (p.window > 0) {
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int rel = 32 * kc + 16 * kk + i;
-                            const float v = fmaf(s[kk][qbk][i], qk_scale, fmaf(slope2, float(rel), bias0));
-                            const bool vis = (rel <= x) & (x - rel < wlim);
-                            s[kk][qbk][i] = vis ? v : -INFINITY;
-                            mx = fmaxf(mx, s[kk][qbk][i]);
+                            const int rel = 16 * kk + i;
+                            s[kk][qbk][i] = ((rel <= x) & (x - rel < p.window)) ? s[kk][qbk][i] : -INFINITY;
                         }
-                    tmax[qbk] = mx;
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            s[kk][qbk][i] = (16 * kk + i <= x) ? s[kk][qbk][i] : -INFINITY;
                 }
             }
-            const bool raise = tmax[0] > m_run[0] + kRescaleSlack || tmax[1] > m_run[1] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-#pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk) {
-                    float r = fmaxf(tmax[qbk], lane_xor<16>(tmax[qbk]));
-                    r = fmaxf(r, lane_xor<32>(r));
-                    const float m_new = fmaxf(m_run[qbk], r);
-                    const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
-                    m_run[qbk] = m_new;
-                    lsum[qbk] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
-                }
-            }
+        }
 
-            // ---- P (bf16) as the B operand of O^T = V^T P^T: slots 0-3 are keys 32 kc + 4 lg + i,
-            // slots 4-7 keys 32 kc + 16 + 4 lg + i.  A row whose max is still -inf has seen no
-            // visible key; its weights are exp2(-inf) = 0 against a finite stand-in max.
-            bf16x8_v pb[2];
+        // ---- running max (lazy: raised only when a row's max grows by more than kRescaleSlack)
+        float crow[2], tmax[2];
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+            crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
+            float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), fmaxf(s[0][qbk][2], s[0][qbk][3]));
+            mx = fmaxf(mx, fmaxf(fmaxf(s[1][qbk][0], s[1][qbk][1]), fmaxf(s[1][qbk][2], s[1][qbk][3])));
+            tmax[qbk] = fmaf(mx, qk_eff, crow[qbk]);
+        }
+        const bool raise = tmax[0] > m_run[0] + kRescaleSlack || tmax[1] > m_run[1] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) {
-                const float m = m_run[qbk] == -INFINITY ? 0.f : m_run[qbk];
-                uint32_t pk[2][2];
+                float r = fmaxf(tmax[qbk], lane_xor<16>(tmax[qbk]));
+                r = fmaxf(r, lane_xor<32>(r));
+                const float m_new = fmaxf(m_run[qbk], r);
+                const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
+                m_run[qbk] = m_new;
+                lsum[qbk] *= alpha;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    float pf[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        pf[i] = simple ? fast_exp2(fmaf(s[kk][qbk][i], qk_scale, -m)) : fast_exp2(s[kk][qbk][i] - m);
-                    pk[kk][0] = pack_bf16x2(pf[0], pf[1]);
-                    pk[kk][1] = pack_bf16x2(pf[2], pf[3]);
-                }
-                pb[qbk] = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+                for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
             }
+        }
 
-            // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile), row sums += 1^T P^T
+        // ---- P (bf16) as the B operand of O^T = V^T P^T: slots 0-3 are keys k0h + 4 lg + i,
+        // slots 4-7 keys k0h + 16 + 4 lg + i.  A row whose max is still -inf has seen no visible
+        // key; its weights are exp2(-inf) = 0 against a finite stand-in max.
+        bf16x8_v pb[2];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16_t *vb = vs + v_off[db & 3] + ((db & ~3) << 4) + 32 * kc * D;
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
-                const v4i16 both[2] = {lo, hi};
-                const bf16x8_v a = __builtin_bit_cast(bf16x8_v, both);
+        for (int qbk = 0; qbk < 2; ++qbk) {
+            const float off = crow[qbk] - (m_run[qbk] == -INFINITY ? 0.f : m_run[qbk]);
+            uint32_t pk[2][2];
 #pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk)
-                    o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qbk], o[qbk][db], 0, 0, 0);
+            for (int kk = 0; kk < 2; ++kk) {
+                float pf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pf[i] = fast_exp2(fmaf(s[kk][qbk][i], qk_eff, off));
+                pk[kk][0] = pack_bf16x2(pf[0], pf[1]);
+                pk[kk][1] = pack_bf16x2(pf[2], pf[3]);
             }
+            pb[qbk] = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+        }
+
+        // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile), row sums += 1^T P^T
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const bf16_t *vb = vs + v_off[db & 3] + ((db & ~3) << 4) + 32 * kc * D;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
+            const v4i16 both[2] = {lo, hi};
+            const bf16x8_v a = __builtin_bit_cast(bf16x8_v, both);
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk)
-                lsum[qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qbk], lsum[qbk], 0, 0, 0);
+                o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qbk], o[qbk][db], 0, 0, 0);
         }
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk)
+            lsum[qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qbk], lsum[qbk], 0, 0, 0);
+    };
+    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
+        half(kt * kBN, 0, ks, vs);
+        half(kt * kBN + 32, 1, ks, vs);
     };
 
     // ---- pipeline: while tile kt is computed from one LDS stage, tile kt + 1 streams into the
     // other; block ids run two tiles ahead.  The loop is unrolled by two so each stage is a
-    // distinct LDS object.
-    // The explicit vmcnt(0) waits cover every global load of the loop (copies, ids); passing the
-    // loaded registers through an empty asm after them keeps the compiler from adding waits of
-    // its own further down, which would also wait for the copies in flight.
-    int ids = fetch_ids(kt_lo);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    asm volatile("" : "+v"(ids));
-    copy_tile(kt_lo, ids, Ks0, Vs0);
-    ids = fetch_ids(kt_lo + 1);
+    // distinct LDS object.  The explicit vmcnt(0) waits cover every global load of the loop
+    // (copies, ids); passing the loaded registers through an empty asm after them keeps the
+    // compiler from adding waits of its own further down, which would also wait for the copies
+    // in flight.  The first tile's ids are scalar loads, so its copies go out together with Q.
+    {
+        int i0 = 0, i1 = 0;
+        const int r0 = kt_lo * kBN + wrow0;
+        if (r0 < si.c) {
+            const int32_t *tab = p.block_tables + int64_t(seq) * p.max_blocks;
+            i0 = tab[r0 >> p.block_shift];
+            i1 = tab[min(r0 + 15, si.c - 1) >> p.block_shift];
+        }
+        copy_tile(kt_lo, i0, i1, Ks0, Vs0);
+    }
+    int ids = fetch_ids(kt_lo + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wavefront's copies, ids and Q landed
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk)
@@ -428,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     __syncthreads();
     for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
         if (kt < kt_hi) {
-            copy_tile(kt + 1, ids, Ks1, Vs1);
+            copy_tile(kt + 1, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks1, Vs1);
             ids = fetch_ids(kt + 2);
         }
         compute_tile(kt, Ks0, Vs0);
@@ -437,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         __syncthreads();
         if (kt + 1 > kt_hi) break;
         if (kt + 1 < kt_hi) {
-            copy_tile(kt + 2, ids, Ks0, Vs0);
+            copy_tile(kt + 2, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks0, Vs0);
             ids = fetch_ids(kt + 3);
         }
         compute_tile(kt + 1, Ks1, Vs1);
@@ -547,10 +605,16 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipS
         const int64_t blocks = (groups + 7) / 8 * 8 * grid.group_size;
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
         grid.num_groups = int(groups);
-        if (head_size == 128)
-            hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p, grid);
+        const dim3 nb = dim3(unsigned(blocks)), nt = dim3(kThreads);
+        const bool alibi = p.alibi_slopes != nullptr;
+        if (head_size == 128 && alibi)
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), nb, nt, 0, stream, p, grid);
+        else if (head_size == 128)
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), nb, nt, 0, stream, p, grid);
+        else if (head_size == 64 && alibi)
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), nb, nt, 0, stream, p, grid);
         else if (head_size == 64)
-            hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p, grid);
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), nb, nt, 0, stream, p, grid);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();

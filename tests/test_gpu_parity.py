@@ -87,6 +87,8 @@ DECODE_LAYERS = [
     _layer(32, 2, 128, 16, window=300),     # 16 heads per KV head: two head groups
     _layer(4, 4, 128, 32, wl.F32, alibi=True, window=37),
     _layer(6, 3, 64, 256, alibi=True),
+    _layer(8, 2, 128, 16, scale=-0.09),     # negative scale
+    _layer(8, 8, 64, 16, alibi=True, scale=0.0),   # zero scale: weights from ALiBi alone
 ]
 DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
 
@@ -150,6 +152,10 @@ PREFILL_LAYERS = [
     _layer(12, 4, 128, 16, window=64),
     _layer(4, 1, 128, 8, alibi=True),
     _layer(4, 2, 128, 16, wl.F32, alibi=True, window=50),
+    _layer(8, 4, 64, 8, window=40),                     # 8-token blocks at D = 64
+    _layer(8, 2, 128, 16, scale=-0.09),                 # negative scale
+    _layer(8, 8, 64, 16, alibi=True, scale=0.0),        # zero scale: weights from ALiBi alone
+    _layer(4, 4, 128, 32, alibi=True, window=700),
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
