@@ -456,27 +456,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             lsum[qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qbk], lsum[qbk], 0, 0, 0);
     };
     auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
-        half(kt * kBN, 0, ks, vs);
         half(kt * kBN + 32, 1, ks, vs);
+        half(kt * kBN, 0, ks, vs);
     };
 
-    // ---- pipeline: while tile kt is computed from one LDS stage, tile kt + 1 streams into the
-    // other; block ids run two tiles ahead.  The loop is unrolled by two so each stage is a
-    // distinct LDS object.  The explicit vmcnt(0) waits cover every global load of the loop
-    // (copies, ids); passing the loaded registers through an empty asm after them keeps the
-    // compiler from adding waits of its own further down, which would also wait for the copies
-    // in flight.  The first tile's ids are scalar loads, so its copies go out together with Q.
+    // ---- pipeline.  Tiles are taken from the last (nearest the diagonal) to the first: with
+    // ALiBi the largest logits of a row sit near its own position, so the running max is found
+    // early and later tiles rarely raise it.  While tile kt is computed from one LDS stage, tile
+    // kt - 1 streams into the other; block ids run two tiles ahead.  The loop is unrolled by two
+    // so each stage is a distinct LDS object.  The explicit vmcnt(0) waits cover every global
+    // load of the loop (copies, ids); passing the loaded registers through an empty asm after
+    // them keeps the compiler from adding waits of its own further down, which would also wait
+    // for the copies in flight.  The first tile's ids are scalar loads, so its copies go out
+    // together with Q.
     {
         int i0 = 0, i1 = 0;
-        const int r0 = kt_lo * kBN + wrow0;
+        const int r0 = kt_hi * kBN + wrow0;
         if (r0 < si.c) {
             const int32_t *tab = p.block_tables + int64_t(seq) * p.max_blocks;
             i0 = tab[r0 >> p.block_shift];
             i1 = tab[min(r0 + 15, si.c - 1) >> p.block_shift];
         }
-        copy_tile(kt_lo, i0, i1, Ks0, Vs0);
+        copy_tile(kt_hi, i0, i1, Ks0, Vs0);
     }
-    int ids = fetch_ids(kt_lo + 1);
+    int ids = kt_hi > kt_lo ? fetch_ids(kt_hi - 1) : 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wavefront's copies, ids and Q landed
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk)
@@ -484,21 +487,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         for (int dc = 0; dc < DC; ++dc) asm volatile("" : "+v"(qf[qbk][dc]));
     asm volatile("" : "+v"(ids));
     __syncthreads();
-    for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-        if (kt < kt_hi) {
-            copy_tile(kt + 1, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks1, Vs1);
-            ids = fetch_ids(kt + 2);
+    for (int kt = kt_hi; kt >= kt_lo; kt -= 2) {
+        if (kt > kt_lo) {
+            copy_tile(kt - 1, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks1, Vs1);
+            if (kt - 2 >= kt_lo) ids = fetch_ids(kt - 2);
         }
         compute_tile(kt, Ks0, Vs0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         asm volatile("" : "+v"(ids));
         __syncthreads();
-        if (kt + 1 > kt_hi) break;
-        if (kt + 1 < kt_hi) {
-            copy_tile(kt + 2, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks0, Vs0);
-            ids = fetch_ids(kt + 3);
+        if (kt - 1 < kt_lo) break;
+        if (kt - 1 > kt_lo) {
+            copy_tile(kt - 2, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks0, Vs0);
+            if (kt - 3 >= kt_lo) ids = fetch_ids(kt - 3);
         }
-        compute_tile(kt + 1, Ks1, Vs1);
+        compute_tile(kt - 1, Ks1, Vs1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         asm volatile("" : "+v"(ids));
         __syncthreads();
