@@ -94,6 +94,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// V tile swizzle of row r: spreads the 8 rows read together by 32 lanes of the transposing load
+// (4 rows at 8 bytes per lane in each 16-lane group) over distinct 32-byte units of a 256-byte
+// bank window.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    return D == 128 ? (r & 7) : ((r >> 1) & 3);
+}
+
 // One 16-byte-per-lane global -> LDS copy: lane l reads base + soff + lane_off (bytes) and fills
 // 16-byte unit l of the 1 KB stretch at lds_dst.  base and soff must be wave-uniform; base goes
 // into a raw buffer descriptor (scalar registers), soff into the scalar offset and the lane
@@ -115,9 +123,9 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 // which 16-byte chunk of the source row to fetch:
 //   K: row-major [64][D], chunk c of row r stored at chunk c ^ (r % CH); the S^T operand read
 //      (16 rows, same chunk) then hits distinct banks.
-//   V: row-major [64][D], 32-byte unit u of key k stored at unit u ^ (k % 4); the transposing
-//      operand read (ds_read_b64_tr_b16: 4 keys x 32 bytes per 16 lanes) then hits distinct
-//      banks.
+//   V: row-major [64][D], 32-byte unit u of key k stored at unit u ^ vswz(k); the transposing
+//      operand read (ds_read_b64_tr_b16: 4 keys x 32 bytes per 16 lanes, 8 keys per 32 lanes)
+//      then hits distinct banks.
 // Each wavefront copies 16 keys (rows 16 w .. 16 w + 15) of each tile, which lie in one cache
 // block (two for 8-token blocks), so one descriptor per block and tile serves all its copies.
 //
@@ -240,8 +248,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     auto k_chunk = [&](int lrow, int pc, int j) __attribute__((always_inline)) -> uint32_t {
         return uint32_t(pc ^ ((j * RPI + lrow) % CH)) * 16;
     };
-    auto v_chunk = [&](int lrow, int pc) __attribute__((always_inline)) -> uint32_t {
-        return uint32_t((((pc >> 1) ^ (lrow & 3)) * 2 + (pc & 1)) * 16);
+    // V swizzle: the 32-byte unit u of tile row r sits at unit u ^ vswz(r); vswz depends on r only
+    // through r mod 8 (D = 128) or r mod 8 / 2 (D = 64), so rows 16 w + j RPI + lrow and
+    // j RPI + lrow share it.
+    auto v_chunk = [&](int lrow, int pc, int j) __attribute__((always_inline)) -> uint32_t {
+        return uint32_t((((pc >> 1) ^ vswz<D>(j * RPI + lrow)) * 2 + (pc & 1)) * 16);
     };
     auto clamp_block = [&](int64_t bl) __attribute__((always_inline)) -> int64_t {
         return bl < 0 ? 0 : (bl >= p.num_blocks ? p.num_blocks - 1 : bl);
@@ -270,7 +281,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             const int64_t off0 = clamp_block(id0_raw) * block_bytes + head_off + int64_t(w0 & bmask) * cache_row_bytes;
             const int64_t off1 = clamp_block(id1_raw) * block_bytes + head_off;
             const uint32_t lro = uint32_t(lrow) * uint32_t(cache_row_bytes);
-            const uint32_t vl = lro + v_chunk(lrow, pc);
             const bool one_block = (1 << p.block_shift) >= 16;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -278,17 +288,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
                 const int64_t off = second ? off1 : off0;
                 const uint32_t soff = uint32_t((second ? j - NJ / 2 : j) * RPI) * uint32_t(cache_row_bytes);
                 dma16(kc_bytes + off, lro + k_chunk(lrow, pc, j), soff, kdst + (NJ * wave + j) * 512);
-                dma16(vc_bytes + off, vl, soff, vdst + (NJ * wave + j) * 512);
+                dma16(vc_bytes + off, lro + v_chunk(lrow, pc, j), soff, vdst + (NJ * wave + j) * 512);
             }
         } else if (w0 >= si.c && w0 + 15 <= key_hi) {
             const int64_t off = int64_t(si.start + (w0 - si.c)) * new_row_bytes + head_off;
             const uint32_t lro = uint32_t(lrow) * uint32_t(new_row_bytes);
-            const uint32_t vl = lro + v_chunk(lrow, pc);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const uint32_t soff = uint32_t(j * RPI) * uint32_t(new_row_bytes);
                 dma16(kn_bytes + off, lro + k_chunk(lrow, pc, j), soff, kdst + (NJ * wave + j) * 512);
-                dma16(vn_bytes + off, vl, soff, vdst + (NJ * wave + j) * 512);
+                dma16(vn_bytes + off, lro + v_chunk(lrow, pc, j), soff, vdst + (NJ * wave + j) * 512);
             }
         } else {
 #pragma unroll
@@ -304,10 +313,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
                 // (a branch rather than a select of the two bases keeps the bases in scalar registers)
                 if (cached) {
                     dma16_lane(kc_bytes + off + k_chunk(lrow, pc, j), kd);
-                    dma16_lane(vc_bytes + off + v_chunk(lrow, pc), vd);
+                    dma16_lane(vc_bytes + off + v_chunk(lrow, pc, j), vd);
                 } else {
                     dma16_lane(kn_bytes + off + k_chunk(lrow, pc, j), kd);
-                    dma16_lane(vn_bytes + off + v_chunk(lrow, pc), vd);
+                    dma16_lane(vn_bytes + off + v_chunk(lrow, pc, j), vd);
                 }
             }
         }
@@ -319,13 +328,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) k_off[dc] = l16 * D + (((4 * dc + lg) ^ (l16 % CH)) << 3);
     // V^T operand for (d-block db, key chunk kc, half hh): lane l16 = 4 a + c of group lg reads,
-    // through the transposing load, key 32 kc + 16 hh + 4 lg + a at d = 16 db + 4 c.  That key is
-    // == a (mod 4), so its 32-byte unit db sits at db ^ a: the low two bits of db pick one of four
-    // lane offsets and the rest of db, kc and hh add constants.
+    // through the transposing load, key 32 kc + 16 hh + 4 lg + a at d = 16 db + 4 c.  32 kc + 16 hh
+    // does not change vswz of that key, so its unit db sits at db ^ vswz(4 lg + a): one lane offset
+    // per d-block, and kc and hh add constants.
     const int va = l16 >> 2;
-    int v_off[4];
+    int v_off[DB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v_off[u] = (4 * lg + va) * D + ((u ^ va) << 4) + 4 * (l16 & 3);
+    for (int u = 0; u < DB; ++u) v_off[u] = (4 * lg + va) * D + ((u ^ vswz<D>(4 * lg + va)) << 4) + 4 * (l16 & 3);
 
     float m_run[2] = {-INFINITY, -INFINITY};   // row max (base 2), uniform over the row's 4 lanes
     floatx4_v o[2][DB];
@@ -341,11 +350,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const bf16x8_v ones = __builtin_bit_cast(bf16x8_v, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
     // One 32-key half (keys k0h .. k0h + 31, key chunk kc of the tile in (ks, vs)).
-    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
+    // LDS operand reads are issued one phase ahead of their MFMAs: the K operands of a half are
+    // read while the previous half finishes (or right after the tile barrier for the first half
+    // of a tile), the V operands right after the half's S^T MFMAs, before its softmax.
+    bf16x8_v ka[DC][2];          // K operands of the coming half
+    bf16x8_v vop[DB];            // V^T operands of the current half
+    auto load_k = [&](const bf16_t *ks, int kc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                ka[dc][kk] = *reinterpret_cast<const bf16x8_v *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
+    };
+    auto load_v = [&](const bf16_t *vs, int kc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const bf16_t *vb = vs + v_off[db] + 32 * kc * D;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
+            const v4i16 both[2] = {lo, hi};
+            vop[db] = __builtin_bit_cast(bf16x8_v, both);
+        }
+    };
+
+    // One 32-key half (keys k0h .. k0h + 31, key chunk kc of the tile in (ks, vs)); ka holds its
+    // K operands on entry.  next_kc >= 0: the next half is chunk next_kc of the same tile, whose
+    // K operands are read into ka here.
+    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs, int next_kc) __attribute__((always_inline)) {
         // wavefront rows are positions p0 .. p0 + 31; a key is visible from pos iff
         // pos - W < key <= pos
         const bool empty = k0h > p0 + 31 || (p.window > 0 && k0h + 31 <= p0 - p.window);
-        if (empty) return;
+        if (empty) {
+            if (next_kc >= 0) load_k(ks, next_kc);
+            return;
+        }
         const bool full = k0h + 31 <= p0 && (p.window <= 0 || k0h > p0 + 31 - p.window);
 
         // ---- S^T = K Q^T (+ ALiBi term): s[kk][qbk] holds keys k0h + 16 kk + 4 lg + i of row 16 qbk + l16
@@ -355,15 +393,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
+        for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8_v a = *reinterpret_cast<const bf16x8_v *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int qbk = 0; qbk < 2; ++qbk)
-                    s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qbk][dc], s[kk][qbk], 0, 0, 0);
-            }
-        }
+                    s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[dc][kk], qf[qbk][dc], s[kk][qbk], 0, 0, 0);
         if constexpr (ALIBI) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -371,6 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
                 for (int qbk = 0; qbk < 2; ++qbk)
                     s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arel[kk], bslope, s[kk][qbk], 0, 0, 0);
         }
+        load_v(vs, kc);
 
         // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
         // 16 kk + i <= x and x - (16 kk + i) < W, x = pos - k0h - 4 lg.
@@ -420,6 +456,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             }
         }
 
+        if (next_kc >= 0) load_k(ks, next_kc);
+
         // ---- P (bf16) as the B operand of O^T = V^T P^T: slots 0-3 are keys k0h + 4 lg + i,
         // slots 4-7 keys k0h + 16 + 4 lg + i.  A row whose max is still -inf has seen no visible
         // key; its weights are exp2(-inf) = 0 against a finite stand-in max.
@@ -441,23 +479,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 
         // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile), row sums += 1^T P^T
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const bf16_t *vb = vs + v_off[db & 3] + ((db & ~3) << 4) + 32 * kc * D;
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
-            const v4i16 both[2] = {lo, hi};
-            const bf16x8_v a = __builtin_bit_cast(bf16x8_v, both);
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk)
-                o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qbk], o[qbk][db], 0, 0, 0);
-        }
+                o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[qbk], o[qbk][db], 0, 0, 0);
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk)
             lsum[qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qbk], lsum[qbk], 0, 0, 0);
     };
+    // Tile kt from stage (ks, vs), second half first; the first half's K operands are read here.
     auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
-        half(kt * kBN + 32, 1, ks, vs);
-        half(kt * kBN, 0, ks, vs);
+        load_k(ks, 1);
+        half(kt * kBN + 32, 1, ks, vs, 0);
+        half(kt * kBN, 0, ks, vs, -1);
     };
 
     // ---- pipeline.  Tiles are taken from the last (nearest the diagonal) to the first: with
