@@ -104,9 +104,10 @@ pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *val
                          int64_t num_tokens, const int64_t *slot_mapping, void *kv_cache, void *stream);
 
 /*
- * Bytes of device workspace pa_decode needs for this batch shape (0 when every sequence
- * fits one split-KV partition).  Depends only on the layer's head counts, num_seqs and
- * max_seq_len.  Returns 0 for invalid arguments.
+ * Bytes of device workspace pa_decode needs for this batch shape (> 0 whenever num_seqs > 0).
+ * Depends on the layer's head counts, head size, block size and dtype, on num_seqs and on the
+ * current device (its compute-unit count sizes the split); max_seq_len does not change it.
+ * Returns 0 for invalid arguments or num_seqs <= 0.
  */
 size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len);
 
@@ -123,12 +124,14 @@ size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t
  *   kv_cache         device cache as above, read only
  *   block_tables     device int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens         device int32 [num_seqs]; 0 marks a padded row, whose output is zeros
- *   max_seq_len      host upper bound of seq_lens (sizes the split-KV grid; a larger device
- *                    value is clamped to it and to max_blocks_per_seq * block_size)
- *   workspace        device scratch of pa_decode_workspace_size() bytes (may be NULL when
- *                    that is 0); 256-byte aligned; overwritten
- * Long sequences are cut into partitions processed in parallel; a second kernel merges the
- * partitions' (max, sum, weighted-V) triples with the log-sum-exp rule.
+ *   max_seq_len      host upper bound of seq_lens (a larger device value is clamped to it
+ *                    and to max_blocks_per_seq * block_size)
+ *   workspace        device scratch of pa_decode_workspace_size() bytes, 256-byte aligned,
+ *                    overwritten; calls that share one workspace must not overlap
+ * The key tiles of all (sequence, KV head) pairs are split evenly over as many wavefronts as
+ * the device holds at once (a small planning kernel computes the split on the device from
+ * seq_lens); a pair cut between wavefronts leaves (max, sum, weighted-V) partials that a third
+ * kernel merges with the log-sum-exp rule.
  */
 pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
                     const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,

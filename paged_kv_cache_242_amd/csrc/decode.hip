@@ -6,12 +6,14 @@
 // sequence (restricted to the last W with a sliding window), which are read through block-table
 // row i; scores scale * <q, k_j> (+ slope_h * (j - pos) with ALiBi); softmax; weighted sum of V.
 //
-// Work decomposition.  One workgroup of 4 wavefronts handles one (sequence, KV head, group of up
-// to 8 query heads, partition of part_size keys).  The query heads of a group share every K/V
-// byte, so each byte read from HBM feeds all of them.  Wavefronts take 32-key tiles of the
-// partition in turn and keep their own running (max, sum, weighted V); the four are merged in
-// LDS at the end.  With more than one partition per sequence the merged partial triple goes to
-// the workspace and decode_merge_kernel combines partitions with the log-sum-exp rule.
+// Work decomposition.  A work unit is one (sequence, KV head, group of up to 8 query heads); the
+// query heads of a group share every K/V byte, so each byte read from HBM feeds all of them.  The
+// key tiles of all units are laid end to end and split evenly over as many single-wavefront
+// workgroups as the device holds at once (decode_plan_kernel computes the per-sequence tile
+// prefix and each wavefront's first sequence on the device, from seq_lens), so every wavefront
+// streams the same number of bytes and no tail of long units is left at the end.  A wavefront
+// walks its tiles in order, keeping a running (max, sum, weighted V); a unit cut between
+// wavefronts leaves partials that decode_merge_kernel combines with the log-sum-exp rule.
 //
 // Lane layout.  A head row of K or V is D elements = D*elt bytes, read as 16-byte chunks by C
 // consecutive lanes; one load instruction covers R = 64 / C rows (4 rows of 256 B for bf16 at
@@ -38,10 +40,6 @@ namespace {
 
 constexpr int kTile = 32;          // keys per wavefront tile
 constexpr int kMaxGroup = 8;       // query heads per work unit
-#ifndef PA_DECODE_MIN_UNITS
-#define PA_DECODE_MIN_UNITS 8192
-#endif
-constexpr int64_t kMinUnits = PA_DECODE_MIN_UNITS;   // work units the partition size aims for
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -113,10 +111,13 @@ template <int C>
 __device__ __forceinline__ float max_row_groups(float x) { return xor_max_from<C>(x); }
 
 struct DecodeShape {
-    int part_size;
-    int num_parts;
-    int head_groups;
-    int heads_per_group;
+    int chunk;              // keys per block-id chunk (<= 128 blocks, multiple of the tile)
+    int head_groups;        // query heads of one KV head are processed in this many groups
+    int heads_per_group;    // real heads per group
+    int units_per_seq;      // num_kv_heads * head_groups
+    int num_waves;          // wavefronts of the split kernel
+    int tile;               // keys per tile of the split kernel instance
+    int max_len;            // bound on every sequence length
 };
 
 template <typename T>
@@ -144,17 +145,49 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
     }
 }
 
-// Load instructions per wavefront tile.  Two tiles of K and V (4 * NI * 4 registers) are live at
-// once, so wide head groups (more accumulators) and fp32 rows (more registers per key) use
-// narrower tiles.
-#ifndef PA_DECODE_NI_SMALL
-#define PA_DECODE_NI_SMALL 8
+// Tile shape per instance: NI load instructions per tile (R rows each), DEPTH register sets in
+// flight, OCC wavefronts per SIMD.  DEPTH sets of K and V take 2 * DEPTH * NI * 4 registers;
+// wide head groups (more accumulators) and fp32 rows (more registers per key) use fewer.
+// Bytes in flight per CU = waves per CU * (DEPTH - 1) * 2 * NI KB (for 16-byte lanes).
+#ifndef PA_DECODE_NI_S
+#define PA_DECODE_NI_S 8        // bf16, head groups of 1 or 2
 #endif
-#ifndef PA_DECODE_WAVES_SMALL
-#define PA_DECODE_WAVES_SMALL 2
+#ifndef PA_DECODE_DEPTH_S
+#define PA_DECODE_DEPTH_S 2
+#endif
+#ifndef PA_DECODE_OCC_S
+#define PA_DECODE_OCC_S 2
+#endif
+#ifndef PA_DECODE_NI_M
+#define PA_DECODE_NI_M 8        // bf16, head groups of 4
+#endif
+#ifndef PA_DECODE_DEPTH_M
+#define PA_DECODE_DEPTH_M 2
+#endif
+#ifndef PA_DECODE_OCC_M
+#define PA_DECODE_OCC_M 2
+#endif
+#ifndef PA_DECODE_NI_B
+#define PA_DECODE_NI_B 4        // bf16, head groups of 8
+#endif
+#ifndef PA_DECODE_DEPTH_B
+#define PA_DECODE_DEPTH_B 2
+#endif
+#ifndef PA_DECODE_OCC_B
+#define PA_DECODE_OCC_B 2
 #endif
 template <typename T, int GP>
-constexpr int tile_loads() { return (GP >= 8 || sizeof(T) == 4) ? 4 : (GP <= 2 ? PA_DECODE_NI_SMALL : 8); }
+constexpr int tile_loads() {
+    return sizeof(T) == 4 ? 4 : (GP <= 2 ? PA_DECODE_NI_S : (GP == 4 ? PA_DECODE_NI_M : PA_DECODE_NI_B));
+}
+template <typename T, int GP>
+constexpr int tile_depth() {
+    return sizeof(T) == 4 ? 2 : (GP <= 2 ? PA_DECODE_DEPTH_S : (GP == 4 ? PA_DECODE_DEPTH_M : PA_DECODE_DEPTH_B));
+}
+template <typename T, int GP>
+constexpr int tile_occ() {
+    return sizeof(T) == 4 ? 2 : (GP <= 2 ? PA_DECODE_OCC_S : (GP == 4 ? PA_DECODE_OCC_M : PA_DECODE_OCC_B));
+}
 
 // The running max is only raised when a tile's max exceeds it by more than this (base-2 units):
 // until then weights are exp2(s - m) <= 2^8, exact enough in fp32 sums and bf16 weights, and the
@@ -169,56 +202,102 @@ struct WaveAcc {
     float acc[GP][EPL];       // weighted V, this lane's elements, all heads, this row group
 };
 
-// Work unit u -> (sequence, KV head, head group, partition).  The partition index varies
-// slowest: workgroups are dispatched in index order, so full partitions start first and the
-// units past a sequence's end (which exit at once) come last.
-struct Unit {
-    int seq, g, hgrp, part;
-};
-__device__ __forceinline__ Unit unit_of(int u, const DecodeParams &p, const DecodeShape &s) {
-    Unit w;
-    const int per_part = p.num_seqs * p.num_kv_heads * s.head_groups;
-    w.part = u / per_part;
-    int rest = u - w.part * per_part;
-    w.hgrp = rest % s.head_groups;
-    rest /= s.head_groups;
-    w.g = rest % p.num_kv_heads;
-    w.seq = rest / p.num_kv_heads;
-    return w;
-}
-
 __device__ __forceinline__ int clamp_len(int L, const DecodeParams &p, const DecodeShape &s) {
-    return max(0, min(L, min(p.max_blocks << p.block_shift, s.num_parts * s.part_size)));
+    return max(0, min(L, min(p.max_blocks << p.block_shift, s.max_len)));
 }
 
-// Block ids of partition `part` of sequence `seq` (at most 128 blocks: lanes 0..63 and 64..127),
-// clamped into the pool.  Read without knowing the sequence length: entries past the
-// sequence's last block are read (within the table row) but never used.
-__device__ __forceinline__ void load_ids(const DecodeParams &p, const DecodeShape &s, int seq, int part, int lane,
+// Tiles (of s.tile keys, absolute alignment) that one work unit of sequence seq covers: keys
+// lo .. L - 1, lo = L - W with a sliding window.
+__device__ __forceinline__ int seq_tiles(const DecodeParams &p, const DecodeShape &s, int seq, int &L, int &lo) {
+    L = clamp_len(p.seq_lens[seq], p, s);
+    lo = p.window > 0 ? max(0, L - p.window) : 0;
+    return L > 0 ? (L + s.tile - 1) / s.tile - lo / s.tile : 0;
+}
+
+// Wavefront that owns tile t of the concatenated tile space (T tiles over N wavefronts,
+// wavefront i owning tiles floor(i T / N) .. floor((i + 1) T / N) - 1).
+__device__ __forceinline__ int wave_of_tile(int64_t t, int64_t T, int N) {
+    const int64_t i = ((t + 1) * N + T - 1) / T - 1;
+    return int(i < N - 1 ? i : N - 1);
+}
+
+// Plan of the even split (one workgroup of 1024 threads): prefix[q] = tiles of the work units of
+// sequences 0 .. q - 1 (prefix[num_seqs] = total T), and for every wavefront the sequence that
+// holds its first tile (-1: no tiles).
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeParams p, DecodeShape s) {
+    __shared__ int64_t part[1024];
+    const int tid = threadIdx.x;
+    const int per = (p.num_seqs + 1023) / 1024;
+    const int a = min(tid * per, p.num_seqs), b = min(a + per, p.num_seqs);
+    const int64_t ups = s.units_per_seq;
+    int L, lo;
+    int64_t sum = 0;
+    for (int q = a; q < b; ++q) sum += seq_tiles(p, s, q, L, lo);
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {           // inclusive scan of the chunk sums
+        const int64_t v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int64_t run = tid > 0 ? part[tid - 1] : 0;
+    for (int q = a; q < b; ++q) {
+        p.ws_prefix[q] = run * ups;
+        run += seq_tiles(p, s, q, L, lo);
+    }
+    const int64_t T = part[1023] * ups;
+    if (tid == 0) p.ws_prefix[p.num_seqs] = T;
+    for (int i = tid; i < s.num_waves; i += 1024) {
+        const int64_t t = int64_t(i) * T / s.num_waves;
+        int seq = -1;
+        if (t < T) {
+            int c0 = 0, c1 = 1023;                       // first chunk whose inclusive sum exceeds t
+            while (c0 < c1) {
+                const int mid = (c0 + c1) / 2;
+                if (part[mid] * ups > t) c1 = mid; else c0 = mid + 1;
+            }
+            int64_t r = c0 > 0 ? part[c0 - 1] * ups : 0;
+            int q = min(c0 * per, p.num_seqs - 1);
+            for (; q < p.num_seqs - 1; ++q) {
+                const int64_t ts = int64_t(seq_tiles(p, s, q, L, lo)) * ups;
+                if (r + ts > t) break;
+                r += ts;
+            }
+            seq = q;
+        }
+        p.ws_wseq[i] = seq;
+    }
+}
+
+// Block ids of key chunk ch of sequence seq (at most 128 blocks: lanes 0..63 and 64..127),
+// clamped into the pool.  Entries past the sequence's last block are read (within the table row)
+// but never used.
+__device__ __forceinline__ void load_ids(const DecodeParams &p, const DecodeShape &s, int seq, int ch, int lane,
                                          int &ids0, int &ids1) {
     const int32_t *table = p.block_tables + int64_t(seq) * p.max_blocks;
-    const int first = (part * s.part_size) >> p.block_shift;
+    const int first = (ch * s.chunk) >> p.block_shift;
     const int last = p.max_blocks - 1;
     const int64_t nbm1 = p.num_blocks - 1;
     int64_t b0 = table[min(first + lane, last)];
     ids0 = int(b0 < 0 ? 0 : (b0 > nbm1 ? nbm1 : b0));
     ids1 = ids0;
-    if ((s.part_size >> p.block_shift) > 64) {
+    if ((s.chunk >> p.block_shift) > 64) {
         int64_t b1 = table[min(first + 64 + lane, last)];
         ids1 = int(b1 < 0 ? 0 : (b1 > nbm1 ? nbm1 : b1));
     }
 }
 
-// Occupancy hint: the accumulators of a head group grow with its size.
-template <int GP>
-constexpr int waves_per_simd() { return GP <= 2 ? PA_DECODE_WAVES_SMALL : 2; }
-
-// One work unit = one wavefront: partition `part` of (sequence, KV head, head group).
+// Even split: wavefront i takes tiles floor(i T / N) .. floor((i + 1) T / N) - 1 of the
+// concatenated tiles of all work units (sequence-major, then KV head, then head group), i.e. a
+// run of segments each inside one work unit.  A segment that is a whole unit writes the output;
+// any other writes a partial (max, sum, weighted V) to slot i + u (unique: along a unit the
+// wavefronts are consecutive and along a wavefront the units are), merged afterwards.
 //   ONE_BLOCK: every tile lies inside one cache block (tile keys <= block size), so a tile needs
 //              one block id; otherwise each load instruction looks up its own block.
-template <typename T, int D, int GP, int NI, bool ONE_BLOCK>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<GP>(), 8)))
-void decode_partition_kernel(DecodeParams p, DecodeShape shape) {
+template <typename T, int D, int GP, int NI, bool ONE_BLOCK, int DEPTH, int OCC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     constexpr int C = Geo<T, D>::kC, R = Geo<T, D>::kR, EPL = Geo<T, D>::kEpl;
     constexpr int TILE = NI * R;                       // keys per tile
     constexpr int WMASK = writer_mask<C, GP>();
@@ -227,325 +306,421 @@ void decode_partition_kernel(DecodeParams p, DecodeShape shape) {
     // Softmax weights of the current tile, [head][row group][instruction].
     __shared__ __align__(16) T p_lds[GP][R][NI];
 
+    const int wave = blockIdx.x;
     const int lane = threadIdx.x;
     const int c = lane % C;
     const int r = lane / C;
     const int my_head = head_of_lane<C, GP>(c);
     const int group = p.num_heads / p.num_kv_heads;
     const int nh = shape.heads_per_group;
+    const int ups = shape.units_per_seq;
     const int bmask = (1 << p.block_shift) - 1;
     const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * sizeof(T);           // one token, all heads
     const int64_t block_bytes = int64_t(row_bytes) << p.block_shift;
     const char *kcache = reinterpret_cast<const char *>(p.k_cache);
     const char *vcache = reinterpret_cast<const char *>(p.v_cache);
     const float qk_scale = p.scale * kLog2e;
-
-    // Length, block ids and query are requested together; none waits for another.
-    const Unit w = unit_of(blockIdx.x, p, shape);
-    int ids0, ids1;
-    load_ids(p, shape, w.seq, w.part, lane, ids0, ids1);
-    const int L = clamp_len(p.seq_lens[w.seq], p, shape);
-    const int head0 = w.g * group + w.hgrp * nh;
-    // Query chunks, head-permuted: slot s holds head s ^ my_head.
-    uint32_t q[GP][4];
-    {
-        const T *qrow =
-            reinterpret_cast<const T *>(p.query) + int64_t(w.seq) * p.q_stride + int64_t(head0) * D + c * EPL;
-#pragma unroll
-        for (int s = 0; s < GP; ++s) {
-            const int hs = s ^ my_head;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (hs < nh) v = *reinterpret_cast<const uint4 *>(qrow + int64_t(hs) * D);
-            q[s][0] = v.x; q[s][1] = v.y; q[s][2] = v.z; q[s][3] = v.w;
-        }
-    }
-    const int lo = p.window > 0 ? max(0, L - p.window) : 0;
-    const int pstart = w.part * shape.part_size;
-    const int pend = min(pstart + shape.part_size, L);
-    const int kb = max(pstart, lo);
-    const int p_first = lo / shape.part_size;
-    const int p_count = L > 0 ? (L + shape.part_size - 1) / shape.part_size - p_first : 0;
-    T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(w.seq) * p.num_heads + head0) * D;
-    if (kb >= pend) {
-        if (L == 0 && w.part == 0)
-            for (int idx = lane; idx < nh * D; idx += 64) store_out<T>(out_row + idx, 0.f);
-        return;
-    }
-
     const bool has_alibi = p.alibi_slopes != nullptr;
-    const float slope2 = (has_alibi && my_head < nh) ? p.alibi_slopes[head0 + my_head] * kLog2e : 0.f;
-    const int pos = L - 1;
-    const int pblock0 = pstart >> p.block_shift;
-    // Lane part of every K/V address: row group r's token inside the instruction, KV head g, chunk c.
-    const uint32_t lane_off = uint32_t(r) * row_bytes + (uint32_t(w.g) * D + c * EPL) * sizeof(T);
 
-    // Scalar (uniform) part of the address of instruction i of the tile starting at tb: block base
-    // plus the instruction's first token inside the block.  Tokens past the sequence's end read
-    // unwritten slots of in-pool blocks; their scores are masked and their V rows zeroed.
-    auto inst_base = [&](int tb, int i, int blk_tile) -> int64_t {
-        const int row0 = tb + i * R;
-        int blk = blk_tile;
-        if constexpr (!ONE_BLOCK) {
-            const int bidx = (row0 >> p.block_shift) - pblock0;
-            blk = __builtin_amdgcn_readlane(bidx < 64 ? ids0 : ids1, bidx & 63);
-        }
-        return int64_t(blk) * block_bytes + int64_t(row0 & bmask) * row_bytes;
-    };
-    auto tile_block = [&](int tb) -> int {
-        if constexpr (ONE_BLOCK) {
-            const int bidx = (tb >> p.block_shift) - pblock0;
-            return __builtin_amdgcn_readlane(bidx < 64 ? ids0 : ids1, bidx & 63);
-        } else {
-            return 0;
-        }
-    };
-    auto load_rows = [&](const char *cache, int tb, uint4 (&x)[NI]) {
-        const int blk = tile_block(tb);
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            x[i] = *reinterpret_cast<const uint4 *>(cache + inst_base(tb, i, blk) + lane_off);
-    };
+    const int64_t Ttot = p.ws_prefix[p.num_seqs];
+    const int64_t t_begin = int64_t(wave) * Ttot / shape.num_waves;
+    const int64_t t_end = int64_t(wave + 1) * Ttot / shape.num_waves;
+    if (t_begin >= t_end) return;
+    int seq = p.ws_wseq[wave];
+    int64_t pre = p.ws_prefix[seq];
 
-    // Online softmax state.  Each row group keeps its own running max (base 2) per head, so no
-    // tile needs a cross-row-group reduction; the groups are brought to a common max at the end.
-    float m_run = -INFINITY;      // head my_head, this row group
-    float l_run = 0.f;            // sum of rounded weights, head my_head, this row group
-    float acc[GP][EPL];           // weighted V, all heads, this lane's elements, this row group
-#pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    int64_t t = t_begin;
+    while (t < t_end) {
+        int L, lo;
+        const int ts = seq_tiles(p, shape, seq, L, lo);
+        if (t >= pre + int64_t(ts) * ups) {               // (sequence without tiles, or exhausted)
+            pre += int64_t(ts) * ups;
+            ++seq;
+            continue;
+        }
+        const int64_t local = t - pre;
+        const int u_in = int(local / ts);
+        const int tile0 = int(local - int64_t(u_in) * ts);
+        const int tile1 = int(min(int64_t(ts), int64_t(tile0) + (t_end - t)));
+        const int g = u_in / shape.head_groups;
+        const int hgrp = u_in - g * shape.head_groups;
+        const int head0 = g * group + hgrp * nh;
 
-    auto scores = [&](int tb, const uint4 (&kr)[NI], float (&sc)[NI]) {
-        const bool edge = tb < lo || tb + TILE - 1 > pos;           // uniform
+        // ---- one segment: tiles tile0 .. tile1 - 1 of unit (seq, g, hgrp)
+        uint32_t q[GP][4];      // query chunks, head-permuted: slot s holds head s ^ my_head
+        {
+            const T *qrow =
+                reinterpret_cast<const T *>(p.query) + int64_t(seq) * p.q_stride + int64_t(head0) * D + c * EPL;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            float part_dot[GP];
-            chunk_dots<T, GP>(kr[i], q, part_dot);
-            butterfly<C, GP, 0>(part_dot);
-            sc[i] = part_dot[0] * qk_scale;
+            for (int s = 0; s < GP; ++s) {
+                const int hs = s ^ my_head;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (hs < nh) v = *reinterpret_cast<const uint4 *>(qrow + int64_t(hs) * D);
+                q[s][0] = v.x; q[s][1] = v.y; q[s][2] = v.z; q[s][3] = v.w;
+            }
         }
-        if (has_alibi) {
+        const float slope2 = (has_alibi && my_head < nh) ? p.alibi_slopes[head0 + my_head] * kLog2e : 0.f;
+        const int pos = L - 1;
+        const int kfirst = (lo / TILE + tile0) * TILE;
+        const int kend = min(L, (lo / TILE + tile1) * TILE);
+        // Lane part of every K/V address: row group r's token inside the instruction, KV head g, chunk c.
+        const uint32_t lane_off = uint32_t(r) * row_bytes + (uint32_t(g) * D + c * EPL) * sizeof(T);
+
+        float m_run = -INFINITY;      // head my_head, this row group
+        float l_run = 0.f;            // sum of rounded weights, head my_head, this row group
+        float acc[GP][EPL];           // weighted V, all heads, this lane's elements, this row group
 #pragma unroll
-            for (int i = 0; i < NI; ++i) sc[i] += slope2 * float(tb + i * R + r - pos);
-        }
-        if (edge) {
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+
+        auto scores = [&](int tb, const uint4 (&kr)[NI], float (&sc)[NI]) {
+            const bool edge = tb < lo || tb + TILE - 1 > pos;           // uniform
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                const int j = tb + i * R + r;
-                sc[i] = (j >= lo && j <= pos) ? sc[i] : -INFINITY;
+                float part_dot[GP];
+                chunk_dots<T, GP>(kr[i], q, part_dot);
+                butterfly<C, GP, 0>(part_dot);
+                sc[i] = part_dot[0] * qk_scale;
             }
-        }
-    };
-    auto softmax_pv = [&](int tb, const float (&sc)[NI], uint4 (&vr)[NI]) {
-        // Lazily raised max: rescale only when some tile max exceeds the running max by more than
-        // kRescaleSlack (always on the first tile, rarely afterwards); uniform over the wavefront.
-        float tmax = sc[0];
+            if (has_alibi) {
 #pragma unroll
-        for (int i = 1; i < NI; ++i) tmax = fmaxf(tmax, sc[i]);
-        const bool raise = tmax > m_run + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-            l_run *= alpha;
-            m_run = m_new;
-#pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                const float a = __shfl(alpha, r * C + lane_of_head<C, GP>(h), 64);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+                for (int i = 0; i < NI; ++i) sc[i] += slope2 * float(tb + i * R + r - pos);
             }
-        }
-        float psum = 0.f;
-        T pv[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const float pf = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
-            if constexpr (sizeof(T) == 2) {
-                pv[i] = f32_to_bf16(pf);
-                psum += bf16_to_f32(pv[i]);
-            } else {
-                pv[i] = pf;
-                psum += pf;
-            }
-        }
-        l_run += psum;
-        if ((c & WMASK) == 0) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) p_lds[my_head][r][i] = pv[i];
-        }
-        // Rows past the sequence's end hold unwritten cache bytes: zero them so that their zero
-        // weights cannot meet a NaN.
-        if (tb + TILE - 1 > pos) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const bool past = tb + i * R + r > pos;
-                vr[i].x = past ? 0u : vr[i].x;
-                vr[i].y = past ? 0u : vr[i].y;
-                vr[i].z = past ? 0u : vr[i].z;
-                vr[i].w = past ? 0u : vr[i].w;
-            }
-        }
-        wave_lds_sync();
-
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int ip = 0; ip < NI / 2; ++ip) {
-                // row pair (2ip, 2ip+1) -> per element e the bf16 pair (v_2ip[e], v_2ip+1[e])
-                const uint4 a = vr[2 * ip], b = vr[2 * ip + 1];
-                const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-                const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-                uint32_t vp[EPL];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    vp[2 * k] = interleave_lo(aw[k], bw[k]);
-                    vp[2 * k + 1] = interleave_hi(aw[k], bw[k]);
-                }
-#pragma unroll
-                for (int h = 0; h < GP; ++h) {
-                    const uint32_t pp = reinterpret_cast<const uint32_t *>(&p_lds[h][r][0])[ip];
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] = dot2_bf16(pp, vp[e], acc[h][e]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < GP; ++h) {
+            if (edge) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    const float pw = p_lds[h][r][i];
-                    const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+                    const int j = tb + i * R + r;
+                    sc[i] = (j >= lo && j <= pos) ? sc[i] : -INFINITY;
+                }
+            }
+        };
+        auto softmax_pv = [&](int tb, const float (&sc)[NI], uint4 (&vr)[NI]) {
+            // Lazily raised max: rescale only when some tile max exceeds the running max by more
+            // than kRescaleSlack (always on the first tile, rarely afterwards); uniform over the wave.
+            float tmax = sc[0];
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw, __uint_as_float(vw[e]), acc[h][e]);
+            for (int i = 1; i < NI; ++i) tmax = fmaxf(tmax, sc[i]);
+            const bool raise = tmax > m_run + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+                const float m_new = fmaxf(m_run, tmax);
+                const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+                l_run *= alpha;
+                m_run = m_new;
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    const float a = __shfl(alpha, r * C + lane_of_head<C, GP>(h), 64);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+                }
+            }
+            float psum = 0.f;
+            T pv[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const float pf = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
+                if constexpr (sizeof(T) == 2) {
+                    pv[i] = f32_to_bf16(pf);
+                    psum += bf16_to_f32(pv[i]);
+                } else {
+                    pv[i] = pf;
+                    psum += pf;
+                }
+            }
+            l_run += psum;
+            if ((c & WMASK) == 0) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) p_lds[my_head][r][i] = pv[i];
+            }
+            // Rows past the sequence's end hold unwritten cache bytes: zero them so that their
+            // zero weights cannot meet a NaN.
+            if (tb + TILE - 1 > pos) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const bool past = tb + i * R + r > pos;
+                    vr[i].x = past ? 0u : vr[i].x;
+                    vr[i].y = past ? 0u : vr[i].y;
+                    vr[i].z = past ? 0u : vr[i].z;
+                    vr[i].w = past ? 0u : vr[i].w;
+                }
+            }
+            wave_lds_sync();
+
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int ip = 0; ip < NI / 2; ++ip) {
+                    // row pair (2ip, 2ip+1) -> per element e the bf16 pair (v_2ip[e], v_2ip+1[e])
+                    const uint4 a = vr[2 * ip], b = vr[2 * ip + 1];
+                    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+                    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+                    uint32_t vp[EPL];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        vp[2 * k] = interleave_lo(aw[k], bw[k]);
+                        vp[2 * k + 1] = interleave_hi(aw[k], bw[k]);
+                    }
+#pragma unroll
+                    for (int h = 0; h < GP; ++h) {
+                        const uint32_t pp = reinterpret_cast<const uint32_t *>(&p_lds[h][r][0])[ip];
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[h][e] = dot2_bf16(pp, vp[e], acc[h][e]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        const float pw = p_lds[h][r][i];
+                        const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw, __uint_as_float(vw[e]), acc[h][e]);
+                    }
+                }
+            }
+            wave_lds_sync();
+        };
+
+        // Key chunks of the segment (chunk boundaries are absolute multiples of shape.chunk, so a
+        // chunk's block ids are one row of the table): ids per chunk, then its tiles in order with
+        // two register sets in turn -- the next tile's K rows are requested once this tile's
+        // scores have consumed K, its V rows once P.V has consumed V.  At a chunk's last tile the
+        // loads re-read it (cache hits), keeping them unconditional.
+        for (int ch = kfirst / shape.chunk; ch * shape.chunk < kend; ++ch) {
+            int ids0, ids1;
+            load_ids(p, shape, seq, ch, lane, ids0, ids1);
+            const int cend = min(kend, (ch + 1) * shape.chunk);
+            const int pblock0 = (ch * shape.chunk) >> p.block_shift;
+            // Scalar part of the address of instruction i of the tile starting at tb: block base
+            // plus the instruction's first token inside the block.  Tokens past the sequence's end
+            // read unwritten slots of in-pool blocks; their scores are masked, their V rows zeroed.
+            auto inst_base = [&](int tb, int i, int blk_tile) -> int64_t {
+                const int row0 = tb + i * R;
+                int blk = blk_tile;
+                if constexpr (!ONE_BLOCK) {
+                    const int bidx = (row0 >> p.block_shift) - pblock0;
+                    blk = __builtin_amdgcn_readlane(bidx < 64 ? ids0 : ids1, bidx & 63);
+                }
+                return int64_t(blk) * block_bytes + int64_t(row0 & bmask) * row_bytes;
+            };
+            auto tile_block = [&](int tb) -> int {
+                if constexpr (ONE_BLOCK) {
+                    const int bidx = (tb >> p.block_shift) - pblock0;
+                    return __builtin_amdgcn_readlane(bidx < 64 ? ids0 : ids1, bidx & 63);
+                } else {
+                    return 0;
+                }
+            };
+            auto load_rows = [&](const char *cache, int tb, uint4 (&x)[NI]) {
+                const int blk = tile_block(tb);
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    x[i] = *reinterpret_cast<const uint4 *>(cache + inst_base(tb, i, blk) + lane_off);
+            };
+            // DEPTH register sets in a ring: while tile t is scored and summed from set t % DEPTH,
+            // tiles t + 1 .. t + DEPTH - 1 are in flight.  Loads past the chunk's last tile
+            // re-read it (cache hits), keeping every load unconditional.
+            const int tfirst = max(kfirst, ch * shape.chunk);
+            const int tlast = ((cend - 1) / TILE) * TILE;
+            uint4 kr[DEPTH][NI], vr[DEPTH][NI];
+#pragma unroll
+            for (int d = 0; d < DEPTH - 1; ++d) {
+                const int tt = min(tfirst + d * TILE, tlast);
+                load_rows(kcache, tt, kr[d]);
+                load_rows(vcache, tt, vr[d]);
+            }
+            int tb = tfirst;
+            bool done = false;
+            while (!done) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    if (!done) {
+                        const int nd = (d + DEPTH - 1) % DEPTH;          // set of the previous tile: free
+                        const int ahead = min(tb + (DEPTH - 1) * TILE, tlast);
+                        load_rows(kcache, ahead, kr[nd]);
+                        float sc[NI];
+                        scores(tb, kr[d], sc);
+                        load_rows(vcache, ahead, vr[nd]);
+                        softmax_pv(tb, sc, vr[d]);
+                        done = tb >= tlast;
+                        tb += TILE;
+                    }
                 }
             }
         }
-        wave_lds_sync();
-    };
 
-    // Tiles of the partition in order, two register sets in turn: the next tile's K rows are
-    // requested once this tile's scores have consumed K, its V rows once P.V has consumed V.  At
-    // the last tile the loads re-read it (cache hits), keeping them unconditional.
-    {
-        int tb = (kb / TILE) * TILE;
-        uint4 ka[NI], va[NI], kb2[NI], vb2[NI];
-        load_rows(kcache, tb, ka);
-        load_rows(vcache, tb, va);
-        while (true) {
-            int tn = tb + TILE;
-            bool more = tn < pend;
-            float sc[NI];
-            scores(tb, ka, sc);
-            load_rows(kcache, more ? tn : tb, kb2);
-            softmax_pv(tb, sc, va);
-            load_rows(vcache, more ? tn : tb, vb2);
-            if (!more) break;
-            tb = tn;
-            tn = tb + TILE;
-            more = tn < pend;
-            scores(tb, kb2, sc);
-            load_rows(kcache, more ? tn : tb, ka);
-            softmax_pv(tb, sc, vb2);
-            load_rows(vcache, more ? tn : tb, va);
-            if (!more) break;
-            tb = tn;
-        }
-    }
-
-    // Bring the row groups to a common max per head, then sum them; lanes of row group 0 end
-    // with the unit's weighted V for all heads.
-    const float m_all = max_row_groups<C>(m_run);
-    const float f_own = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_all);
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        const float f = __shfl(f_own, r * C + lane_of_head<C, GP>(h), 64);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = sum_row_groups<C>(acc[h][e] * f);
-    }
-    const float l_sum = sum_row_groups<C>(l_run * f_own);
-    if (p_count == 1) {
-        // The whole (windowed) sequence is this partition: write the normalized output.
+        // Bring the row groups to a common max per head, then sum them; lanes of row group 0
+        // end with the segment's weighted V for all heads.
+        const float m_all = max_row_groups<C>(m_run);
+        const float f_own = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_all);
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
-            const float lh = __shfl(l_sum, lane_of_head<C, GP>(h), 64);
-            if (r == 0 && h < nh) {
-                const float inv = 1.f / lh;
+            const float f = __shfl(f_own, r * C + lane_of_head<C, GP>(h), 64);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) store_out<T>(out_row + h * D + c * EPL + e, acc[h][e] * inv);
-            }
+            for (int e = 0; e < EPL; ++e) acc[h][e] = sum_row_groups<C>(acc[h][e] * f);
         }
-    } else {
-        const int64_t slot0 = (int64_t(w.seq) * p.num_heads + head0) * shape.num_parts + w.part;
+        const float l_sum = sum_row_groups<C>(l_run * f_own);
+        if (tile0 == 0 && tile1 == ts) {
+            // The whole (windowed) unit is this segment: write the normalized output.
+            T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head0) * D;
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            const float lh = __shfl(l_sum, lane_of_head<C, GP>(h), 64);
-            const float mh = __shfl(m_all, lane_of_head<C, GP>(h), 64);
-            if (r == 0 && h < nh) {
-                const int64_t slot = slot0 + int64_t(h) * shape.num_parts;
-                float4 *dst = reinterpret_cast<float4 *>(p.ws_acc + slot * D + c * EPL);
+            for (int h = 0; h < GP; ++h) {
+                const float lh = __shfl(l_sum, lane_of_head<C, GP>(h), 64);
+                if (r == 0 && h < nh) {
+                    const float inv = 1.f / lh;
 #pragma unroll
-                for (int e = 0; e < EPL; e += 4)
-                    dst[e / 4] = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
-                if (c == 0) {
-                    p.ws_ml[slot * 2] = mh;
-                    p.ws_ml[slot * 2 + 1] = lh;
+                    for (int e = 0; e < EPL; ++e) store_out<T>(out_row + h * D + c * EPL + e, acc[h][e] * inv);
                 }
             }
+        } else {
+            const int64_t slot0 = (int64_t(wave) + int64_t(seq) * ups + u_in) * nh;
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                const float lh = __shfl(l_sum, lane_of_head<C, GP>(h), 64);
+                const float mh = __shfl(m_all, lane_of_head<C, GP>(h), 64);
+                if (r == 0 && h < nh) {
+                    const int64_t slot = slot0 + h;
+                    float4 *dst = reinterpret_cast<float4 *>(p.ws_acc + slot * D + c * EPL);
+#pragma unroll
+                    for (int e = 0; e < EPL; e += 4)
+                        dst[e / 4] = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+                    if (c == 0) {
+                        p.ws_ml[slot * 2] = mh;
+                        p.ws_ml[slot * 2 + 1] = lh;
+                    }
+                }
+            }
+        }
+
+        t += tile1 - tile0;
+        if (tile1 == ts && u_in == ups - 1) {
+            pre += int64_t(ts) * ups;
+            ++seq;
         }
     }
 }
 
-// Merge of split-KV partials: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// Merge, one wavefront per (work unit, head of its group): zero rows of empty sequences, and for
+// units split over several wavefronts out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i over
+// their partials.  Lane j takes partial i0 + j (+ 64 k) for the (max, sum) step, so the step
+// costs a few dependent loads however many partials there are.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, DecodeShape shape) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
-    const int h = blockIdx.x % p.num_heads;
-    const int seq = blockIdx.x / p.num_heads;
-    T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + h) * D;
-    int L = p.seq_lens[seq];
-    L = max(0, min(L, min(p.max_blocks << p.block_shift, shape.num_parts * shape.part_size)));
-    if (L == 0) return;                       // padded row: written by its first unit
-    const int lo = p.window > 0 ? max(0, L - p.window) : 0;
-    const int p0 = lo / shape.part_size;
-    const int p1 = (L + shape.part_size - 1) / shape.part_size;
-    if (p1 - p0 <= 1) return;                 // one partition: its unit wrote the output
-    const int64_t base = (int64_t(seq) * p.num_heads + h) * shape.num_parts;
+    const int nh = shape.heads_per_group;
+    const int u = blockIdx.x / nh;
+    const int h = blockIdx.x - u * nh;
+    const int ups = shape.units_per_seq;
+    const int seq = u / ups;
+    const int u_in = u - seq * ups;
+    const int g = u_in / shape.head_groups;
+    const int hgrp = u_in - g * shape.head_groups;
+    const int head0 = g * (p.num_heads / p.num_kv_heads) + hgrp * nh;
+    T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head0 + h) * D;
+    int L, lo;
+    const int ts = seq_tiles(p, shape, seq, L, lo);
+    if (ts == 0) {                          // empty sequence: zero output
+#pragma unroll
+        for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, 0.f);
+        return;
+    }
+    const int64_t Ttot = p.ws_prefix[p.num_seqs];
+    const int64_t U = p.ws_prefix[seq] + int64_t(u_in) * ts;
+    const int i0 = wave_of_tile(U, Ttot, shape.num_waves);
+    const int i1 = wave_of_tile(U + ts - 1, Ttot, shape.num_waves);
+    if (i0 == i1) return;                   // one segment: its wavefront wrote the output
+    const int n = i1 - i0 + 1;
+    // Wavefronts between i0 and i1 with no tiles at all (only when there are fewer tiles than
+    // wavefronts) wrote nothing and are skipped.
+    auto has_tiles = [&](int i) {
+        return int64_t(i) * Ttot / shape.num_waves < int64_t(i + 1) * Ttot / shape.num_waves;
+    };
+    auto slot_of = [&](int j) { return (int64_t(i0 + j) + u) * nh + h; };
     float M = -INFINITY;
-    for (int pp = p0; pp < p1; ++pp) M = fmaxf(M, p.ws_ml[(base + pp) * 2]);
+    for (int j = lane; j < n; j += 64)
+        if (has_tiles(i0 + j)) M = fmaxf(M, p.ws_ml[slot_of(j) * 2]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float den = 0.f;
     float num[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) num[k] = 0.f;
-    float den = 0.f;
-    for (int pp = p0; pp < p1; ++pp) {
-        const float f = fast_exp2(p.ws_ml[(base + pp) * 2] - M);
-        den += f * p.ws_ml[(base + pp) * 2 + 1];
-        const float *a = p.ws_acc + (base + pp) * D;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        float f = 0.f;
+        if (j < n && has_tiles(i0 + j)) {
+            f = fast_exp2(p.ws_ml[slot_of(j) * 2] - M);
+            den += f * p.ws_ml[slot_of(j) * 2 + 1];
+        }
+        const int cnt = min(64, n - j0);
+        for (int jj = 0; jj < cnt; ++jj) {
+            const float fj = __shfl(f, jj, 64);
+            if (fj != 0.f) {
+                const float *a = p.ws_acc + slot_of(j0 + jj) * D;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) num[k] += f * a[lane + 64 * k];
+                for (int k = 0; k < PER; ++k) num[k] += fj * a[lane + 64 * k];
+            }
+        }
     }
 #pragma unroll
-    for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] / den);
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] * inv);
 }
 
-template <typename T, int D, int GP, int NI, bool ONE>
-hipError_t launch_units(const DecodeParams &p, const DecodeShape &s, int64_t units, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, GP, NI, ONE>), dim3(unsigned(units)), dim3(64), 0, stream, p, s);
+template <typename T, int D, int GP>
+constexpr int tile_keys() { return tile_loads<T, GP>() * Geo<T, D>::kR; }
+
+template <typename T, int D, int GP, bool ONE>
+const void *split_kernel_fn() {
+    return reinterpret_cast<const void *>(
+        &decode_split_kernel<T, D, GP, tile_loads<T, GP>(), ONE, tile_depth<T, GP>(), tile_occ<T, GP>()>);
+}
+
+// Resident wavefronts of the split kernel instance on the current device (occupancy x CUs),
+// cached per device and instance.
+template <typename T, int D, int GP>
+int split_waves(int block_shift) {
+    constexpr int NI = tile_loads<T, GP>();
+    constexpr int TILE = NI * Geo<T, D>::kR;
+    const bool one = (1 << block_shift) >= TILE;
+    static int cache[64][2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int &slot = cache[dev][one ? 1 : 0];
+    if (slot > 0) return slot;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const void *fn = one ? split_kernel_fn<T, D, GP, true>() : split_kernel_fn<T, D, GP, false>();
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 8;
+    slot = cus * per_cu;
+    return slot;
+}
+
+template <typename T, int D, int GP, bool ONE>
+hipError_t launch_split(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, GP, tile_loads<T, GP>(), ONE, tile_depth<T, GP>(), tile_occ<T, GP>()>),
+                       dim3(unsigned(s.num_waves)), dim3(64), 0, stream, p, s);
     return hipGetLastError();
 }
 
 template <typename T, int D, int GP>
 hipError_t launch_typed(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
-    const int64_t units = int64_t(p.num_seqs) * p.num_kv_heads * s.head_groups * s.num_parts;
-    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int NI = tile_loads<T, GP>();
     constexpr int TILE = NI * Geo<T, D>::kR;
+    const int64_t units = int64_t(p.num_seqs) * s.units_per_seq;
+    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const bool one_block = (1 << p.block_shift) >= TILE;
-    hipError_t e = one_block ? launch_units<T, D, GP, NI, true>(p, s, units, stream)
-                             : launch_units<T, D, GP, NI, false>(p, s, units, stream);
-    if (e != hipSuccess || s.num_parts == 1) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(unsigned(p.num_seqs * p.num_heads)), dim3(64), 0, stream, p,
-                       s);
+    e = one_block ? launch_split<T, D, GP, true>(p, s, stream) : launch_split<T, D, GP, false>(p, s, stream);
+    if (e != hipSuccess) return e;
+    const int64_t merges = units * s.heads_per_group;
+    if (merges > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(unsigned(merges)), dim3(64), 0, stream, p, s);
     return hipGetLastError();
 }
 
@@ -560,10 +735,20 @@ hipError_t launch_group(const DecodeParams &p, const DecodeShape &s, int padded_
     }
 }
 
+template <typename T, int D>
+void instance_info(int padded_group, int block_shift, int &tile, int &waves) {
+    switch (padded_group) {
+        case 1: tile = tile_keys<T, D, 1>(); waves = split_waves<T, D, 1>(block_shift); break;
+        case 2: tile = tile_keys<T, D, 2>(); waves = split_waves<T, D, 2>(block_shift); break;
+        case 4: tile = tile_keys<T, D, 4>(); waves = split_waves<T, D, 4>(block_shift); break;
+        default: tile = tile_keys<T, D, 8>(); waves = split_waves<T, D, 8>(block_shift); break;
+    }
+}
+
 }  // namespace
 
 DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                       int32_t num_seqs, int32_t max_seq_len) {
+                       int32_t dtype, int32_t num_seqs, int32_t max_seq_len) {
     int block_shift = 0;
     while ((1 << block_shift) < block_size) ++block_shift;
     DecodePlan plan{};
@@ -572,35 +757,43 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     plan.heads_per_group = (group + plan.head_groups - 1) / plan.head_groups;
     plan.padded_group = 1;
     while (plan.padded_group < plan.heads_per_group) plan.padded_group <<= 1;
-    const int64_t units = int64_t(num_seqs) * num_kv_heads * plan.head_groups;
-    const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
-    // Partition size: the largest of 4096 / 2048 / 1024 / 512 / 256 keys that still gives >= 8192
-    // work units (one single-wavefront workgroup each; 256 CUs hold ~2048-4096 at once) for the
-    // longest sequence: long partitions amortize the per-unit start and the partial-result
-    // traffic, enough units keep every CU fed to the end.  At most 128 blocks per partition
-    // (two id registers per lane).
-    int part = 256;
-    for (int cand : {4096, 2048, 1024, 512}) {
-        if ((cand >> block_shift) <= 128 && units * ((len + cand - 1) / cand) >= kMinUnits) {
-            part = cand;
-            break;
-        }
+    plan.units_per_seq = num_kv_heads * plan.head_groups;
+    // Block-id chunk: 128 blocks (two id registers per lane), at most 4096 keys.
+    plan.chunk = (128 << block_shift) < 4096 ? (128 << block_shift) : 4096;
+    int tile = 32, waves = 2048;
+    if (dtype == 1) {
+        if (head_size == 128) instance_info<bf16_t, 128>(plan.padded_group, block_shift, tile, waves);
+        else instance_info<bf16_t, 64>(plan.padded_group, block_shift, tile, waves);
+    } else {
+        if (head_size == 128) instance_info<float, 128>(plan.padded_group, block_shift, tile, waves);
+        else instance_info<float, 64>(plan.padded_group, block_shift, tile, waves);
     }
-    plan.part_size = part;
-    plan.num_parts = int((len + part - 1) / part);
-    plan.workspace_bytes = 0;
-    if (plan.num_parts > 1) {
-        const size_t slots = size_t(num_seqs) * num_heads * plan.num_parts;
-        const size_t acc = slots * head_size * sizeof(float);
-        const size_t acc_aligned = (acc + 255) / 256 * 256;
-        plan.workspace_bytes = acc_aligned + slots * 2 * sizeof(float);
-    }
+    plan.tile = tile;
+    plan.num_waves = waves;
+    // Workspace: tile prefix per sequence, first sequence per wavefront, then the partial slots
+    // (one per (wavefront, unit) pair that can meet: at most num_waves + units) of nh heads.
+    const size_t units = size_t(num_seqs) * plan.units_per_seq;
+    const size_t slots = (size_t(waves) + units) * plan.heads_per_group;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    plan.ws_prefix_off = 0;
+    plan.ws_wseq_off = up(size_t(num_seqs + 1) * sizeof(int64_t));
+    plan.ws_acc_off = plan.ws_wseq_off + up(size_t(waves) * sizeof(int32_t));
+    plan.ws_ml_off = plan.ws_acc_off + up(slots * head_size * sizeof(float));
+    plan.workspace_bytes = plan.ws_ml_off + up(slots * 2 * sizeof(float));
+    (void)max_seq_len;
     return plan;
 }
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtype, int head_size,
                          hipStream_t stream) {
-    DecodeShape s{plan.part_size, plan.num_parts, plan.head_groups, plan.heads_per_group};
+    DecodeShape s;
+    s.chunk = plan.chunk;
+    s.head_groups = plan.head_groups;
+    s.heads_per_group = plan.heads_per_group;
+    s.units_per_seq = plan.units_per_seq;
+    s.num_waves = plan.num_waves;
+    s.tile = plan.tile;
+    s.max_len = p.max_seq_len;
     if (dtype == 1) {
         if (head_size == 128) return launch_group<bf16_t, 128>(p, s, plan.padded_group, stream);
         if (head_size == 64) return launch_group<bf16_t, 64>(p, s, plan.padded_group, stream);

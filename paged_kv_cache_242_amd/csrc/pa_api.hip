@@ -115,8 +115,8 @@ pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *val
 
 size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len) {
     if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0) return 0;
-    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, num_seqs,
-                           max_seq_len)
+    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, layer->dtype,
+                           num_seqs, max_seq_len)
         .workspace_bytes;
 }
 
@@ -141,9 +141,8 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache) || (q_row_stride * eb) % 16 != 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: out/query/kv_cache must be 16-byte aligned with 16-byte row strides",
                     fn);
-    const pa::DecodePlan plan =
-        pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, num_seqs,
-                           max_seq_len);
+    const pa::DecodePlan plan = pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size,
+                                                layer->block_size, layer->dtype, num_seqs, max_seq_len);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes)
             return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", fn, plan.workspace_bytes,
@@ -169,14 +168,12 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     p.scale = layer->scale;
     p.alibi_slopes = layer->alibi_slopes;
     p.window = layer->sliding_window;
-    p.ws_acc = nullptr;
-    p.ws_ml = nullptr;
-    if (plan.workspace_bytes > 0) {
-        const size_t slots = size_t(num_seqs) * layer->num_heads * plan.num_parts;
-        const size_t acc = (slots * layer->head_size * sizeof(float) + 255) / 256 * 256;
-        p.ws_acc = static_cast<float *>(workspace);
-        p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc);
-    }
+    p.max_seq_len = max_seq_len;
+    char *ws = static_cast<char *>(workspace);
+    p.ws_prefix = reinterpret_cast<int64_t *>(ws + plan.ws_prefix_off);
+    p.ws_wseq = reinterpret_cast<int32_t *>(ws + plan.ws_wseq_off);
+    p.ws_acc = reinterpret_cast<float *>(ws + plan.ws_acc_off);
+    p.ws_ml = reinterpret_cast<float *>(ws + plan.ws_ml_off);
     hipError_t e = pa::launch_decode(p, plan, layer->dtype, layer->head_size, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();

@@ -20,17 +20,20 @@ struct CacheWriteParams {
 };
 hipError_t launch_cache_write(const CacheWriteParams &p, hipStream_t stream);
 
-// Split-KV policy shared by pa_decode and pa_decode_workspace_size.
+// Decode policy shared by pa_decode and pa_decode_workspace_size.
 struct DecodePlan {
     int32_t head_groups;      // query heads of one KV head are processed in this many groups
     int32_t heads_per_group;  // real heads per group (<= 8)
     int32_t padded_group;     // heads_per_group rounded up to 1, 2, 4 or 8
-    int32_t part_size;        // keys per split-KV partition (multiple of 256, <= 128 blocks)
-    int32_t num_parts;        // partitions of the longest sequence
-    size_t workspace_bytes;   // 0 when num_parts == 1
+    int32_t units_per_seq;    // num_kv_heads * head_groups work units per sequence
+    int32_t chunk;            // keys per block-id chunk
+    int32_t tile;             // keys per tile of the kernel instance
+    int32_t num_waves;        // wavefronts of the even split (resident at once on the device)
+    size_t ws_prefix_off, ws_wseq_off, ws_acc_off, ws_ml_off;   // workspace layout (bytes)
+    size_t workspace_bytes;
 };
 DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                       int32_t num_seqs, int32_t max_seq_len);
+                       int32_t dtype, int32_t num_seqs, int32_t max_seq_len);
 
 struct DecodeParams {
     void *out;                // [B, H*D]
@@ -42,6 +45,7 @@ struct DecodeParams {
     int32_t max_blocks;
     const int32_t *seq_lens;
     int32_t num_seqs;
+    int32_t max_seq_len;
     int32_t num_heads;
     int32_t num_kv_heads;
     int32_t block_shift;      // log2(block_size)
@@ -49,8 +53,10 @@ struct DecodeParams {
     float scale;
     const float *alibi_slopes;
     int32_t window;
-    float *ws_acc;            // [B, H, num_parts, D]
-    float *ws_ml;             // [B, H, num_parts, 2]
+    int64_t *ws_prefix;       // [B + 1] tiles of the work units of sequences before q
+    int32_t *ws_wseq;         // [num_waves] sequence of each wavefront's first tile
+    float *ws_acc;            // [slots, D] partial weighted V
+    float *ws_ml;             // [slots, 2] partial (max, sum)
 };
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtype, int head_size,
                          hipStream_t stream);

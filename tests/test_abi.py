@@ -97,10 +97,14 @@ def test_bad_pointers_and_alignment(pa):
     assert st == 1 and "cached context" in lib.pa_last_error_message().decode()
 
 
-def test_workspace_size_short_context_is_zero(pa):
+def test_workspace_size(pa):
+    """Any batch needs the split's workspace; its size does not depend on max_seq_len."""
     lib = pa.library()
     c = _layer(pa)
-    assert lib.pa_decode_workspace_size(ctypes.byref(c), 8, 100) == 0
+    short = lib.pa_decode_workspace_size(ctypes.byref(c), 8, 100)
+    assert short > 0 and short % 256 == 0
+    assert lib.pa_decode_workspace_size(ctypes.byref(c), 8, 100000) == short
+    assert lib.pa_decode_workspace_size(ctypes.byref(c), 16, 100) > short
     assert lib.pa_decode_workspace_size(ctypes.byref(c), 0, 100) == 0
 
 
