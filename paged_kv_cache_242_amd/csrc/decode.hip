@@ -118,6 +118,7 @@ struct DecodeShape {
     int num_waves;          // wavefronts of the split kernel
     int tile;               // keys per tile of the split kernel instance
     int max_len;            // bound on every sequence length
+    int kvh;                // KV heads per work unit
 };
 
 template <typename T>
@@ -174,7 +175,7 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
 #define PA_DECODE_DEPTH_B 2
 #endif
 #ifndef PA_DECODE_OCC_B
-#define PA_DECODE_OCC_B 2
+#define PA_DECODE_OCC_B 1
 #endif
 template <typename T, int GP>
 constexpr int tile_loads() {
@@ -295,11 +296,16 @@ __device__ __forceinline__ void load_ids(const DecodeParams &p, const DecodeShap
 // wavefronts are consecutive and along a wavefront the units are), merged afterwards.
 //   ONE_BLOCK: every tile lies inside one cache block (tile keys <= block size), so a tile needs
 //              one block id; otherwise each load instruction looks up its own block.
-template <typename T, int D, int GP, int NI, bool ONE_BLOCK, int DEPTH, int OCC>
+//   KVH: KV heads per work unit (1, or 2 for small head groups): the R row groups of a load
+//        instruction are then KVH adjacent head rows of R / KVH tokens, so one instruction reads
+//        KVH * 16 * C contiguous bytes per token instead of one head's slice.
+template <typename T, int D, int GP, int NI, bool ONE_BLOCK, int DEPTH, int OCC, int KVH>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     constexpr int C = Geo<T, D>::kC, R = Geo<T, D>::kR, EPL = Geo<T, D>::kEpl;
-    constexpr int TILE = NI * R;                       // keys per tile
+    constexpr int TR = R / KVH;                        // tokens per load instruction
+    constexpr int TILE = NI * TR;                      // keys per tile
+    static_assert(R % KVH == 0, "row groups split evenly over the unit's KV heads");
     constexpr int WMASK = writer_mask<C, GP>();
     static_assert(NI % 2 == 0, "rows are paired for v_dot2");
 
@@ -310,6 +316,8 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     const int lane = threadIdx.x;
     const int c = lane % C;
     const int r = lane / C;
+    const int hk = r % KVH;                  // KV head of this row group within the unit
+    const int tr = r / KVH;                  // token of this row group within an instruction
     const int my_head = head_of_lane<C, GP>(c);
     const int group = p.num_heads / p.num_kv_heads;
     const int nh = shape.heads_per_group;
@@ -342,11 +350,12 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
         const int u_in = int(local / ts);
         const int tile0 = int(local - int64_t(u_in) * ts);
         const int tile1 = int(min(int64_t(ts), int64_t(tile0) + (t_end - t)));
-        const int g = u_in / shape.head_groups;
-        const int hgrp = u_in - g * shape.head_groups;
-        const int head0 = g * group + hgrp * nh;
+        const int gu = u_in / shape.head_groups;
+        const int hgrp = u_in - gu * shape.head_groups;
+        const int g = gu * KVH + hk;                       // this lane's KV head
+        const int head0 = g * group + hgrp * nh;           // this lane's first query head
 
-        // ---- one segment: tiles tile0 .. tile1 - 1 of unit (seq, g, hgrp)
+        // ---- one segment: tiles tile0 .. tile1 - 1 of unit (seq, KV heads gu KVH.., hgrp)
         uint32_t q[GP][4];      // query chunks, head-permuted: slot s holds head s ^ my_head
         {
             const T *qrow =
@@ -364,7 +373,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
         const int kfirst = (lo / TILE + tile0) * TILE;
         const int kend = min(L, (lo / TILE + tile1) * TILE);
         // Lane part of every K/V address: row group r's token inside the instruction, KV head g, chunk c.
-        const uint32_t lane_off = uint32_t(r) * row_bytes + (uint32_t(g) * D + c * EPL) * sizeof(T);
+        const uint32_t lane_off = uint32_t(tr) * row_bytes + (uint32_t(g) * D + c * EPL) * sizeof(T);
 
         float m_run = -INFINITY;      // head my_head, this row group
         float l_run = 0.f;            // sum of rounded weights, head my_head, this row group
@@ -385,12 +394,12 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             }
             if (has_alibi) {
 #pragma unroll
-                for (int i = 0; i < NI; ++i) sc[i] += slope2 * float(tb + i * R + r - pos);
+                for (int i = 0; i < NI; ++i) sc[i] += slope2 * float(tb + i * TR + tr - pos);
             }
             if (edge) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    const int j = tb + i * R + r;
+                    const int j = tb + i * TR + tr;
                     sc[i] = (j >= lo && j <= pos) ? sc[i] : -INFINITY;
                 }
             }
@@ -437,7 +446,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             if (tb + TILE - 1 > pos) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    const bool past = tb + i * R + r > pos;
+                    const bool past = tb + i * TR + tr > pos;
                     vr[i].x = past ? 0u : vr[i].x;
                     vr[i].y = past ? 0u : vr[i].y;
                     vr[i].z = past ? 0u : vr[i].z;
@@ -495,7 +504,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             // plus the instruction's first token inside the block.  Tokens past the sequence's end
             // read unwritten slots of in-pool blocks; their scores are masked, their V rows zeroed.
             auto inst_base = [&](int tb, int i, int blk_tile) -> int64_t {
-                const int row0 = tb + i * R;
+                const int row0 = tb + i * TR;
                 int blk = blk_tile;
                 if constexpr (!ONE_BLOCK) {
                     const int bidx = (row0 >> p.block_shift) - pblock0;
@@ -549,36 +558,36 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             }
         }
 
-        // Bring the row groups to a common max per head, then sum them; lanes of row group 0
-        // end with the segment's weighted V for all heads.
-        const float m_all = max_row_groups<C>(m_run);
+        // Bring the row groups of each KV head to a common max per head, then sum them; lanes of
+        // row groups 0 .. KVH - 1 end with the segment's weighted V for all heads of their KV head.
+        const float m_all = max_row_groups<C * KVH>(m_run);
         const float f_own = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_all);
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
             const float f = __shfl(f_own, r * C + lane_of_head<C, GP>(h), 64);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = sum_row_groups<C>(acc[h][e] * f);
+            for (int e = 0; e < EPL; ++e) acc[h][e] = sum_row_groups<C * KVH>(acc[h][e] * f);
         }
-        const float l_sum = sum_row_groups<C>(l_run * f_own);
+        const float l_sum = sum_row_groups<C * KVH>(l_run * f_own);
         if (tile0 == 0 && tile1 == ts) {
             // The whole (windowed) unit is this segment: write the normalized output.
             T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head0) * D;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                const float lh = __shfl(l_sum, lane_of_head<C, GP>(h), 64);
-                if (r == 0 && h < nh) {
+                const float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
+                if (tr == 0 && h < nh) {
                     const float inv = 1.f / lh;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) store_out<T>(out_row + h * D + c * EPL + e, acc[h][e] * inv);
                 }
             }
         } else {
-            const int64_t slot0 = (int64_t(wave) + int64_t(seq) * ups + u_in) * nh;
+            const int64_t slot0 = (int64_t(wave) + int64_t(seq) * ups + u_in) * (KVH * nh) + hk * nh;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                const float lh = __shfl(l_sum, lane_of_head<C, GP>(h), 64);
-                const float mh = __shfl(m_all, lane_of_head<C, GP>(h), 64);
-                if (r == 0 && h < nh) {
+                const float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
+                const float mh = __shfl(m_all, r * C + lane_of_head<C, GP>(h), 64);
+                if (tr == 0 && h < nh) {
                     const int64_t slot = slot0 + h;
                     float4 *dst = reinterpret_cast<float4 *>(p.ws_acc + slot * D + c * EPL);
 #pragma unroll
@@ -609,15 +618,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
     const int nh = shape.heads_per_group;
-    const int u = blockIdx.x / nh;
-    const int h = blockIdx.x - u * nh;
+    const int nhu = nh * shape.kvh;          // heads of a work unit
+    const int u = blockIdx.x / nhu;
+    const int hh = blockIdx.x - u * nhu;
     const int ups = shape.units_per_seq;
     const int seq = u / ups;
     const int u_in = u - seq * ups;
-    const int g = u_in / shape.head_groups;
-    const int hgrp = u_in - g * shape.head_groups;
-    const int head0 = g * (p.num_heads / p.num_kv_heads) + hgrp * nh;
-    T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head0 + h) * D;
+    const int gu = u_in / shape.head_groups;
+    const int hgrp = u_in - gu * shape.head_groups;
+    const int g = gu * shape.kvh + hh / nh;
+    const int head = g * (p.num_heads / p.num_kv_heads) + hgrp * nh + hh % nh;
+    T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head) * D;
     int L, lo;
     const int ts = seq_tiles(p, shape, seq, L, lo);
     if (ts == 0) {                          // empty sequence: zero output
@@ -636,7 +647,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     auto has_tiles = [&](int i) {
         return int64_t(i) * Ttot / shape.num_waves < int64_t(i + 1) * Ttot / shape.num_waves;
     };
-    auto slot_of = [&](int j) { return (int64_t(i0 + j) + u) * nh + h; };
+    auto slot_of = [&](int j) { return (int64_t(i0 + j) + u) * nhu + hh; };
     float M = -INFINITY;
     for (int j = lane; j < n; j += 64)
         if (has_tiles(i0 + j)) M = fmaxf(M, p.ws_ml[slot_of(j) * 2]);
@@ -670,21 +681,36 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] * inv);
 }
 
-template <typename T, int D, int GP>
-constexpr int tile_keys() { return tile_loads<T, GP>() * Geo<T, D>::kR; }
+// KV heads per work unit: 2 for bf16 head groups of 1 or 2 (whole 512-byte runs of two adjacent
+// head rows per token instead of 256-byte slices), when the KV head count is even.
+#ifndef PA_DECODE_KVH_S
+#define PA_DECODE_KVH_S 2
+#endif
+#ifndef PA_DECODE_KVH_M
+#define PA_DECODE_KVH_M 2
+#endif
+#ifndef PA_DECODE_KVH_B
+#define PA_DECODE_KVH_B 1
+#endif
+template <typename T, int GP>
+constexpr int kvh_max() {
+    return sizeof(T) == 4 ? 1 : (GP <= 2 ? PA_DECODE_KVH_S : (GP == 4 ? PA_DECODE_KVH_M : PA_DECODE_KVH_B));
+}
 
-template <typename T, int D, int GP, bool ONE>
+template <typename T, int D, int GP, int KVH>
+constexpr int tile_keys() { return tile_loads<T, GP>() * Geo<T, D>::kR / KVH; }
+
+template <typename T, int D, int GP, bool ONE, int KVH>
 const void *split_kernel_fn() {
     return reinterpret_cast<const void *>(
-        &decode_split_kernel<T, D, GP, tile_loads<T, GP>(), ONE, tile_depth<T, GP>(), tile_occ<T, GP>()>);
+        &decode_split_kernel<T, D, GP, tile_loads<T, GP>(), ONE, tile_depth<T, GP>(), tile_occ<T, GP>(), KVH>);
 }
 
 // Resident wavefronts of the split kernel instance on the current device (occupancy x CUs),
 // cached per device and instance.
-template <typename T, int D, int GP>
+template <typename T, int D, int GP, int KVH>
 int split_waves(int block_shift) {
-    constexpr int NI = tile_loads<T, GP>();
-    constexpr int TILE = NI * Geo<T, D>::kR;
+    constexpr int TILE = tile_keys<T, D, GP, KVH>();
     const bool one = (1 << block_shift) >= TILE;
     static int cache[64][2];
     int dev = 0;
@@ -693,55 +719,75 @@ int split_waves(int block_shift) {
     if (slot > 0) return slot;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    const void *fn = one ? split_kernel_fn<T, D, GP, true>() : split_kernel_fn<T, D, GP, false>();
+    const void *fn = one ? split_kernel_fn<T, D, GP, true, KVH>() : split_kernel_fn<T, D, GP, false, KVH>();
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 8;
     slot = cus * per_cu;
     return slot;
 }
 
-template <typename T, int D, int GP, bool ONE>
+template <typename T, int D, int GP, bool ONE, int KVH>
 hipError_t launch_split(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<T, D, GP, tile_loads<T, GP>(), ONE, tile_depth<T, GP>(), tile_occ<T, GP>()>),
-                       dim3(unsigned(s.num_waves)), dim3(64), 0, stream, p, s);
+    hipLaunchKernelGGL(
+        (decode_split_kernel<T, D, GP, tile_loads<T, GP>(), ONE, tile_depth<T, GP>(), tile_occ<T, GP>(), KVH>),
+        dim3(unsigned(s.num_waves)), dim3(64), 0, stream, p, s);
     return hipGetLastError();
 }
 
-template <typename T, int D, int GP>
+template <typename T, int D, int GP, int KVH>
 hipError_t launch_typed(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
-    constexpr int NI = tile_loads<T, GP>();
-    constexpr int TILE = NI * Geo<T, D>::kR;
+    constexpr int TILE = tile_keys<T, D, GP, KVH>();
     const int64_t units = int64_t(p.num_seqs) * s.units_per_seq;
     if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const bool one_block = (1 << p.block_shift) >= TILE;
-    e = one_block ? launch_split<T, D, GP, true>(p, s, stream) : launch_split<T, D, GP, false>(p, s, stream);
+    e = one_block ? launch_split<T, D, GP, true, KVH>(p, s, stream) : launch_split<T, D, GP, false, KVH>(p, s, stream);
     if (e != hipSuccess) return e;
-    const int64_t merges = units * s.heads_per_group;
+    const int64_t merges = units * s.heads_per_group * KVH;
     if (merges > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(unsigned(merges)), dim3(64), 0, stream, p, s);
     return hipGetLastError();
 }
 
+template <typename T, int D, int GP>
+hipError_t launch_kvh(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
+    if constexpr (kvh_max<T, GP>() > 1) {
+        if (s.kvh == kvh_max<T, GP>()) return launch_typed<T, D, GP, kvh_max<T, GP>()>(p, s, stream);
+    }
+    return launch_typed<T, D, GP, 1>(p, s, stream);
+}
+
 template <typename T, int D>
 hipError_t launch_group(const DecodeParams &p, const DecodeShape &s, int padded_group, hipStream_t stream) {
     switch (padded_group) {
-        case 1: return launch_typed<T, D, 1>(p, s, stream);
-        case 2: return launch_typed<T, D, 2>(p, s, stream);
-        case 4: return launch_typed<T, D, 4>(p, s, stream);
-        case 8: return launch_typed<T, D, 8>(p, s, stream);
+        case 1: return launch_kvh<T, D, 1>(p, s, stream);
+        case 2: return launch_kvh<T, D, 2>(p, s, stream);
+        case 4: return launch_kvh<T, D, 4>(p, s, stream);
+        case 8: return launch_kvh<T, D, 8>(p, s, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <typename T, int D, int GP>
+void instance_info_gp(int num_kv_heads, int block_shift, int &kvh, int &tile, int &waves) {
+    kvh = (kvh_max<T, GP>() > 1 && num_kv_heads % kvh_max<T, GP>() == 0) ? kvh_max<T, GP>() : 1;
+    if (kvh > 1) {
+        tile = tile_keys<T, D, GP, kvh_max<T, GP>()>();
+        waves = split_waves<T, D, GP, kvh_max<T, GP>()>(block_shift);
+    } else {
+        tile = tile_keys<T, D, GP, 1>();
+        waves = split_waves<T, D, GP, 1>(block_shift);
+    }
+}
+
 template <typename T, int D>
-void instance_info(int padded_group, int block_shift, int &tile, int &waves) {
+void instance_info(int padded_group, int num_kv_heads, int block_shift, int &kvh, int &tile, int &waves) {
     switch (padded_group) {
-        case 1: tile = tile_keys<T, D, 1>(); waves = split_waves<T, D, 1>(block_shift); break;
-        case 2: tile = tile_keys<T, D, 2>(); waves = split_waves<T, D, 2>(block_shift); break;
-        case 4: tile = tile_keys<T, D, 4>(); waves = split_waves<T, D, 4>(block_shift); break;
-        default: tile = tile_keys<T, D, 8>(); waves = split_waves<T, D, 8>(block_shift); break;
+        case 1: instance_info_gp<T, D, 1>(num_kv_heads, block_shift, kvh, tile, waves); break;
+        case 2: instance_info_gp<T, D, 2>(num_kv_heads, block_shift, kvh, tile, waves); break;
+        case 4: instance_info_gp<T, D, 4>(num_kv_heads, block_shift, kvh, tile, waves); break;
+        default: instance_info_gp<T, D, 8>(num_kv_heads, block_shift, kvh, tile, waves); break;
     }
 }
 
@@ -757,23 +803,24 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     plan.heads_per_group = (group + plan.head_groups - 1) / plan.head_groups;
     plan.padded_group = 1;
     while (plan.padded_group < plan.heads_per_group) plan.padded_group <<= 1;
-    plan.units_per_seq = num_kv_heads * plan.head_groups;
     // Block-id chunk: 128 blocks (two id registers per lane), at most 4096 keys.
     plan.chunk = (128 << block_shift) < 4096 ? (128 << block_shift) : 4096;
-    int tile = 32, waves = 2048;
+    int kvh = 1, tile = 32, waves = 2048;
     if (dtype == 1) {
-        if (head_size == 128) instance_info<bf16_t, 128>(plan.padded_group, block_shift, tile, waves);
-        else instance_info<bf16_t, 64>(plan.padded_group, block_shift, tile, waves);
+        if (head_size == 128) instance_info<bf16_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+        else instance_info<bf16_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
     } else {
-        if (head_size == 128) instance_info<float, 128>(plan.padded_group, block_shift, tile, waves);
-        else instance_info<float, 64>(plan.padded_group, block_shift, tile, waves);
+        if (head_size == 128) instance_info<float, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+        else instance_info<float, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
     }
+    plan.kv_per_unit = kvh;
+    plan.units_per_seq = num_kv_heads / kvh * plan.head_groups;
     plan.tile = tile;
     plan.num_waves = waves;
     // Workspace: tile prefix per sequence, first sequence per wavefront, then the partial slots
     // (one per (wavefront, unit) pair that can meet: at most num_waves + units) of nh heads.
     const size_t units = size_t(num_seqs) * plan.units_per_seq;
-    const size_t slots = (size_t(waves) + units) * plan.heads_per_group;
+    const size_t slots = (size_t(waves) + units) * plan.heads_per_group * kvh;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     plan.ws_prefix_off = 0;
     plan.ws_wseq_off = up(size_t(num_seqs + 1) * sizeof(int64_t));
@@ -794,6 +841,7 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
     s.num_waves = plan.num_waves;
     s.tile = plan.tile;
     s.max_len = p.max_seq_len;
+    s.kvh = plan.kv_per_unit;
     if (dtype == 1) {
         if (head_size == 128) return launch_group<bf16_t, 128>(p, s, plan.padded_group, stream);
         if (head_size == 64) return launch_group<bf16_t, 64>(p, s, plan.padded_group, stream);
