@@ -86,7 +86,7 @@ def decode_source_hash() -> str:
 
 
 def measured_traffic(workload: int):
-    """HBM bytes per decode call (partition + merge kernels) from the committed rocprofv3 counter
+    """HBM bytes per decode call (plan + split + merge kernels) from the committed rocprofv3 counter
     summary, or None when there is none for this workload or the decode kernel source changed
     since the counters were taken."""
     try:
@@ -270,7 +270,7 @@ def main(argv=None):
                                "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
         roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
-                    "kernel": "decode_partition_kernel (+ decode_merge_kernel when split)",
+                    "kernel": "decode_split_kernel (+ decode_plan_kernel and decode_merge_kernel: one pa_decode call)",
                     "algorithmic_bytes_per_launch": nbytes}
     else:
         value = secondary["prefill"]["TFLOP_per_s"]
