@@ -102,6 +102,17 @@ __device__ __forceinline__ int vswz(int r) {
     return D == 128 ? (r & 7) : ((r >> 1) & 3);
 }
 
+// max(x, x of lane ^ 16) and max(x, x of lane ^ 32) with the gfx950 row-swap moves (VALU, no
+// LDS traffic): swapping x with itself leaves each lane one of its own value and its partner's.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // One 16-byte-per-lane global -> LDS copy: lane l reads base + soff + lane_off (bytes) and fills
 // 16-byte unit l of the 1 KB stretch at lds_dst.  base and soff must be wave-uniform; base goes
 // into a raw buffer descriptor (scalar registers), soff into the scalar offset and the lane
@@ -392,6 +403,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+        // Raised wave priority while the score MFMAs issue: when both wavefronts of a SIMD want the
+        // matrix unit, this one goes first and the other turns to its exponentials, so the two
+        // drift into alternating phases instead of colliding.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
@@ -406,6 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
                 for (int qbk = 0; qbk < 2; ++qbk)
                     s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arel[kk], bslope, s[kk][qbk], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         load_v(vs, kc);
 
         // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
@@ -445,8 +461,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) {
-                float r = fmaxf(tmax[qbk], lane_xor<16>(tmax[qbk]));
-                r = fmaxf(r, lane_xor<32>(r));
+                const float r = max_xor32(max_xor16(tmax[qbk]));
                 const float m_new = fmaxf(m_run[qbk], r);
                 const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
                 m_run[qbk] = m_new;
