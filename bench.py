@@ -127,16 +127,18 @@ def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20
     q = wl.host_bits(batch.query[tp:])
     lens = batch.decode_seq_lens
     order = np.random.default_rng(batch.seed).permutation(len(lens))
-    # calibrate on a small slice, then size the sample for ~budget_s of CPU work
-    per_byte = None
+    # Calibrate on a small slice, then size the sample for ~budget_s of CPU work, cycling over the
+    # sequences (in the same seeded order) as often as the budget allows, at most `max_passes` times.
+    max_passes = 1000
     done_bytes = 0
     done_time = 0.0
     used = 0
-    taken = []
+    calls = 0
     start = 0
     chunk = 4
-    while start < len(order):
-        idx = order[start:start + chunk]
+    while start < max_passes * len(order):
+        pos = start % len(order)
+        idx = order[pos:pos + min(chunk, len(order) - pos)]
         t0 = time.perf_counter()
         _, used = oracle.decode(ol, q[idx], pool, batch.decode_block_tables[idx], lens[idx], return_threads=True)
         dt = time.perf_counter() - t0
@@ -144,20 +146,21 @@ def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20
         nbytes = int(vis.astype(np.int64).sum()) * L.num_kv_heads * L.head_size * 2 * L.elt_bytes
         done_bytes += nbytes
         done_time += dt
-        taken.extend(int(i) for i in idx)
-        start += chunk
-        per_byte = done_time / max(done_bytes, 1)
+        calls += len(idx)
+        start += len(idx)
+        per_seq = done_time / calls
         remaining = budget_s - done_time
         if remaining <= 0:
             break
-        chunk = max(1, min(len(order) - start, int(remaining / max(per_byte * nbytes / len(idx), 1e-9))))
+        chunk = max(1, int(remaining / max(per_seq, 1e-9)))
     return {
         "value": done_bytes / done_time / 1e9,
         "unit": "GB/s",
         "cores": int(used),
         "kind": "oracle",
-        "sample": f"fp64 oracle decode of {len(taken)} of {len(lens)} decode sequences of the same batch "
-                  f"({done_bytes / 1e9:.2f} GB of visible K+V, {done_time:.1f} s), cpu "
+        "sample": f"fp64 oracle decode of {calls} sequences ({calls / len(lens):.1f} passes over the {len(lens)} "
+                  f"decode sequences of the same batch, seeded order; {done_bytes / 1e9:.2f} GB of visible K+V, "
+                  f"{done_time:.1f} s), cpu "
                   f"{platform.processor() or platform.machine()}",
     }
 
