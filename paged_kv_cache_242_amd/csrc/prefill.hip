@@ -7,13 +7,15 @@
 // 0 .. c_i + t, the first c_i of which are read from the paged cache through the block table and
 // the rest from the key/value rows of the call; sliding window and ALiBi as in decode.
 //
-// bf16 kernel (MFMA).  A workgroup of 4 wavefronts owns 128 consecutive query rows of one
-// (sequence, query head); each wavefront owns 32 rows (two 16-row MFMA blocks).  It walks the
-// needed keys in 64-key tiles that are staged in LDS:
+// bf16 kernel (MFMA).  A workgroup of 4 wavefronts owns 128 (query row, head) pairs of one
+// sequence and KV head: 32 consecutive rows of 4 query heads of the group when the group size is
+// a multiple of 4 (all four wavefronts then share one diagonal), 64 rows of 2 heads, or 128 rows
+// of one head.  Each wavefront owns 32 rows of one head (two 16-row MFMA blocks).  The workgroup
+// walks the needed keys in 64-key tiles that are staged in LDS:
 //   * K tile row-major [64][D] (16-byte chunks xor-swizzled by row, so the 16 rows an MFMA
 //     operand read touches hit distinct banks);
-//   * V tile transposed [D][64] (keys contiguous per d, in a key order matched to the P
-//     operand below, 16-byte units xor-swizzled by d).
+//   * V tile row-major [64][D] (32-byte units xor-swizzled by row), read transposed by
+//     ds_read_b64_tr_b16.
 // Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the accumulator
 // layout then gives every lane 4 consecutive keys of ONE query row, so the row's max and sum
 // need only two cross-lane steps, and two key blocks of those lanes are exactly the 8-key
@@ -30,7 +32,7 @@
 namespace pa {
 namespace {
 
-constexpr int kBM = 128;       // query rows per workgroup
+constexpr int kRowsPerBlock = 128;   // (query row, head) pairs per workgroup: 4 wavefronts x 32 rows
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;
 // The running row max is raised only when a tile's max exceeds it by more than this (base-2
@@ -82,10 +84,12 @@ __device__ __forceinline__ void row_ptrs(const PrefillParams &p, const SeqInfo &
 // one XCD and share its L2, and each XCD takes every 8th group in heavy-first order (late query
 // tiles see the most keys).
 struct PrefillGrid {
-    int num_qtiles;        // ceil(max_subquery_len / kBM)
+    int heads;             // query heads per workgroup (hp = 4, 2 or 1; divides G)
+    int rows;              // query rows per workgroup (128 / hp)
+    int num_qtiles;        // ceil(max_subquery_len / rows)
     int qtiles_per_group;  // query tiles in a group
     int num_qblocks;       // ceil(num_qtiles / qtiles_per_group)
-    int group_size;        // G * qtiles_per_group workgroups
+    int group_size;        // (G / hp) * qtiles_per_group workgroups
     int num_groups;        // num_qblocks * num_seqs * num_kv_heads
 };
 
@@ -174,18 +178,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const int qb = grid.num_qblocks - 1 - k / per_qb;
     const int seq = (k % per_qb) / p.num_kv_heads;
     const int g = k % p.num_kv_heads;
-    const int h = g * group + member % group;
-    const int qt = qb * grid.qtiles_per_group + member / group;
+    const int hblocks = group / grid.heads;
+    const int qt = qb * grid.qtiles_per_group + member / hblocks;
     const SeqInfo si = seq_info(p, seq);
-    if (qt >= grid.num_qtiles || qt * kBM >= si.n) return;
+    if (qt >= grid.num_qtiles || qt * grid.rows >= si.n) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int lg = lane >> 4;
-    const int t0 = qt * kBM + wave * 32;     // first subquery row of this wavefront
-    const int p0 = si.c + t0;                // its position
+    // wavefront -> (head, 32-row strip): with hp heads per workgroup the wavefronts share strips,
+    // so for hp = 4 all four see the same diagonal and reach every tile with equal work
+    const int h = g * group + (member % hblocks) * grid.heads + wave % grid.heads;
+    const int t0 = qt * grid.rows + (wave / grid.heads) * 32;   // first subquery row of this wavefront
+    const int p0 = si.c + t0;                                  // its position
 
     const float qk_scale = p.scale * kLog2e;
     const float qk_eff = qk_scale > 0.f ? qk_scale : (qk_scale < 0.f ? -qk_scale : 1.f);
@@ -210,8 +217,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         }
     }
 
-    const int row_hi = min(qt * kBM + kBM, si.n) - 1;
-    const int pos_lo = si.c + qt * kBM;
+    const int row_hi = min(qt * grid.rows + grid.rows, si.n) - 1;
+    const int pos_lo = si.c + qt * grid.rows;
     const int key_hi = si.c + row_hi;
     const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
     const int kt_lo = key_lo / kBN, kt_hi = key_hi / kBN;
@@ -646,12 +653,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipStream_t stream) {
     if (dtype == 1) {
         PrefillGrid grid;
-        grid.num_qtiles = (p.max_subquery_len + kBM - 1) / kBM;
         const int group = p.num_heads / p.num_kv_heads;
-        grid.qtiles_per_group = group >= 8 ? 1 : min(8 / group, grid.num_qtiles);
+        grid.heads = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+        grid.rows = kRowsPerBlock / grid.heads;
+        grid.num_qtiles = (p.max_subquery_len + grid.rows - 1) / grid.rows;
+        const int hblocks = group / grid.heads;
+        grid.qtiles_per_group = hblocks >= 8 ? 1 : min(8 / hblocks, grid.num_qtiles);
         if (grid.qtiles_per_group < 1) grid.qtiles_per_group = 1;
         grid.num_qblocks = (grid.num_qtiles + grid.qtiles_per_group - 1) / grid.qtiles_per_group;
-        grid.group_size = group * grid.qtiles_per_group;
+        grid.group_size = hblocks * grid.qtiles_per_group;
         const int64_t groups = int64_t(grid.num_qblocks) * p.num_seqs * p.num_kv_heads;
         if (groups == 0) return hipSuccess;
         const int64_t blocks = (groups + 7) / 8 * 8 * grid.group_size;
