@@ -156,6 +156,8 @@ PREFILL_LAYERS = [
     _layer(8, 2, 128, 16, scale=-0.09),                 # negative scale
     _layer(8, 8, 64, 16, alibi=True, scale=0.0),        # zero scale: weights from ALiBi alone
     _layer(4, 4, 128, 32, alibi=True, window=700),
+    _layer(16, 2, 128, 64),                             # 8 heads per KV head: two workgroups of 4 heads
+    _layer(8, 8, 128, 256, alibi=True, window=300),     # 256-token blocks
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
