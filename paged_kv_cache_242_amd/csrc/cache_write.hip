@@ -13,26 +13,48 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;      // 16-byte chunks in flight per thread
 
+// A workgroup moves `tokens_per_block` whole tokens (K row then V row, 16-byte chunks, chunk
+// index idx = token * 2 * chunks_per_row + which * chunks_per_row + chunk); thread x takes chunks
+// x, x + 256, ...  Each thread first issues up to kUnroll source loads (they do not depend on the
+// slot), then looks up the slots and stores, so several loads per thread are in flight instead of
+// one load-store round trip at a time.
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams p, int tokens_per_block,
                                                                 int chunks_per_row) {
-    const int per_token = 2 * chunks_per_row;                  // K row then V row
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int per_token = 2 * chunks_per_row;
     const int64_t first = int64_t(blockIdx.x) * tokens_per_block;
     const int total = tokens_per_block * per_token;
-    for (int idx = threadIdx.x; idx < total; idx += kThreads) {
-        const int local = idx / per_token;
-        const int rem = idx - local * per_token;
-        const int which = rem >= chunks_per_row;               // 0 = key, 1 = value
-        const int chunk = rem - which * chunks_per_row;
-        const int64_t t = first + local;
-        if (t >= p.num_tokens) break;
-        const int64_t s = p.slot_mapping[t];
-        if (s < 0 || s >= p.num_slots) continue;               // padded token or out-of-range slot
-        const char *src = (which ? p.value : p.key) + t * p.kv_stride_bytes + int64_t(chunk) * 16;
-        char *dst = p.kv_cache + which * p.plane_bytes + s * p.row_bytes + int64_t(chunk) * 16;
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
-        *reinterpret_cast<u32x4 *>(dst) = v;
+    for (int base = threadIdx.x; base < total; base += kThreads * kUnroll) {
+        u32x4 v[kUnroll];
+        int64_t slot[kUnroll];
+        int64_t dst_off[kUnroll];   // destination byte offset of the chunk inside its plane row
+        bool live[kUnroll];
+        // loads are unconditional (a chunk past the end re-reads one of the last token) so that
+        // they all stay in flight together
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int idx = base + u * kThreads;
+            const int local = idx / per_token;
+            const int rem = idx - local * per_token;
+            const int which = rem >= chunks_per_row;           // 0 = key, 1 = value
+            const int chunk = rem - which * chunks_per_row;
+            const int64_t t = first + local;
+            live[u] = idx < total && t < p.num_tokens;
+            const int64_t tc = t < p.num_tokens ? t : p.num_tokens - 1;
+            const char *src = (which ? p.value : p.key) + tc * p.kv_stride_bytes + int64_t(chunk) * 16;
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+            slot[u] = p.slot_mapping[tc];
+            dst_off[u] = which * p.plane_bytes + int64_t(chunk) * 16;
+        }
+        __builtin_amdgcn_sched_barrier(0);      // every load issues before the first slot test
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t sl = slot[u];
+            if (live[u] && sl >= 0 && sl < p.num_slots)          // else padded token or out-of-range slot
+                *reinterpret_cast<u32x4 *>(p.kv_cache + dst_off[u] + sl * p.row_bytes) = v[u];
+        }
     }
 }
 
@@ -40,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(CacheWriteParams 
 
 hipError_t launch_cache_write(const CacheWriteParams &p, hipStream_t stream) {
     const int chunks = p.row_bytes / 16;
-    int tokens_per_block = kThreads / (2 * chunks);
+    int tokens_per_block = kThreads * kUnroll / (2 * chunks);
     if (tokens_per_block < 1) tokens_per_block = 1;
     const int64_t blocks = (p.num_tokens + tokens_per_block - 1) / tokens_per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
