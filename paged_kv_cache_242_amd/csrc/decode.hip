@@ -233,7 +233,11 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeParams p, Decod
     const int64_t ups = s.units_per_seq;
     int L, lo;
     int64_t sum = 0;
-    for (int q = a; q < b; ++q) sum += seq_tiles(p, s, q, L, lo);
+    // with one sequence per thread (up to 1024 sequences) its tile count stays in a register
+    const int own = per == 1 && a < b ? seq_tiles(p, s, a, L, lo) : 0;
+    if (per == 1) sum = own;
+    else
+        for (int q = a; q < b; ++q) sum += seq_tiles(p, s, q, L, lo);
     part[tid] = sum;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {           // inclusive scan of the chunk sums
@@ -243,12 +247,29 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeParams p, Decod
         __syncthreads();
     }
     int64_t run = tid > 0 ? part[tid - 1] : 0;
-    for (int q = a; q < b; ++q) {
-        p.ws_prefix[q] = run * ups;
-        run += seq_tiles(p, s, q, L, lo);
+    if (per == 1) {
+        if (a < b) p.ws_prefix[a] = run * ups;
+    } else {
+        for (int q = a; q < b; ++q) {
+            p.ws_prefix[q] = run * ups;
+            run += seq_tiles(p, s, q, L, lo);
+        }
     }
     const int64_t T = part[1023] * ups;
     if (tid == 0) p.ws_prefix[p.num_seqs] = T;
+    if (per == 1 && T > 0) {
+        // Wavefront i starts at tile floor(i T / N), inside sequence q iff it lies in
+        // [P_q, P_q+1): the wavefronts ceil(P_q N / T) .. ceil(P_q+1 N / T) - 1, which this
+        // sequence's thread writes (the ranges cover 0 .. N - 1 exactly).
+        if (a < b) {
+            const int64_t N = s.num_waves;
+            const int64_t p0 = (tid > 0 ? part[tid - 1] : 0) * ups, p1 = part[tid] * ups;
+            const int64_t lo = (p0 * N + T - 1) / T;
+            const int64_t hi = min((p1 * N + T - 1) / T, N);
+            for (int64_t i = lo; i < hi; ++i) p.ws_wseq[i] = a;
+        }
+        return;
+    }
     for (int i = tid; i < s.num_waves; i += 1024) {
         const int64_t t = int64_t(i) * T / s.num_waves;
         int seq = -1;
@@ -258,12 +279,14 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeParams p, Decod
                 const int mid = (c0 + c1) / 2;
                 if (part[mid] * ups > t) c1 = mid; else c0 = mid + 1;
             }
-            int64_t r = c0 > 0 ? part[c0 - 1] * ups : 0;
             int q = min(c0 * per, p.num_seqs - 1);
-            for (; q < p.num_seqs - 1; ++q) {
-                const int64_t ts = int64_t(seq_tiles(p, s, q, L, lo)) * ups;
-                if (r + ts > t) break;
-                r += ts;
+            if (per > 1) {                               // the sequence inside the chunk
+                int64_t r = c0 > 0 ? part[c0 - 1] * ups : 0;
+                for (; q < p.num_seqs - 1; ++q) {
+                    const int64_t ts = int64_t(seq_tiles(p, s, q, L, lo)) * ups;
+                    if (r + ts > t) break;
+                    r += ts;
+                }
             }
             seq = q;
         }
@@ -648,6 +671,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
         return int64_t(i) * Ttot / shape.num_waves < int64_t(i + 1) * Ttot / shape.num_waves;
     };
     auto slot_of = [&](int j) { return (int64_t(i0 + j) + u) * nhu + hh; };
+    // (m, l) of partial j in lane j (chunks of 64), maximum over all of them
     float M = -INFINITY;
     for (int j = lane; j < n; j += 64)
         if (has_tiles(i0 + j)) M = fmaxf(M, p.ws_ml[slot_of(j) * 2]);
@@ -661,16 +685,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
         const int j = j0 + lane;
         float f = 0.f;
         if (j < n && has_tiles(i0 + j)) {
-            f = fast_exp2(p.ws_ml[slot_of(j) * 2] - M);
-            den += f * p.ws_ml[slot_of(j) * 2 + 1];
+            const float2 ml = *reinterpret_cast<const float2 *>(p.ws_ml + slot_of(j) * 2);
+            f = fast_exp2(ml.x - M);
+            den += f * ml.y;
         }
         const int cnt = min(64, n - j0);
-        for (int jj = 0; jj < cnt; ++jj) {
-            const float fj = __shfl(f, jj, 64);
-            if (fj != 0.f) {
-                const float *a = p.ws_acc + slot_of(j0 + jj) * D;
+        // partials four at a time: their accumulator rows are loaded together (a slot of a
+        // wavefront that wrote nothing holds stale bits; the select drops them, NaN included)
+        for (int jb = 0; jb < cnt; jb += 4) {
+            float a[4][PER];
 #pragma unroll
-                for (int k = 0; k < PER; ++k) num[k] += fj * a[lane + 64 * k];
+            for (int q = 0; q < 4; ++q) {
+                const int jj = min(jb + q, cnt - 1);
+                const float *row = p.ws_acc + slot_of(j0 + jj) * D;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) a[q][k] = row[lane + 64 * k];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float fj = jb + q < cnt ? __shfl(f, jb + q, 64) : 0.f;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) num[k] += fj != 0.f ? fj * a[q][k] : 0.f;
             }
         }
     }
