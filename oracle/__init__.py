@@ -71,6 +71,11 @@ def _load():
                                     P, ctypes.c_int32, P, P, ctypes.c_int32, P, ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_int)]
         lib.orc_prefill.restype = ctypes.c_int
+        lib.orc_copy_blocks.argtypes = [ctypes.POINTER(_Layer), P, ctypes.c_int32, P, ctypes.c_int64]
+        lib.orc_copy_blocks.restype = ctypes.c_int
+        lib.orc_swap_blocks.argtypes = [ctypes.POINTER(_Layer), P, ctypes.c_int64, P, ctypes.c_int64, P,
+                                        ctypes.c_int64]
+        lib.orc_swap_blocks.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -130,6 +135,32 @@ def cache_write(layer: OracleLayer, key: np.ndarray, value: np.ndarray, slot_map
     st = _load().orc_cache_write(ctypes.byref(c), _ptr(key), _ptr(value), key.shape[1],
                                  key.shape[0], _ptr(slot_mapping), _ptr(kv_cache))
     _check(st, "cache_write")
+
+
+def copy_blocks(layer: OracleLayer, kv_caches, block_pairs: np.ndarray) -> None:
+    """In place, every cache of the list: block src -> block dst for each (src, dst) pair
+    (both planes; pairs outside [0, num_blocks) skipped; applied in order)."""
+    et = _elt_dtype(layer)
+    pairs = np.ascontiguousarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    for c in kv_caches:
+        assert c.dtype == et and c.flags.c_contiguous
+    ptrs = (ctypes.c_void_p * max(1, len(kv_caches)))(*[c.ctypes.data for c in kv_caches])
+    c, keep = layer._c()
+    st = _load().orc_copy_blocks(ctypes.byref(c), ptrs, len(kv_caches), _ptr(pairs), pairs.shape[0])
+    _check(st, "copy_blocks")
+
+
+def swap_blocks(layer: OracleLayer, src_cache: np.ndarray, dst_cache: np.ndarray, block_pairs: np.ndarray) -> None:
+    """In place: block src of src_cache -> block dst of dst_cache, both planes, for each pair.
+    The caches are [2, n_blocks, block elements] with their own block counts."""
+    et = _elt_dtype(layer)
+    assert src_cache.dtype == et and dst_cache.dtype == et and dst_cache.flags.c_contiguous
+    src_cache = np.ascontiguousarray(src_cache)
+    pairs = np.ascontiguousarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    c, keep = layer._c()
+    st = _load().orc_swap_blocks(ctypes.byref(c), _ptr(src_cache), src_cache.shape[1], _ptr(dst_cache),
+                                 dst_cache.shape[1], _ptr(pairs), pairs.shape[0])
+    _check(st, "swap_blocks")
 
 
 def decode(layer: OracleLayer, query: np.ndarray, kv_cache: np.ndarray, block_tables: np.ndarray,

@@ -102,6 +102,60 @@ static int layer_ok(const orc_layer *L)
 }
 
 /*
+ * Block moves (aphrodite-engine "xformers.py", XFormersBackend.copy_blocks and swap_blocks,
+ * which hand a block map to the paged-attention ops).  One block of one plane is
+ * block_size * num_kv_heads * head_size contiguous elements; a move carries both planes.
+ *
+ * copy_blocks: a map from a source block to a list of destination blocks, applied to the
+ * cache of every layer in the list.  Here the map arrives flattened into (src, dst) pairs; a
+ * pair naming a block outside [0, num_blocks) is skipped.  The pairs are applied in order.
+ * swap_blocks: a map from source block to destination block between two caches (which may
+ * hold different numbers of blocks); an index out of range is an error and nothing moves.
+ */
+static int64_t block_bytes(const orc_layer *L)
+{
+    return (int64_t)L->block_size * L->num_kv_heads * L->head_size * elt_bytes(L->dtype);
+}
+
+int orc_copy_blocks(const orc_layer *L, void *const *caches, int32_t num_layers, const int64_t *pairs,
+                    int64_t num_pairs)
+{
+    if (!layer_ok(L) || num_layers < 0 || num_pairs < 0) return ORC_BAD_ARG;
+    if (num_layers > 0 && num_pairs > 0 && (!caches || !pairs)) return ORC_BAD_ARG;
+    const int64_t bb = block_bytes(L);
+    const int64_t plane = L->num_blocks * bb;
+    for (int32_t l = 0; l < num_layers; ++l) {
+        char *c = (char *)caches[l];
+        if (!c) return ORC_BAD_ARG;
+        for (int64_t i = 0; i < num_pairs; ++i) {
+            const int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+            if (src < 0 || src >= L->num_blocks || dst < 0 || dst >= L->num_blocks) continue;
+            for (int pl = 0; pl < 2; ++pl) memmove(c + pl * plane + dst * bb, c + pl * plane + src * bb, (size_t)bb);
+        }
+    }
+    return ORC_OK;
+}
+
+int orc_swap_blocks(const orc_layer *L, const void *src_cache, int64_t src_blocks, void *dst_cache,
+                    int64_t dst_blocks, const int64_t *pairs, int64_t num_pairs)
+{
+    if (!layer_ok(L) || src_blocks < 0 || dst_blocks < 0 || num_pairs < 0) return ORC_BAD_ARG;
+    if (num_pairs > 0 && (!src_cache || !dst_cache || !pairs)) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+        if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return ORC_BAD_INDEX;
+    }
+    const int64_t bb = block_bytes(L);
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+        for (int pl = 0; pl < 2; ++pl)
+            memcpy((char *)dst_cache + (pl * dst_blocks + dst) * bb,
+                   (const char *)src_cache + (pl * src_blocks + src) * bb, (size_t)bb);
+    }
+    return ORC_OK;
+}
+
+/*
  * Cache write: for every token t whose slot s = slot_mapping[t] is >= 0, copy the bits of
  * key row t into the key plane at (s / block_size, s % block_size) and the bits of value
  * row t into the value plane at the same place.  key/value rows are num_kv_heads *

@@ -381,9 +381,63 @@ def pin_bf16_inputs():
                       seed=1300)
 
 
+def _numbered_cache(nb, elems, planes=2):
+    """[planes, nb, elems] fp32 cache whose every element is distinct: 1000 * plane + 10 * block + index."""
+    c = np.zeros((planes, nb, elems), dtype=np.float32)
+    for pl in range(planes):
+        for b in range(nb):
+            c[pl, b] = 1000 * pl + 10 * b + np.arange(elems) / 1000.0
+    return c
+
+
+def pin_copy_blocks_map():
+    """copy_blocks applies a source -> destinations map (the pages' Dict[int, List[int]],
+    flattened to pairs) to every layer's cache, both planes, and nothing else: expected
+    arrays built by slicing here, not by the oracle."""
+    bs, Hkv, D = 2, 2, 4
+    ol = oracle.OracleLayer(2, Hkv, D, bs, 5, oracle.DTYPE_F32, 1.0)
+    elems = bs * Hkv * D
+    layers = [_numbered_cache(5, elems) + 100 * l for l in range(3)]
+    src_to_dsts = {0: [3, 4], 2: [1]}
+    pairs = np.array([(s, d) for s, ds in src_to_dsts.items() for d in ds] + [(7, 0), (1, -1)])  # last two skipped
+    got = [c.copy() for c in layers]
+    oracle.copy_blocks(ol, got, pairs)
+    for l, c in enumerate(layers):
+        want = c.copy()
+        want[:, 3] = c[:, 0]
+        want[:, 4] = c[:, 0]
+        want[:, 1] = c[:, 2]
+        assert np.array_equal(got[l], want), f"layer {l}: copy_blocks moved the wrong bits"
+
+
+def pin_swap_blocks_map():
+    """swap_blocks moves block src of one cache to block dst of another with a different block
+    count (both planes); an index out of range moves nothing and fails."""
+    bs, Hkv, D = 2, 1, 4
+    ol = oracle.OracleLayer(1, Hkv, D, bs, 3, oracle.DTYPE_F32, 1.0)
+    elems = bs * Hkv * D
+    src = _numbered_cache(3, elems)
+    dst = _numbered_cache(6, elems) + 5000
+    want = dst.copy()
+    for s_, d_ in [(2, 0), (0, 5), (1, 2)]:
+        want[:, d_] = src[:, s_]
+    got = dst.copy()
+    oracle.swap_blocks(ol, src, got, np.array([(2, 0), (0, 5), (1, 2)]))
+    assert np.array_equal(got, want), "swap_blocks moved the wrong bits"
+    untouched = dst.copy()
+    try:
+        oracle.swap_blocks(ol, src, untouched, np.array([(0, 1), (3, 0)]))
+    except RuntimeError:
+        pass
+    else:
+        raise AssertionError("swap_blocks accepted a source block out of range")
+    assert np.array_equal(untouched, dst), "a rejected swap_blocks moved bits"
+
+
 PINS = [
     pin_slot_worked_example, pin_negative_slot_skipped, pin_start_loc_worked_example, pin_identity_block_table,
     pin_sdpa_causal_gqa, pin_sdpa_chunked_context, pin_sdpa_alibi, pin_sdpa_window, pin_window_one_closed_form,
     pin_single_key_closed_form, pin_zero_query_mean, pin_block_relabel_invariance, pin_gqa_equals_repeated_kv,
     pin_decode_is_last_prefill_row, pin_chunked_equals_full_rows, pin_padded_decode_row, pin_bf16_inputs,
+    pin_copy_blocks_map, pin_swap_blocks_map,
 ]

@@ -29,6 +29,9 @@ MUTANTS = [
     ("softmax_denominator", "out[d] /= denom;", "out[d] /= (denom + 1e-3);"),
     ("bf16_promotion", "<< 16;\n        float f;", "<< 15;\n        float f;"),
     ("value_plane", "const char *vc = kc + plane * elt_bytes(L->dtype);", "const char *vc = kc;"),
+    ("copy_direction", "memmove(c + pl * plane + dst * bb, c + pl * plane + src * bb", "memmove(c + pl * plane + src * bb, c + pl * plane + dst * bb"),
+    ("copy_key_plane_only", "for (int pl = 0; pl < 2; ++pl) memmove(", "for (int pl = 0; pl < 1; ++pl) memmove("),
+    ("swap_plane_stride", "(char *)dst_cache + (pl * dst_blocks + dst) * bb", "(char *)dst_cache + (pl * src_blocks + dst) * bb"),
 ]
 
 
