@@ -1,6 +1,6 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline] [--no-block-moves]
 
 One step is one pass of the whole hot path over one synthetic batch, all inputs resident in HBM:
 pa_cache_write of the step's new K/V rows, pa_prefill_varlen over the prefill rows and pa_decode
@@ -15,7 +15,10 @@ per-call times are kernel times; the K timed steps are bracketed by torch.cuda.s
 Prints ONE JSON line:
   value         decode KV-read throughput, GB/s = visible K+V bytes / decode time
   secondary     prefill attention TFLOP/s (4 * head_size flops per visible (row, key, head)),
-                cache-write GB/s (bytes read + written), each with its fraction of peak
+                cache-write GB/s (bytes read + written), each with its fraction of peak; and,
+                outside the timed steps, pa_copy_blocks GB/s (1024 scattered blocks of the
+                workload's geometry in a scratch cache, bytes read + written) and pa_swap_blocks
+                GB/s to and from pinned host memory (--no-block-moves skips them)
   roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s;
                 traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
                 (profiles/decode_traffic.json), null when the decode source changed since
@@ -165,6 +168,41 @@ def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20
     }
 
 
+def block_moves(pa, L, dev, num_pairs: int = 1024, reps: int = 10):
+    """Timing of pa.copy_blocks (one layer, num_pairs scattered pairs inside a scratch cache of
+    the workload's layer geometry) and pa.swap_blocks (num_pairs blocks device -> pinned host
+    and back, in runs).  Outside the timed step; the step's own cache is not touched."""
+    elems = L.block_size * L.row_elems
+    bb = elems * L.elt_bytes                                    # bytes per block and plane
+    nb = 4 * num_pairs
+    layer = pa.Layer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, nb, L.torch_dtype, L.scale, None, 0)
+    scratch = torch.zeros((2, nb, elems), dtype=L.torch_dtype, device=dev)
+    perm = np.random.default_rng(0).permutation(nb)
+    pairs = torch.as_tensor(np.stack([perm[:num_pairs], perm[num_pairs:2 * num_pairs]], 1), device=dev)
+    host = torch.zeros((2, num_pairs, elems), dtype=L.torch_dtype).pin_memory()
+    runs_out = np.stack([np.arange(num_pairs), np.arange(num_pairs)], 1)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, fn, nbytes in (
+            ("copy_blocks", lambda: pa.copy_blocks([scratch], pairs, layer), 2 * 2 * num_pairs * bb),
+            ("swap_blocks_d2h", lambda: pa.swap_blocks(scratch, host, runs_out, layer), 2 * num_pairs * bb),
+            ("swap_blocks_h2d", lambda: pa.swap_blocks(host, scratch, runs_out, layer), 2 * num_pairs * bb)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": ms, "blocks": num_pairs, "bytes_per_call": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+    out["copy_blocks"]["frac_hbm_peak"] = out["copy_blocks"]["GB_per_s"] / HBM_PEAK_GBPS
+    del scratch, host
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +210,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-moves", action="store_true", help="skip the copy_blocks / swap_blocks timing")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (counter calibration) and exit")
@@ -255,6 +294,8 @@ def main(argv=None):
     cw_ms, _ = avg_ms("cw")
     cw_gbps = cache_write_bytes(batch) / (cw_ms * 1e-3) / 1e9
     secondary = {"cache_write": {"ms": cw_ms, "GB_per_s": cw_gbps, "frac_hbm_peak": cw_gbps / HBM_PEAK_GBPS}}
+    if not args.no_block_moves:
+        secondary.update(block_moves(pa, L, dev))
     value = None
     unit = "GB/s"
     roofline = None

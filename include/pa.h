@@ -168,6 +168,40 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
                             int64_t num_tokens, int32_t max_subquery_len, int32_t max_context_len,
                             void *stream);
 
+/*
+ * Block copy inside the caches of several layers (copy-on-write of blocks shared between
+ * sequences): for every pair (src, dst) of block_pairs and every layer l, block src of both
+ * planes of cache l is copied to block dst; bits are copied unchanged.
+ * (aphrodite-engine "xformers.py", XFormersBackend.copy_blocks: a map from a source block to a
+ * list of destination blocks over the list of per-layer caches; here flattened to pairs.)
+ *   kv_caches    device array of num_layers device pointers, each a whole cache of this layer
+ *                geometry ([2, num_blocks, ...], 16-byte aligned -- a device-side precondition)
+ *   block_pairs  device int64 [num_pairs][2]: (src, dst).  A pair naming a block outside
+ *                [0, num_blocks) is skipped.  A destination must not also be a source in the
+ *                same call: the pairs are copied concurrently.
+ * One kernel launch; num_layers == 0 or num_pairs == 0 returns PA_OK and launches nothing.
+ */
+pa_status pa_copy_blocks(const pa_layer *layer, void *const *kv_caches, int32_t num_layers,
+                         const int64_t *block_pairs, int64_t num_pairs, void *stream);
+
+/*
+ * Block swap between two caches of one layer geometry, e.g. device and pinned host memory:
+ * for every pair (src, dst) of block_pairs, block src of both planes of src_cache is copied to
+ * block dst of dst_cache.  (aphrodite-engine "xformers.py", XFormersBackend.swap_blocks: a
+ * source -> destination block map between two caches.)
+ *   src_cache, dst_cache  whole caches [2, src_num_blocks, ...] and [2, dst_num_blocks, ...]
+ *                         in device or host memory (host memory should be pinned for the
+ *                         copies to be asynchronous); they must not overlap
+ *   block_pairs           HOST int64 [num_pairs][2]: (src, dst), checked on the host; any
+ *                         index out of range returns PA_ERR_INVALID_ARGUMENT and enqueues
+ *                         nothing
+ * Enqueued as hipMemcpyAsync copies on the stream, one per plane for every run of pairs
+ * (s, d), (s + 1, d + 1), ...  A failure of the HIP runtime part way returns PA_ERR_HIP; copies
+ * already enqueued stay enqueued.
+ */
+pa_status pa_swap_blocks(const pa_layer *layer, const void *src_cache, int64_t src_num_blocks, void *dst_cache,
+                         int64_t dst_num_blocks, const int64_t *block_pairs, int64_t num_pairs, void *stream);
+
 /* Static text for a status code. */
 const char *pa_status_string(pa_status status);
 

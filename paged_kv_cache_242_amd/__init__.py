@@ -28,7 +28,7 @@ PA_ERR_HIP = 4
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 
-EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen",
+EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
             "pa_status_string", "pa_last_error_message", "pa_version")
 
 
@@ -67,6 +67,10 @@ def _load_library(path: str = LIB_PATH):
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [LP, P, P, I64, P, P, I64, P, P, I32, P, P, I32, I64, I32, I32, P]
     lib.pa_prefill_varlen.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [LP, P, I32, P, I64, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [LP, P, I64, P, I64, P, I64, P]
+    lib.pa_swap_blocks.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error_message.argtypes = []
@@ -173,6 +177,42 @@ def cache_write(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor, 
     c = layer._c()
     _check(_lib.pa_cache_write(ctypes.byref(c), key.data_ptr(), value.data_ptr(), ks, T, sm,
                                _cache(kv_cache, layer), _stream(key.device)))
+
+
+def copy_blocks(kv_caches, block_pairs: torch.Tensor, layer: Layer) -> None:
+    """Copy block src -> dst (both planes) in every cache of ``kv_caches`` for each row
+    (src, dst) of ``block_pairs`` (int64 [n, 2] on the GPU); in place, one launch."""
+    caches = list(kv_caches)
+    if not caches:
+        return
+    ptrs = [_cache(c, layer) for c in caches]
+    pairs = _index(block_pairs, "block_pairs", torch.int64)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, f"block_pairs must be [n, 2], got {tuple(block_pairs.shape)}")
+    dev = caches[0].device
+    table = torch.tensor(ptrs, dtype=torch.int64, device=dev)     # device array of cache pointers
+    c = layer._c()
+    _check(_lib.pa_copy_blocks(ctypes.byref(c), table.data_ptr(), len(caches), pairs, block_pairs.shape[0],
+                               _stream(dev)))
+
+
+def swap_blocks(src_cache: torch.Tensor, dst_cache: torch.Tensor, block_pairs, layer: Layer) -> None:
+    """Copy block src of ``src_cache`` -> block dst of ``dst_cache`` (both planes) for each pair
+    (src, dst) of ``block_pairs`` (host int64 [n, 2]: a CPU tensor, array or list).  Either cache
+    may live in (pinned) host memory; the copies go on the current stream of the GPU side."""
+    elems = layer.block_size * layer.num_kv_heads * layer.head_size
+    for name, t in (("src_cache", src_cache), ("dst_cache", dst_cache)):
+        if t.dim() != 3 or t.shape[0] != 2 or t.shape[2] != elems or not t.is_contiguous() or t.dtype != layer.dtype:
+            raise PaError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous {layer.dtype} tensor [2, blocks, {elems}]")
+    pairs = torch.as_tensor(block_pairs, dtype=torch.int64).reshape(-1, 2).contiguous()
+    if pairs.is_cuda:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, "block_pairs must be on the host")
+    dev = src_cache.device if src_cache.is_cuda else dst_cache.device
+    if not dev.type == "cuda":
+        raise PaError(PA_ERR_INVALID_ARGUMENT, "one of the caches must be a GPU tensor")
+    c = layer._c()
+    _check(_lib.pa_swap_blocks(ctypes.byref(c), src_cache.data_ptr(), src_cache.shape[1], dst_cache.data_ptr(),
+                               dst_cache.shape[1], pairs.data_ptr(), pairs.shape[0], _stream(dev)))
 
 
 def decode_workspace_size(layer: Layer, num_seqs: int, max_seq_len: int) -> int:

@@ -113,6 +113,66 @@ pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *val
     return ok();
 }
 
+pa_status pa_copy_blocks(const pa_layer *layer, void *const *kv_caches, int32_t num_layers, const int64_t *block_pairs,
+                         int64_t num_pairs, void *stream) {
+    const char *fn = "pa_copy_blocks";
+    pa_status st = check_layer(layer, fn);
+    if (st != PA_OK) return st;
+    if (num_layers < 0 || num_pairs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (num_layers == 0 || num_pairs == 0) return ok();
+    if (!kv_caches || !block_pairs) return fail(PA_ERR_INVALID_ARGUMENT, "%s: kv_caches and block_pairs must be non-NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(kv_caches) & 7) != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: kv_caches must be 8-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(block_pairs) & 7) != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: block_pairs must be 8-byte aligned", fn);
+    pa::CopyBlocksParams p;
+    p.caches = kv_caches;
+    p.pairs = block_pairs;
+    p.num_pairs = num_pairs;
+    p.num_blocks = layer->num_blocks;
+    p.block_bytes = int64_t(layer->block_size) * layer->num_kv_heads * layer->head_size * elt_bytes(layer->dtype);
+    p.plane_bytes = p.num_blocks * p.block_bytes;
+    hipError_t e = pa::launch_copy_blocks(p, num_layers, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+pa_status pa_swap_blocks(const pa_layer *layer, const void *src_cache, int64_t src_num_blocks, void *dst_cache,
+                         int64_t dst_num_blocks, const int64_t *block_pairs, int64_t num_pairs, void *stream) {
+    const char *fn = "pa_swap_blocks";
+    pa_status st = check_layer(layer, fn);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_pairs must be >= 0 and the block counts > 0", fn);
+    if (num_pairs == 0) return ok();
+    if (!src_cache || !dst_cache || !block_pairs)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: src_cache, dst_cache and block_pairs must be non-NULL", fn);
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t s = block_pairs[2 * i], d = block_pairs[2 * i + 1];
+        if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks)
+            return fail(PA_ERR_INVALID_ARGUMENT, "%s: pair %lld (%lld -> %lld) out of range (%lld / %lld blocks)", fn,
+                        (long long)i, (long long)s, (long long)d, (long long)src_num_blocks,
+                        (long long)dst_num_blocks);
+    }
+    const int64_t bb = int64_t(layer->block_size) * layer->num_kv_heads * layer->head_size * elt_bytes(layer->dtype);
+    const char *src = static_cast<const char *>(src_cache);
+    char *dst = static_cast<char *>(dst_cache);
+    hipStream_t s_ = static_cast<hipStream_t>(stream);
+    // runs of pairs (s, d), (s + 1, d + 1), ... go out as one copy per plane
+    for (int64_t i = 0; i < num_pairs;) {
+        const int64_t s0 = block_pairs[2 * i], d0 = block_pairs[2 * i + 1];
+        int64_t n = 1;
+        while (i + n < num_pairs && block_pairs[2 * (i + n)] == s0 + n && block_pairs[2 * (i + n) + 1] == d0 + n) ++n;
+        for (int pl = 0; pl < 2; ++pl) {
+            hipError_t e = hipMemcpyAsync(dst + (pl * dst_num_blocks + d0) * bb, src + (pl * src_num_blocks + s0) * bb,
+                                          size_t(n * bb), hipMemcpyDefault, s_);
+            if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipMemcpyAsync failed: %s", fn, hipGetErrorString(e));
+        }
+        i += n;
+    }
+    return ok();
+}
+
 size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len) {
     if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0) return 0;
     return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, layer->dtype,

@@ -20,6 +20,16 @@ struct CacheWriteParams {
 };
 hipError_t launch_cache_write(const CacheWriteParams &p, hipStream_t stream);
 
+struct CopyBlocksParams {
+    void *const *caches;      // device array of per-layer cache bases
+    const int64_t *pairs;     // device [num_pairs][2]: (src, dst)
+    int64_t num_pairs;
+    int64_t num_blocks;       // blocks per plane
+    int64_t block_bytes;      // block_size * num_kv_heads * head_size * elt, multiple of 16
+    int64_t plane_bytes;      // num_blocks * block_bytes
+};
+hipError_t launch_copy_blocks(const CopyBlocksParams &p, int32_t num_layers, hipStream_t stream);
+
 // Decode policy shared by pa_decode and pa_decode_workspace_size.
 struct DecodePlan {
     int32_t head_groups;      // query heads of one KV head are processed in this many groups

@@ -23,8 +23,8 @@ def pa():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["pa_cache_write", "pa_decode", "pa_decode_workspace_size",
-                                           "pa_prefill_varlen", "pa_status_string", "pa_last_error_message",
-                                           "pa_version"])
+                                           "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
+                                           "pa_status_string", "pa_last_error_message", "pa_version"])
 
 
 def test_library_exports_every_declared_symbol(pa):
@@ -115,3 +115,25 @@ def test_python_binding_rejects_cpu_tensors(pa):
     with pytest.raises(pa.PaError):
         pa.cache_write(k, k, torch.zeros(2, 4, 16 * 256, dtype=torch.bfloat16), torch.zeros(3, dtype=torch.int64),
                        layer)
+
+
+def test_block_moves_host_validation(pa):
+    """copy/swap: counts, NULLs and (for swap, whose map is on the host) indices are checked
+    before anything is enqueued."""
+    import numpy as np
+    lib = pa.library()
+    c = _layer(pa)
+    assert lib.pa_copy_blocks(ctypes.byref(c), None, 0, None, 5, None) == 0          # no layers: no-op
+    assert lib.pa_copy_blocks(ctypes.byref(c), None, 2, None, 0, None) == 0          # no pairs: no-op
+    assert lib.pa_copy_blocks(ctypes.byref(c), None, 2, 64, 3, None) == 1
+    assert lib.pa_copy_blocks(ctypes.byref(c), 64, -1, 64, 3, None) == 1
+    assert lib.pa_copy_blocks(ctypes.byref(c), 64, 2, 68, 3, None) == 1               # misaligned pairs
+    pairs = np.array([[0, 1], [3, 2]], dtype=np.int64)
+    assert lib.pa_swap_blocks(ctypes.byref(c), None, 4, None, 8, pairs.ctypes.data, 0, None) == 0
+    bad = np.array([[0, 1], [4, 2]], dtype=np.int64)                                   # src 4 of 4 blocks
+    assert lib.pa_swap_blocks(ctypes.byref(c), 256, 4, 256, 8, bad.ctypes.data, 2, None) == 1
+    assert "out of range" in lib.pa_last_error_message().decode()
+    bad = np.array([[0, 8]], dtype=np.int64)                                           # dst 8 of 8 blocks
+    assert lib.pa_swap_blocks(ctypes.byref(c), 256, 4, 256, 8, bad.ctypes.data, 1, None) == 1
+    assert lib.pa_swap_blocks(ctypes.byref(c), None, 4, 256, 8, pairs.ctypes.data, 2, None) == 1
+    assert lib.pa_swap_blocks(ctypes.byref(c), 256, 0, 256, 8, pairs.ctypes.data, 2, None) == 1

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import gpu_harness as gh
+import oracle
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -73,6 +74,74 @@ def test_cache_write_strided_rows_and_padding():
     torch.cuda.synchronize()
     pool = gh.oracle_pool(batch)
     assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8))
+
+
+# ------------------------------------------------------------------------------ block copy / swap
+
+def _random_cache(layer, nb, rng, dev):
+    """[2, nb, block elements] cache of random bit patterns (NaNs and infinities included)."""
+    elems = layer.block_size * layer.num_kv_heads * layer.head_size
+    if layer.dtype == wl.BF16:
+        bits = rng.integers(0, 1 << 16, size=(2, nb, elems), dtype=np.uint16)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bits = rng.integers(0, 1 << 32, size=(2, nb, elems), dtype=np.uint32)
+    return torch.from_numpy(bits.view(np.float32)).to(dev)
+
+
+def _bits(t):
+    return wl.host_bits(t).view(np.uint16 if t.dtype == torch.bfloat16 else np.uint32)
+
+
+@pytest.mark.parametrize("H,Hkv,D,bs,dtype", [(8, 2, 128, 16, wl.BF16), (4, 4, 64, 8, wl.F32), (16, 8, 128, 256, wl.BF16)])
+def test_copy_blocks_bit_exact(H, Hkv, D, bs, dtype):
+    layer = _layer(H, Hkv, D, bs, dtype)
+    nb = 64
+    layer = dataclasses.replace(layer, num_blocks=nb)
+    _say(f"copy_blocks {layer}")
+    rng = np.random.default_rng(90 + bs)
+    dev = gh.device()
+    caches = [_random_cache(layer, nb, rng, dev) for _ in range(3)]
+    perm = rng.permutation(nb)
+    srcs, dsts = perm[:16], perm[16:40]                   # no destination is also a source
+    pairs = [(int(srcs[i % 16]), int(d)) for i, d in enumerate(dsts)] + [(nb, 0), (0, -1)]   # last two skipped
+    before = [wl.host_bits(c) for c in caches]          # the oracle's element types (uint16 bits or float32)
+    gh.pa().copy_blocks(caches, gh.i64(np.array(pairs)), gh.player(layer))
+    torch.cuda.synchronize()
+    ol = gh.olayer(layer)
+    ref = [b.copy() for b in before]
+    oracle.copy_blocks(ol, ref, np.array(pairs))
+    for l in range(3):
+        assert np.array_equal(_bits(caches[l]), ref[l].view(_bits(caches[l]).dtype)), f"layer {l}: copy_blocks bits differ"
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_swap_blocks_device_host_device(dtype):
+    layer = dataclasses.replace(_layer(8, 2, 64, 16, dtype), num_blocks=32)
+    _say(f"swap_blocks {layer}")
+    rng = np.random.default_rng(95)
+    dev = gh.device()
+    pl = gh.player(layer)
+    gpu = _random_cache(layer, 32, rng, dev)
+    host = _random_cache(layer, 48, rng, torch.device("cpu")).pin_memory()
+    gpu2 = _random_cache(layer, 32, rng, dev)
+    out_pairs = [(3, 10), (4, 11), (5, 12), (0, 47), (31, 0), (7, 30)]        # a run of three, then singles
+    in_pairs = [(10, 1), (11, 2), (47, 30), (0, 29)]
+    g0, h0, g20 = wl.host_bits(gpu), wl.host_bits(host), wl.host_bits(gpu2)
+    gh.pa().swap_blocks(gpu, host, out_pairs, pl)                             # device -> pinned host
+    gh.pa().swap_blocks(host, gpu2, in_pairs, pl)                             # pinned host -> device
+    gh.pa().swap_blocks(gpu, gpu2, [(1, 5), (2, 6)], pl)                       # device -> device
+    torch.cuda.synchronize()
+    ol = gh.olayer(layer)
+    h_ref, g2_ref = h0.copy(), g20.copy()
+    oracle.swap_blocks(ol, g0, h_ref, np.array(out_pairs))
+    oracle.swap_blocks(ol, h_ref, g2_ref, np.array(in_pairs))
+    oracle.swap_blocks(ol, g0, g2_ref, np.array([(1, 5), (2, 6)]))
+    u = np.uint16 if dtype == wl.BF16 else np.uint32
+    assert np.array_equal(_bits(host), h_ref.view(u)), "device -> host swap bits differ"
+    assert np.array_equal(_bits(gpu2), g2_ref.view(u)), "host -> device / device -> device swap bits differ"
+    assert np.array_equal(_bits(gpu), g0.view(u)), "the source cache changed"
+    with pytest.raises(gh.pa().PaError):
+        gh.pa().swap_blocks(gpu, host, [(32, 0)], pl)
 
 
 # ------------------------------------------------------------------------------ decode grid
