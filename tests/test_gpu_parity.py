@@ -1,6 +1,7 @@
 """GPU parity: libpa (through the C ABI) against the fp64 oracle on the same seeded inputs.
 
-Cache write: bit-exact over the whole pool (unused slots keep their NaN fill).  Attention:
+Cache write, block copy and block swap: bit-exact over the whole pool (unused slots keep their NaN
+fill).  Attention:
 bf16 max-abs <= 2e-2 and mean-abs <= 2e-3, fp32 max-abs <= 1e-4.  Small grids are compared
 element by element; the five full-size workloads run in the same launch configuration the
 benchmark times and are compared on sampled sequences / rows (the oracle computes those one by
@@ -258,6 +259,17 @@ def test_mixed_batch_small():
     batch = wl.make_batch(layer, seed=71, prefill=[(100, 150), (0, 90), (333, 1)], decode=[1, 250, 700, 0],
                           device=gh.device())
     _check_full(batch, "mixed small")
+
+
+@pytest.mark.parametrize("k,layer", [(4, _layer(32, 8, 128, 16)), (2, _layer(8, 8, 64, 32, alibi=True, window=500))])
+def test_multi_token_decode_as_chunked_prefill(k, layer):
+    """Speculative ("uniform batch") decode: every sequence brings k query tokens at the end of
+    its cached context, causal among themselves -- chunked prefill with context L - k and a
+    k-token subquery."""
+    rng = np.random.default_rng(72 + k)
+    lens = rng.integers(k + 1, 3000, size=24)
+    batch = wl.make_batch(layer, seed=73 + k, prefill=[(int(L) - k, k) for L in lens], device=gh.device())
+    _check_full(batch, f"multi-token decode k={k}")
 
 
 # ------------------------------------------------------------------------------ full-size workloads
