@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this module; the product package never does.  It shares no
 code with the GPU library.  Every function takes host numpy arrays holding the exact bytes
-the GPU side uses (bf16 tensors as ``uint16`` bit patterns, fp32 as ``float32``) and
+the GPU side uses (bf16 and fp16 tensors as ``uint16`` bit patterns, fp32 as ``float32``) and
 returns fp64 results.
 
 Citations for what each function computes live in the header comment of ``pa_oracle.c``
@@ -25,6 +25,7 @@ _LIB = os.path.join(_HERE, "libpa_oracle.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 
 
 def build(force: bool = True) -> str:
@@ -49,6 +50,8 @@ class _Layer(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("alibi_slopes", ctypes.c_void_p),
         ("sliding_window", ctypes.c_int32),
+        ("logits_soft_cap", ctypes.c_float),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -88,21 +91,27 @@ class OracleLayer:
     head_size: int
     block_size: int
     num_blocks: int
-    dtype: int                       # DTYPE_F32 or DTYPE_BF16
+    dtype: int                       # DTYPE_F32, DTYPE_BF16 or DTYPE_F16
     scale: float
     alibi_slopes: Optional[np.ndarray] = None   # float32 [num_heads]
     sliding_window: int = 0
+    logits_soft_cap: float = 0.0               # <= 0: off
+    sinks: Optional[np.ndarray] = None          # float32 [num_heads] sink logits
 
     def _c(self):
-        slopes = None
-        if self.alibi_slopes is not None:
-            slopes = np.ascontiguousarray(self.alibi_slopes, dtype=np.float32)
-            assert slopes.shape == (self.num_heads,)
+        def f32_heads(a):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a, dtype=np.float32)
+            assert a.shape == (self.num_heads,)
+            return a
+        slopes, sinks = f32_heads(self.alibi_slopes), f32_heads(self.sinks)
         c = _Layer(self.num_heads, self.num_kv_heads, self.head_size, self.block_size,
                    self.num_blocks, self.dtype, float(np.float32(self.scale)),
                    slopes.ctypes.data if slopes is not None else None,
-                   int(self.sliding_window))
-        return c, slopes   # keep slopes alive while c is used
+                   int(self.sliding_window), float(np.float32(self.logits_soft_cap)),
+                   sinks.ctypes.data if sinks is not None else None)
+        return c, (slopes, sinks)   # keep the arrays alive while c is used
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -232,3 +241,21 @@ def prefill(layer: OracleLayer, query: np.ndarray, key: np.ndarray, value: np.nd
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact value of bf16 bit patterns (uint16) as float64."""
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of IEEE binary16 bit patterns (uint16) as float64."""
+    b = bits.astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 31
+    f = (b & 1023).astype(np.float64)
+    v = np.where(e == 0, np.ldexp(f, -24), np.ldexp(1024.0 + f, (e - 25).astype(np.int32)))
+    v = np.where(e == 31, np.where(f != 0, np.nan, np.inf), v)
+    return sign * v
+
+
+def bits_to_f64(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact value of stored elements of the given oracle dtype as float64."""
+    if dtype == DTYPE_F32:
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
+    return f16_bits_to_f64(bits) if dtype == DTYPE_F16 else bf16_bits_to_f64(bits)

@@ -42,8 +42,19 @@
  *  - Softmax attention in fp64: m = max s_j, p_j = exp(s_j - m), out = sum p_j v_j /
  *    sum p_j (vLLM "cpu_attn", _run_sdpa_forward, scaled_dot_product_attention).
  *
+ *  - Logits soft-cap and attention sinks.  The pages only name them: a logits_soft_cap
+ *    argument of the backend constructor (vLLM "cpu_attn", TorchSDPABackendImpl.__init__,
+ *    which warns that SDPA ignores it) and per-layer logits_soft_cap / has_sinks parameters
+ *    (vLLM "utils" page, PerLayerParameters).  Readings taken here:
+ *      soft-cap c > 0: the scaled dot product x = scale * <q, k_j> becomes c * tanh(x / c)
+ *      before the ALiBi bias and the mask; c <= 0 leaves it alone;
+ *      sink sigma_h: one extra logit per query head that joins the softmax normalisation
+ *      but carries no value, so out = sum_j e^(s_j) v_j / (e^(sigma_h) + sum_j e^(s_j)).
+ *
  * Inputs are promoted exactly to double: fp32 directly, bf16 by placing its 16 bits in
- * the high half of an fp32.  Outputs are double.  Element types: 0 = fp32, 1 = bf16.
+ * the high half of an fp32, fp16 from its sign, exponent and fraction fields.  Outputs are
+ * double.  Element types: 0 = fp32, 1 = bf16, 2 = fp16 (the pages list all three as
+ * supported dtypes: vLLM "cpu_attn", TorchSDPABackend.get_supported_dtypes).
  */
 #include <math.h>
 #include <stdint.h>
@@ -64,19 +75,34 @@ typedef struct {
     int32_t head_size;      /* D */
     int32_t block_size;     /* tokens per cache block */
     int64_t num_blocks;     /* physical blocks in each plane */
-    int32_t dtype;          /* 0 = fp32, 1 = bf16 */
+    int32_t dtype;          /* 0 = fp32, 1 = bf16, 2 = fp16 */
     float scale;            /* multiplies <q, k> */
     const float *alibi_slopes; /* [H] or NULL */
     int32_t sliding_window; /* <= 0: no window */
+    float logits_soft_cap;  /* <= 0: no soft-cap */
+    const float *sinks;     /* [H] sink logits, or NULL */
 } orc_layer;
 
 static int elt_bytes(int32_t dtype) { return dtype == 0 ? 4 : 2; }
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double half_to_double(uint16_t h)
+{
+    const int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 31) v = f ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)f, -24);            /* subnormal: f * 2^-24 */
+    else v = ldexp((double)(1024 + f), e - 25);            /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
 
 /* Exact promotion of one stored element to double. */
 static double elt_to_double(const void *base, int64_t idx, int32_t dtype)
 {
     if (dtype == 0) {
         return (double)((const float *)base)[idx];
+    } else if (dtype == 2) {
+        return half_to_double(((const uint16_t *)base)[idx]);
     } else {
         uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
         float f;
@@ -96,7 +122,7 @@ static int layer_ok(const orc_layer *L)
     if (!L || L->num_heads <= 0 || L->num_kv_heads <= 0 || L->head_size <= 0 || L->block_size <= 0)
         return 0;
     if (L->num_heads % L->num_kv_heads != 0) return 0;
-    if (L->dtype != 0 && L->dtype != 1) return 0;
+    if (L->dtype < 0 || L->dtype > 2) return 0;
     if (L->num_blocks < 0) return 0;
     return 1;
 }
@@ -219,8 +245,11 @@ static int unpage(const orc_layer *L, const void *kv_cache, const int32_t *table
  * D doubles to out.
  */
 static void attend_row(const orc_layer *L, const double *q, const double *K, const double *V,
-                       int64_t pos, double slope, int has_alibi, double *out)
+                       int64_t pos, int64_t h, double *out)
 {
+    const int has_alibi = L->alibi_slopes != NULL;
+    const double slope = has_alibi ? (double)L->alibi_slopes[h] : 0.0;
+    const double cap = (double)L->logits_soft_cap;
     const int64_t D = L->head_size;
     const int64_t W = L->sliding_window;
     const int64_t first = (W > 0 && pos - W + 1 > 0) ? pos - W + 1 : 0;
@@ -232,12 +261,18 @@ static void attend_row(const orc_layer *L, const double *q, const double *K, con
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += q[d] * K[j * D + d];
         double sj = (double)L->scale * dot;
+        if (cap > 0.0) sj = cap * tanh(sj / cap);
         if (has_alibi) sj += slope * (double)(j - pos);
         s[j - first] = sj;
         if (sj > m) m = sj;
     }
-    /* softmax-weighted sum of values */
-    double denom = 0.0;
+    /* softmax-weighted sum of values; a sink logit only adds to the denominator */
+    double sink = -INFINITY;
+    if (L->sinks) {
+        sink = (double)L->sinks[h];
+        if (sink > m) m = sink;
+    }
+    double denom = L->sinks ? exp(sink - m) : 0.0;
     for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
     for (int64_t j = first; j <= pos; ++j) {
         double p = exp(s[j - first] - m);
@@ -304,8 +339,7 @@ int orc_decode(const orc_layer *L, double *out, const void *query, int64_t q_str
         } else {
             for (int64_t h = g * G; h < (g + 1) * G; ++h) {
                 for (int64_t d = 0; d < D; ++d) q[d] = elt_to_double(query, i * q_stride + h * D + d, L->dtype);
-                double slope = L->alibi_slopes ? (double)L->alibi_slopes[h] : 0.0;
-                attend_row(L, q, K, V, n - 1, slope, L->alibi_slopes != NULL, out + (i * H + h) * D);
+                attend_row(L, q, K, V, n - 1, h, out + (i * H + h) * D);
             }
         }
         free(K); free(V); free(q);
@@ -380,9 +414,7 @@ int orc_prefill(const orc_layer *L, double *out, const void *query, int64_t q_st
                 for (int64_t h = g * G; h < (g + 1) * G; ++h) {
                     for (int64_t d = 0; d < D; ++d)
                         q[d] = elt_to_double(query, (start + t) * q_stride + h * D + d, L->dtype);
-                    double slope = L->alibi_slopes ? (double)L->alibi_slopes[h] : 0.0;
-                    attend_row(L, q, K, V, c + t, slope, L->alibi_slopes != NULL,
-                               out + ((start + t) * H + h) * D);
+                    attend_row(L, q, K, V, c + t, h, out + ((start + t) * H + h) * D);
                 }
             }
         }

@@ -29,17 +29,21 @@ NAN_BF16 = np.uint16(0x7FC0)
 
 # ------------------------------------------------------------------------------ helpers
 
+ORACLE_DTYPE = {wl.F32: oracle.DTYPE_F32, wl.BF16: oracle.DTYPE_BF16, wl.F16: oracle.DTYPE_F16}
+NAN_F16 = np.uint16(0x7E00)
+
+
 def oracle_layer(layer: wl.LayerSpec) -> oracle.OracleLayer:
     return oracle.OracleLayer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size,
-                              layer.num_blocks, oracle.DTYPE_F32 if layer.dtype == wl.F32 else oracle.DTYPE_BF16,
-                              layer.scale, layer.alibi_slopes, layer.sliding_window)
+                              layer.num_blocks, ORACLE_DTYPE[layer.dtype], layer.scale, layer.alibi_slopes,
+                              layer.sliding_window, layer.logits_soft_cap, layer.sinks)
 
 
 def nan_pool(layer: wl.LayerSpec) -> np.ndarray:
     shape = (2, layer.num_blocks, layer.block_size * layer.num_kv_heads * layer.head_size)
     if layer.dtype == wl.F32:
         return np.full(shape, np.nan, dtype=np.float32)
-    return np.full(shape, NAN_BF16, dtype=np.uint16)
+    return np.full(shape, NAN_F16 if layer.dtype == wl.F16 else NAN_BF16, dtype=np.uint16)
 
 
 def oracle_cache(batch: wl.PagedBatch) -> np.ndarray:
@@ -381,6 +385,117 @@ def pin_bf16_inputs():
                       seed=1300)
 
 
+def _direct_decode(layer: wl.LayerSpec, K: np.ndarray, V: np.ndarray, Q: np.ndarray, **extra) -> np.ndarray:
+    """Oracle decode of one query row over the n rows of K/V ([n, Hkv*D] float32) stored
+    through the identity block table; ``extra`` overrides OracleLayer fields."""
+    n = K.shape[0]
+    bs = layer.block_size
+    nb = -(-n // bs)
+    ol = dataclasses.replace(oracle_layer(dataclasses.replace(layer, num_blocks=nb)), **extra)
+    pool = np.zeros((2, nb, bs * K.shape[1]), dtype=np.float32)
+    oracle.cache_write(ol, np.ascontiguousarray(K, dtype=np.float32), np.ascontiguousarray(V, dtype=np.float32),
+                       np.arange(n), pool)
+    return oracle.decode(ol, np.ascontiguousarray(Q, dtype=np.float32), pool, np.arange(nb)[None], np.array([n]))[0]
+
+
+def pin_soft_cap_saturation_and_order():
+    """Soft-cap c: scores far above c all saturate at c (tanh = 1 exactly in fp64), so two
+    keys with scores 1000 and 2000 get equal weight and out is the mean of their values;
+    an ALiBi bias added after the cap then splits them by exp(slope * (j - pos)) alone."""
+    layer = _layer(1, 1, 4, 4, scale=1.0)
+    K = np.array([[1, 0, 0, 0], [2, 0, 0, 0]], dtype=np.float32)
+    V = np.array([[1, 2, 3, 4], [-3, 0, 5, 1]], dtype=np.float32)
+    Q = np.array([[1000, 0, 0, 0]], dtype=np.float32)
+    no_cap = _direct_decode(layer, K, V, Q)
+    _close(no_cap[0], V[1], 1e-12, "uncapped: the larger score wins")
+    capped = _direct_decode(layer, K, V, Q, logits_soft_cap=2.0)
+    _close(capped[0], V.mean(axis=0), 1e-15, "saturated soft-cap: equal weights")
+    slope = 0.75
+    both = _direct_decode(layer, K, V, Q, logits_soft_cap=2.0, alibi_slopes=np.array([slope], dtype=np.float32))
+    w = np.array([np.exp(-slope), 1.0])
+    _close(both[0], (w[:, None] * V).sum(axis=0) / w.sum(), 1e-14, "ALiBi after a saturated soft-cap")
+
+
+def pin_soft_cap_known_value():
+    """A score x = c * atanh(1/2) caps to c / 2 (up to the fp32 rounding of x) and a zero
+    score stays 0, so out = (e^(c/2) v_0 + v_1) / (e^(c/2) + 1); a very large cap leaves
+    the scores unchanged."""
+    c = 4.0
+    x = float(np.float32(c * np.arctanh(0.5)))
+    layer = _layer(1, 1, 4, 4, scale=1.0)
+    K = np.array([[1, 0, 0, 0], [0, 1, 0, 0]], dtype=np.float32)
+    V = np.array([[2, -1, 0, 4], [1, 1, -2, 0]], dtype=np.float32)
+    Q = np.array([[x, 0, 0, 0]], dtype=np.float32)
+    got = _direct_decode(layer, K, V, Q, logits_soft_cap=c)
+    e = np.exp(c / 2)
+    _close(got[0], (e * V[0] + V[1]) / (e + 1), 1e-6, "soft-cap of c atanh(1/2)")
+    big = _direct_decode(layer, K, V, Q, logits_soft_cap=1e30)
+    _close(big, _direct_decode(layer, K, V, Q), 1e-15, "huge cap = no cap")
+
+
+def pin_sinks_closed_forms():
+    """Sinks: with q = 0 every visible key scores 0, so out = sum of visible v / (n + e^sigma)
+    for the head's own sigma; a single key gives v_0 / (1 + e^sigma); sigma = -inf is no
+    sink at all; decode stays the last row of prefill."""
+    H, Hkv, D = 4, 2, 8
+    sig = np.array([0.5, -1.0, 3.0, 2.0], dtype=np.float32)
+    for W in (0, 3):
+        layer = dataclasses.replace(_layer(H, Hkv, D, 4, window=W), sinks=sig)
+        batch = wl.make_batch(layer, seed=1400 + W, prefill=[(5, 4)], decode=[9, 1])
+        batch.query.zero_()
+        pre, dec = run_oracle(batch)
+        for kind, i, cpos, K, V, Q, rows in seq_rows(batch):
+            Vn = V.numpy()
+            for t in range(Q.shape[0]):
+                pos = cpos + t
+                lo = max(0, pos - W + 1) if W > 0 else 0
+                got = pre[rows][t] if kind == "prefill" else dec[i]
+                for h in range(H):
+                    ref = Vn[lo:pos + 1, h // (H // Hkv)].sum(axis=0) / (pos + 1 - lo + np.exp(np.float64(sig[h])))
+                    _close(got[h], ref, 1e-14, f"sink closed form ({kind}, W={W}, head {h})")
+    layer = dataclasses.replace(_layer(H, Hkv, D, 4, alibi=True, window=5),
+                                sinks=np.full(H, -np.inf, dtype=np.float32))
+    batch = wl.make_batch(layer, seed=1410, prefill=[(3, 5)], decode=[7, 2])
+    p1, d1 = run_oracle(batch)
+    p2, d2 = run_oracle(dataclasses.replace(batch, layer=dataclasses.replace(batch.layer, sinks=None)))
+    _close(p1, p2, 0.0, "sink -inf vs no sink (prefill)")
+    _close(d1, d2, 0.0, "sink -inf vs no sink (decode)")
+    layer = dataclasses.replace(_layer(H, Hkv, D, 4, alibi=True), sinks=sig, logits_soft_cap=wl.fp32(1.5))
+    for L in (1, 6):
+        b = wl.make_batch(layer, seed=1420 + L, decode=[L])
+        pool = oracle_cache(b)
+        ol = oracle_layer(b.layer)
+        dec = oracle.decode(ol, wl.host_bits(b.query), pool, b.decode_block_tables, b.decode_seq_lens)
+        pre = oracle.prefill(ol, wl.host_bits(b.query), wl.host_bits(b.key), wl.host_bits(b.value),
+                             pool, b.decode_block_tables, np.array([L - 1]), np.array([0, 1]))
+        _close(dec, pre, 0.0, f"decode vs last prefill row with sinks and soft-cap (L={L})")
+
+
+def pin_f16_promotion():
+    """fp16 elements are read exactly: every one of the 65536 bit patterns, passed through a
+    one-key decode (q = 0, K = 0, so out = v_0), equals numpy's float16 value, NaN and
+    infinities included; the Python helper agrees with numpy too."""
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    lib_vals = codes.view(np.float16).astype(np.float64)
+    helper = oracle.f16_bits_to_f64(codes)
+    assert np.array_equal(np.isnan(helper), np.isnan(lib_vals))
+    fin = ~np.isnan(lib_vals)
+    assert np.array_equal(helper[fin], lib_vals[fin]), "f16_bits_to_f64 disagrees with numpy"
+    D = 65536
+    ol = oracle.OracleLayer(1, 1, D, 1, 1, oracle.DTYPE_F16, 1.0)
+    pool = np.zeros((2, 1, D), dtype=np.uint16)
+    oracle.cache_write(ol, np.zeros((1, D), dtype=np.uint16), codes[None], np.array([0]), pool)
+    out = oracle.decode(ol, np.zeros((1, D), dtype=np.uint16), pool, np.array([[0]]), np.array([1]))[0, 0]
+    assert np.array_equal(np.isnan(out), np.isnan(lib_vals))
+    assert np.array_equal(out[fin], lib_vals[fin]), "oracle fp16 promotion disagrees with numpy"
+
+
+def pin_f16_inputs():
+    """fp16 layers: the oracle on fp16 bit patterns equals SDPA on the same values in fp64."""
+    _sdpa_batch_check(_layer(4, 2, 16, 4, dtype=wl.F16, alibi=True, window=6), prefill=[(4, 6)], decode=[3, 9],
+                      seed=1500)
+
+
 def _numbered_cache(nb, elems, planes=2):
     """[planes, nb, elems] fp32 cache whose every element is distinct: 1000 * plane + 10 * block + index."""
     c = np.zeros((planes, nb, elems), dtype=np.float32)
@@ -439,5 +554,6 @@ PINS = [
     pin_sdpa_causal_gqa, pin_sdpa_chunked_context, pin_sdpa_alibi, pin_sdpa_window, pin_window_one_closed_form,
     pin_single_key_closed_form, pin_zero_query_mean, pin_block_relabel_invariance, pin_gqa_equals_repeated_kv,
     pin_decode_is_last_prefill_row, pin_chunked_equals_full_rows, pin_padded_decode_row, pin_bf16_inputs,
-    pin_copy_blocks_map, pin_swap_blocks_map,
+    pin_copy_blocks_map, pin_swap_blocks_map, pin_soft_cap_saturation_and_order, pin_soft_cap_known_value,
+    pin_sinks_closed_forms, pin_f16_promotion, pin_f16_inputs,
 ]

@@ -24,13 +24,21 @@ MUTANTS = [
     ("kv_head_in_unpage", "cache_index(L, block, offset, g, d);\n            K[", "cache_index(L, block, offset, 0, d);\n            K["),
     ("gqa_map_decode", "for (int64_t h = g * G; h < (g + 1) * G; ++h) {\n                for (int64_t d = 0; d < D; ++d) q[d] = elt_to_double(query, i * q_stride + h * D + d",
      "for (int64_t h = g * G; h < (g + 1) * G; ++h) {\n                for (int64_t d = 0; d < D; ++d) q[d] = elt_to_double(query, i * q_stride + ((h % Hkv) * G + h / Hkv) * D + d"),
-    ("prefill_local_position", "attend_row(L, q, K, V, c + t, slope", "attend_row(L, q, K, V, t + (c > 0 ? c - 1 : 0), slope"),
-    ("decode_position", "attend_row(L, q, K, V, n - 1, slope", "attend_row(L, q, K, V, n > 1 ? n - 2 : 0, slope"),
+    ("prefill_local_position", "attend_row(L, q, K, V, c + t, h", "attend_row(L, q, K, V, t + (c > 0 ? c - 1 : 0), h"),
+    ("decode_position", "attend_row(L, q, K, V, n - 1, h", "attend_row(L, q, K, V, n > 1 ? n - 2 : 0, h"),
     ("softmax_denominator", "out[d] /= denom;", "out[d] /= (denom + 1e-3);"),
     ("bf16_promotion", "<< 16;\n        float f;", "<< 15;\n        float f;"),
     ("value_plane", "const char *vc = kc + plane * elt_bytes(L->dtype);", "const char *vc = kc;"),
     ("copy_direction", "memmove(c + pl * plane + dst * bb, c + pl * plane + src * bb", "memmove(c + pl * plane + src * bb, c + pl * plane + dst * bb"),
     ("copy_key_plane_only", "for (int pl = 0; pl < 2; ++pl) memmove(", "for (int pl = 0; pl < 1; ++pl) memmove("),
+    ("softcap_divisor", "sj = cap * tanh(sj / cap);", "sj = cap * tanh(sj);"),
+    ("softcap_after_alibi", "if (cap > 0.0) sj = cap * tanh(sj / cap);\n        if (has_alibi) sj += slope * (double)(j - pos);",
+     "if (has_alibi) sj += slope * (double)(j - pos);\n        if (cap > 0.0) sj = cap * tanh(sj / cap);"),
+    ("softcap_dropped", "if (cap > 0.0) sj = cap", "if (0) sj = cap"),
+    ("sink_in_max_only", "double denom = L->sinks ? exp(sink - m) : 0.0;", "double denom = 0.0;"),
+    ("sink_wrong_head", "sink = (double)L->sinks[h];", "sink = (double)L->sinks[0];"),
+    ("f16_exponent_bias", "e - 25);            /* (1 + f/1024)", "e - 24);            /* (1 + f/1024)"),
+    ("f16_subnormal", "ldexp((double)f, -24);", "ldexp((double)f, -25);"),
     ("swap_plane_stride", "(char *)dst_cache + (pl * dst_blocks + dst) * bb", "(char *)dst_cache + (pl * src_blocks + dst) * bb"),
 ]
 

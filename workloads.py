@@ -15,7 +15,7 @@ The recipe (also stated in the design notes):
   * integer structure (lengths, permutation of physical blocks) from
     ``numpy.random.default_rng(seed)``;
   * values N(0, 1) from ``torch.Generator`` seeded with ``seed`` on the target device,
-    drawn in the layer dtype (fp32, or bf16 rounded to nearest even);
+    drawn in the layer dtype (fp32, or bf16 / fp16 rounded to nearest even);
   * physical blocks: one random permutation of the pool; each sequence takes the next
     ceil(len / block_size) ids; block-table padding points at a spare block no sequence
     owns (the "poison" block), so a kernel that reads past a sequence's length reads
@@ -37,6 +37,7 @@ import torch
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 
 @dataclass
@@ -46,14 +47,16 @@ class LayerSpec:
     head_size: int
     block_size: int
     num_blocks: int
-    dtype: str                                   # F32 or BF16
+    dtype: str                                   # F32, BF16 or F16
     scale: float                                 # already rounded to fp32
     alibi_slopes: Optional[np.ndarray] = None    # float32 [num_heads]
     sliding_window: int = 0                      # <= 0: off
+    logits_soft_cap: float = 0.0                 # <= 0: off (already rounded to fp32)
+    sinks: Optional[np.ndarray] = None           # float32 [num_heads] sink logits
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == F32 else torch.bfloat16
+        return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[self.dtype]
 
     @property
     def elt_bytes(self) -> int:
@@ -116,6 +119,11 @@ def fp32(x: float) -> float:
 def alibi_slopes_geometric(num_heads: int) -> np.ndarray:
     """Slopes 2^(-8 (h + 1) / num_heads), rounded to fp32 (the chunked-prefill workload)."""
     return np.array([2.0 ** (-8.0 * (h + 1) / num_heads) for h in range(num_heads)], dtype=np.float32)
+
+
+def sink_logits(num_heads: int, seed: int) -> np.ndarray:
+    """Per-head sink logits, N(0, 2^2) drawn from ``numpy.random.default_rng(seed)``, fp32."""
+    return np.random.default_rng(seed).normal(0.0, 2.0, size=num_heads).astype(np.float32)
 
 
 def _normal(shape: Tuple[int, ...], dtype, device, gen) -> torch.Tensor:
@@ -273,9 +281,9 @@ def workload(k: int) -> Workload:
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:
-    """Exact bytes of a tensor as numpy (bf16 -> uint16 bit patterns, fp32 -> float32)."""
+    """Exact bytes of a tensor as numpy (bf16, fp16 -> uint16 bit patterns, fp32 -> float32)."""
     t = t.detach().to("cpu").contiguous()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.numpy()
