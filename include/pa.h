@@ -27,6 +27,13 @@
  * compose.  Query head h reads KV head h / (num_heads / num_kv_heads) (grouped-query
  * attention; aphrodite-engine "xformers.py", _run_memory_efficient_xformers_forward).
  *
+ * Optional logits soft-cap and attention sinks (named on the pages -- vLLM "cpu_attn",
+ * TorchSDPABackendImpl.__init__ logits_soft_cap; vLLM "utils", PerLayerParameters
+ * logits_soft_cap and has_sinks -- but not defined there; these are this library's readings):
+ * with a cap c > 0 the scaled dot product x = scale * <q, k_j> becomes c * tanh(x / c), and the
+ * ALiBi bias and the mask apply after it; a sink sigma_h is one extra logit of query head h
+ * that joins the softmax denominator only: out = sum_j e^(s_j) v_j / (e^(sigma_h) + sum_j e^(s_j)).
+ *
  * Numerics: products and softmax in fp32; for bf16 layers the softmax weights are rounded to
  * bf16 (nearest even) before they multiply V, and outputs are rounded to nearest even.
  *
@@ -71,6 +78,8 @@ typedef enum pa_dtype {
  *   scale           fp32 multiplier of <q, k>
  *   alibi_slopes    device fp32 [H], or NULL for no ALiBi
  *   sliding_window  W; <= 0 disables the window
+ *   logits_soft_cap c; <= 0 disables the soft-cap (NaN or infinity: PA_ERR_INVALID_ARGUMENT)
+ *   sinks           device fp32 [H] sink logits, or NULL for none
  */
 typedef struct pa_layer {
     int32_t num_heads;
@@ -82,6 +91,8 @@ typedef struct pa_layer {
     float scale;
     const float *alibi_slopes;
     int32_t sliding_window;
+    float logits_soft_cap;
+    const float *sinks;
 } pa_layer;
 
 /*

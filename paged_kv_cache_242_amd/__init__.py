@@ -49,6 +49,8 @@ class _CLayer(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("alibi_slopes", ctypes.c_void_p),
         ("sliding_window", ctypes.c_int32),
+        ("logits_soft_cap", ctypes.c_float),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -109,6 +111,8 @@ class Layer:
     scale: float
     alibi_slopes: Optional[torch.Tensor] = None      # fp32 [num_heads] on the GPU
     sliding_window: int = 0                          # <= 0: off
+    logits_soft_cap: float = 0.0                     # <= 0: off
+    sinks: Optional[torch.Tensor] = None             # fp32 [num_heads] sink logits on the GPU
 
     def _c(self) -> _CLayer:
         if self.dtype == torch.float32:
@@ -117,14 +121,15 @@ class Layer:
             dt = PA_DTYPE_BF16
         else:
             raise PaError(PA_ERR_UNSUPPORTED, f"dtype {self.dtype} is not supported (float32, bfloat16)")
-        slopes = None
-        if self.alibi_slopes is not None:
-            s = self.alibi_slopes
-            if s.dtype != torch.float32 or not s.is_cuda or s.numel() != self.num_heads or not s.is_contiguous():
-                raise PaError(PA_ERR_INVALID_ARGUMENT, "alibi_slopes must be a contiguous fp32 GPU tensor [num_heads]")
-            slopes = s.data_ptr()
+        def heads_ptr(t, name):
+            if t is None:
+                return None
+            if t.dtype != torch.float32 or not t.is_cuda or t.numel() != self.num_heads or not t.is_contiguous():
+                raise PaError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous fp32 GPU tensor [num_heads]")
+            return t.data_ptr()
         return _CLayer(self.num_heads, self.num_kv_heads, self.head_size, self.block_size, self.num_blocks, dt,
-                       float(self.scale), slopes, int(self.sliding_window or 0))
+                       float(self.scale), heads_ptr(self.alibi_slopes, "alibi_slopes"), int(self.sliding_window or 0),
+                       float(self.logits_soft_cap or 0.0), heads_ptr(self.sinks, "sinks"))
 
 
 def _stream(device: torch.device) -> int:

@@ -5,6 +5,8 @@
 // decode_block_tables): query row i, at position L_i - 1, attends to keys 0 .. L_i - 1 of its
 // sequence (restricted to the last W with a sliding window), which are read through block-table
 // row i; scores scale * <q, k_j> (+ slope_h * (j - pos) with ALiBi); softmax; weighted sum of V.
+// Optional soft-cap (c tanh(x / c) of the scaled dot product, before the bias) and per-head sink
+// logits (added to the softmax denominator only) follow the readings stated in pa.h.
 //
 // Work decomposition.  A work unit is one (sequence, KV head, group of up to 8 query heads); the
 // query heads of a group share every K/V byte, so each byte read from HBM feeds all of them.  The
@@ -350,7 +352,11 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     const int64_t block_bytes = int64_t(row_bytes) << p.block_shift;
     const char *kcache = reinterpret_cast<const char *>(p.k_cache);
     const char *vcache = reinterpret_cast<const char *>(p.v_cache);
-    const float qk_scale = p.scale * kLog2e;
+    const bool has_cap = p.softcap > 0.f;
+    // scores in base-2 units: dot * scale * log2(e), or with a soft-cap c,
+    // c log2(e) * tanh(dot * scale / c)
+    const float qk_scale = has_cap ? p.scale / p.softcap : p.scale * kLog2e;
+    const float cap2 = p.softcap * kLog2e;
     const bool has_alibi = p.alibi_slopes != nullptr;
 
     const int64_t Ttot = p.ws_prefix[p.num_seqs];
@@ -414,6 +420,10 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
                 chunk_dots<T, GP>(kr[i], q, part_dot);
                 butterfly<C, GP, 0>(part_dot);
                 sc[i] = part_dot[0] * qk_scale;
+            }
+            if (has_cap) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) sc[i] = cap2 * tanh_fast(sc[i]);
             }
             if (has_alibi) {
 #pragma unroll
@@ -597,8 +607,11 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head0) * D;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
-                const float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
+                float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
+                const float mh = __shfl(m_all, r * C + lane_of_head<C, GP>(h), 64);
                 if (tr == 0 && h < nh) {
+                    // a sink logit joins the denominator only
+                    if (p.sinks) lh += fast_exp2(p.sinks[head0 + h] * kLog2e - mh);
                     const float inv = 1.f / lh;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) store_out<T>(out_row + h * D + c * EPL + e, acc[h][e] * inv);
@@ -711,6 +724,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    if (p.sinks) den += fast_exp2(p.sinks[head] * kLog2e - M);
     const float inv = 1.f / den;
 #pragma unroll
     for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] * inv);

@@ -59,6 +59,8 @@ pa_status check_layer(const pa_layer *L, const char *fn) {
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_blocks %lld exceeds int32 block ids", fn,
                     (long long)L->num_blocks);
     if (!(L->scale == L->scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
+    if (!(L->logits_soft_cap == L->logits_soft_cap) || L->logits_soft_cap > 3.0e38f)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: logits_soft_cap must be finite", fn);
     return PA_OK;
 }
 
@@ -228,6 +230,8 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     p.scale = layer->scale;
     p.alibi_slopes = layer->alibi_slopes;
     p.window = layer->sliding_window;
+    p.softcap = layer->logits_soft_cap > 0.f ? layer->logits_soft_cap : 0.f;
+    p.sinks = layer->sinks;
     p.max_seq_len = max_seq_len;
     char *ws = static_cast<char *>(workspace);
     p.ws_prefix = reinterpret_cast<int64_t *>(ws + plan.ws_prefix_off);
@@ -292,6 +296,8 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
     p.scale = layer->scale;
     p.alibi_slopes = layer->alibi_slopes;
     p.window = layer->sliding_window;
+    p.softcap = layer->logits_soft_cap > 0.f ? layer->logits_soft_cap : 0.f;
+    p.sinks = layer->sinks;
     p.max_subquery_len = max_subquery_len;
     p.max_context_len = max_context_len;
     hipError_t e = pa::launch_prefill(p, layer->dtype, layer->head_size, static_cast<hipStream_t>(stream));

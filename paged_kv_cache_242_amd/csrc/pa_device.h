@@ -98,6 +98,13 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// tanh x = 1 - 2 / (e^(2x) + 1): v_exp and v_rcp, absolute error a few 1e-7; saturates to +-1
+// (e^(2x) overflows to infinity or underflows to 0).
+__device__ __forceinline__ float tanh_fast(float x) {
+    const float e = fast_exp2(x * (2.f * kLog2e));
+    return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
+
 // Compiler barrier for LDS traffic that stays inside one wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

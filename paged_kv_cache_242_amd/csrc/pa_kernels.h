@@ -64,6 +64,8 @@ struct DecodeParams {
     float scale;
     const float *alibi_slopes;
     int32_t window;
+    float softcap;            // <= 0: off
+    const float *sinks;       // [H] natural-log sink logits, or null
     int64_t *ws_prefix;       // [B + 1] tiles of the work units of sequences before q
     int32_t *ws_wseq;         // [num_waves] sequence of each wavefront's first tile
     float *ws_acc;            // [slots, D] partial weighted V
@@ -94,6 +96,8 @@ struct PrefillParams {
     float scale;
     const float *alibi_slopes;
     int32_t window;
+    float softcap;            // <= 0: off
+    const float *sinks;       // [H] natural-log sink logits, or null
     int32_t max_subquery_len;
     int32_t max_context_len;
 };

@@ -5,7 +5,8 @@
 // _run_memory_efficient_xformers_forward; vLLM "cpu_attn": flash_attn_varlen_func call): the
 // subquery token t of sequence i sits at position c_i + t and attends causally to keys
 // 0 .. c_i + t, the first c_i of which are read from the paged cache through the block table and
-// the rest from the key/value rows of the call; sliding window and ALiBi as in decode.
+// the rest from the key/value rows of the call; sliding window, ALiBi, soft-cap and sinks as in
+// decode.
 //
 // bf16 kernel (MFMA).  A workgroup of 4 wavefronts owns 128 (query row, head) pairs of one
 // sequence and KV head: 32 consecutive rows of 4 query heads of the group when the group size is
@@ -152,8 +153,13 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 //   * full when none is -- no per-score work besides the max and the exponent;
 //   * partial otherwise -- masked scores are set to -inf.
 // A negative scale is folded into a sign flip of Q (exact in bf16), a zero scale into Q = 0.
+//
+// With a logits soft-cap c (SOFTCAP) the raw scores become c log2(e) tanh(s |scale| / c) right
+// after the score MFMAs, the ALiBi key term is added to them in fp32 (it must stay outside the
+// cap, so the rank-1 MFMA is not used), and the exponent takes them with a unit multiplier.
+// Sink logits (p.sinks) join the row sums in the epilogue.
 
-template <int D, bool ALIBI>
+template <int D, bool ALIBI, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams p, PrefillGrid grid) {
     constexpr int CH = D / 8;        // 16-byte chunks per row
     constexpr int DC = D / 32;       // k-chunks of S^T
@@ -198,6 +204,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const float qk_eff = qk_scale > 0.f ? qk_scale : (qk_scale < 0.f ? -qk_scale : 1.f);
     const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // bf16 sign flips
     const uint32_t qand = qk_scale == 0.f ? 0u : 0xffffffffu;
+    // multiplier of the (transformed) scores in the exponent: |scale| log2(e), or 1 once the
+    // soft-cap has turned them into base-2 logits
+    const float s_mul = SOFTCAP ? 1.f : qk_eff;
+    const float cap_in = SOFTCAP ? fabsf(p.scale) / p.softcap : 0.f;
+    const float cap2 = SOFTCAP ? p.softcap * kLog2e : 0.f;
 
     // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qbk + l16), d = 32 dc + 8 lg .. +7.
     bf16x8_v qf[2][DC];
@@ -240,6 +251,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             const uint32_t rr = lane < 16 ? (uint32_t(r) | (uint32_t(r) << 16)) : 0u;
             arel[kk] = __builtin_bit_cast(bf16x8_v, make_uint4(rr, 0u, 0u, 0u));
         }
+    }
+
+    // ALiBi key term of slot (kk, i) relative to the half's first key, for the soft-cap path
+    float kbias[2][4] = {};
+    if constexpr (SOFTCAP && ALIBI) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kbias[kk][i] = slope2 * float(16 * kk + 4 * lg + i);
     }
 
     // ---- copies
@@ -421,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
                 for (int qbk = 0; qbk < 2; ++qbk)
                     s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[dc][kk], qf[qbk][dc], s[kk][qbk], 0, 0, 0);
-        if constexpr (ALIBI) {
+        if constexpr (ALIBI && !SOFTCAP) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -430,6 +450,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         }
         __builtin_amdgcn_s_setprio(0);
         load_v(vs, kc);
+        if constexpr (SOFTCAP) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cap_in), kbias[kk][i]);
+        }
 
         // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
         // 16 kk + i <= x and x - (16 kk + i) < W, x = pos - k0h - 4 lg.
@@ -462,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
             float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), fmaxf(s[0][qbk][2], s[0][qbk][3]));
             mx = fmaxf(mx, fmaxf(fmaxf(s[1][qbk][0], s[1][qbk][1]), fmaxf(s[1][qbk][2], s[1][qbk][3])));
-            tmax[qbk] = fmaf(mx, qk_eff, crow[qbk]);
+            tmax[qbk] = fmaf(mx, s_mul, crow[qbk]);
         }
         const bool raise = tmax[0] > m_run[0] + kRescaleSlack || tmax[1] > m_run[1] + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -492,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             for (int kk = 0; kk < 2; ++kk) {
                 float pf[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pf[i] = fast_exp2(fmaf(s[kk][qbk][i], qk_eff, off));
+                for (int i = 0; i < 4; ++i) pf[i] = fast_exp2(fmaf(s[kk][qbk][i], s_mul, off));
                 pk[kk][0] = pack_bf16x2(pf[0], pf[1]);
                 pk[kk][1] = pack_bf16x2(pf[2], pf[3]);
             }
@@ -568,7 +597,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     for (int qbk = 0; qbk < 2; ++qbk) {
         const int trow = t0 + 16 * qbk + l16;
         if (trow < si.n) {
-            const float inv = 1.f / lsum[qbk][0];
+            // a sink logit joins the row sum only (m_run is finite: the diagonal key is visible)
+            const float sink = p.sinks ? fast_exp2(p.sinks[h] * kLog2e - m_run[qbk]) : 0.f;
+            const float inv = 1.f / (lsum[qbk][0] + sink);
             bf16_t *orow = reinterpret_cast<bf16_t *>(p.out) + int64_t(si.start + trow) * p.num_heads * D +
                            int64_t(h) * D + 4 * lg;
 #pragma unroll
@@ -607,7 +638,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
     const float *qrow = reinterpret_cast<const float *>(p.query) + t * p.q_stride + int64_t(h) * D;
     for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
     __syncthreads();
-    const float qk_scale = p.scale * kLog2e;
+    const bool has_cap = p.softcap > 0.f;
+    const float qk_scale = has_cap ? p.scale / p.softcap : p.scale * kLog2e;
+    const float cap2 = p.softcap * kLog2e;
     const float slope2 = p.alibi_slopes ? p.alibi_slopes[h] * kLog2e : 0.f;
     float m = -INFINITY, l = 0.f, acc[PER];
 #pragma unroll
@@ -625,7 +658,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
             dot = fmaf(kv.z, qs[d + 2], dot);
             dot = fmaf(kv.w, qs[d + 3], dot);
         }
-        const float sc = key <= pos ? dot * qk_scale + slope2 * float(key - pos) : -INFINITY;
+        const float x = dot * qk_scale;
+        const float sc = key <= pos ? (has_cap ? cap2 * tanh_fast(x) : x) + slope2 * float(key - pos) : -INFINITY;
         const float tmax = xor_max_from<1>(sc);
         const float m_new = fmaxf(m, tmax);
         const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
@@ -643,6 +677,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
             for (int k = 0; k < PER; ++k) acc[k] = fmaf(pj, vq[lane + 64 * k], acc[k]);
         }
     }
+    if (p.sinks) l += fast_exp2(p.sinks[h] * kLog2e - m);
     float *orow = reinterpret_cast<float *>(p.out) + t * p.num_heads * D + int64_t(h) * D;
 #pragma unroll
     for (int k = 0; k < PER; ++k) orow[lane + 64 * k] = acc[k] / l;
@@ -668,17 +703,24 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipS
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
         grid.num_groups = int(groups);
         const dim3 nb = dim3(unsigned(blocks)), nt = dim3(kThreads);
-        const bool alibi = p.alibi_slopes != nullptr;
-        if (head_size == 128 && alibi)
-            hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), nb, nt, 0, stream, p, grid);
-        else if (head_size == 128)
-            hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), nb, nt, 0, stream, p, grid);
-        else if (head_size == 64 && alibi)
-            hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), nb, nt, 0, stream, p, grid);
-        else if (head_size == 64)
-            hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), nb, nt, 0, stream, p, grid);
-        else
-            return hipErrorInvalidValue;
+        const int variant = (p.alibi_slopes != nullptr ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
+        if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
+        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, nb, nt, 0, stream, p, grid); };
+        if (head_size == 128) {
+            switch (variant) {
+                case 0: go(prefill_bf16_kernel<128, false, false>); break;
+                case 1: go(prefill_bf16_kernel<128, true, false>); break;
+                case 2: go(prefill_bf16_kernel<128, false, true>); break;
+                default: go(prefill_bf16_kernel<128, true, true>); break;
+            }
+        } else {
+            switch (variant) {
+                case 0: go(prefill_bf16_kernel<64, false, false>); break;
+                case 1: go(prefill_bf16_kernel<64, true, false>); break;
+                case 2: go(prefill_bf16_kernel<64, false, true>); break;
+                default: go(prefill_bf16_kernel<64, true, true>); break;
+            }
+        }
         return hipGetLastError();
     }
     const int64_t blocks = p.num_tokens * p.num_heads;

@@ -23,17 +23,22 @@ def device():
     return torch.device("cuda:0")
 
 
+NAN_F16 = np.uint16(0x7E00)
+ORACLE_DTYPE = {wl.F32: oracle.DTYPE_F32, wl.BF16: oracle.DTYPE_BF16, wl.F16: oracle.DTYPE_F16}
+
+
 def player(layer: wl.LayerSpec, dev=None):
     dev = dev or device()
-    slopes = torch.tensor(layer.alibi_slopes, device=dev) if layer.alibi_slopes is not None else None
+    heads = lambda a: torch.tensor(a, dtype=torch.float32, device=dev) if a is not None else None
     return pa().Layer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size, layer.num_blocks,
-                      layer.torch_dtype, layer.scale, slopes, layer.sliding_window)
+                      layer.torch_dtype, layer.scale, heads(layer.alibi_slopes), layer.sliding_window,
+                      layer.logits_soft_cap, heads(layer.sinks))
 
 
 def olayer(layer: wl.LayerSpec) -> oracle.OracleLayer:
     return oracle.OracleLayer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size,
-                              layer.num_blocks, oracle.DTYPE_F32 if layer.dtype == wl.F32 else oracle.DTYPE_BF16,
-                              layer.scale, layer.alibi_slopes, layer.sliding_window)
+                              layer.num_blocks, ORACLE_DTYPE[layer.dtype], layer.scale, layer.alibi_slopes,
+                              layer.sliding_window, layer.logits_soft_cap, layer.sinks)
 
 
 def i32(a, dev=None):
@@ -97,7 +102,7 @@ def oracle_pool(batch: wl.PagedBatch, prefill_seqs: Optional[Iterable[int]] = No
     if subset or not fill_nan:
         pool = np.zeros(shape, dtype=et)
     else:
-        pool = np.full(shape, np.nan if et == np.float32 else NAN_BF16, dtype=et)
+        pool = np.full(shape, np.nan if et == np.float32 else (NAN_F16 if L.dtype == wl.F16 else NAN_BF16), dtype=et)
     off = ctx_offsets(batch)
     if not subset:
         if batch.ctx_key.shape[0]:
@@ -116,14 +121,17 @@ def oracle_pool(batch: wl.PagedBatch, prefill_seqs: Optional[Iterable[int]] = No
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     bits = wl.host_bits(t)
+    if t.dtype == torch.float16:
+        return oracle.f16_bits_to_f64(bits)
     if bits.dtype == np.uint16:
         return oracle.bf16_bits_to_f64(bits)
     return bits.astype(np.float64)
 
 
 def tolerance(layer: wl.LayerSpec):
-    """(max-abs, mean-abs) bounds: bf16 2e-2 / 2e-3, fp32 1e-4 max-abs."""
-    return (2e-2, 2e-3) if layer.dtype == wl.BF16 else (1e-4, 1e-4)
+    """(max-abs, mean-abs) bounds: bf16 2e-2 / 2e-3, fp32 1e-4 max-abs, fp16 5e-3 / 5e-4 (the
+    bf16 bounds scaled by the 8x finer fp16 rounding, with a margin of 2)."""
+    return {wl.BF16: (2e-2, 2e-3), wl.F16: (5e-3, 5e-4)}.get(layer.dtype, (1e-4, 1e-4))
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, layer: wl.LayerSpec, what: str):

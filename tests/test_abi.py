@@ -44,7 +44,7 @@ def test_version_and_status_strings(pa):
 
 def _layer(pa, **kw):
     base = dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=4, dtype=1, scale=0.1,
-                alibi_slopes=None, sliding_window=0)
+                alibi_slopes=None, sliding_window=0, logits_soft_cap=0.0, sinks=None)
     base.update(kw)
     return pa._CLayer(*base.values())
 
@@ -56,6 +56,8 @@ def _layer(pa, **kw):
     (dict(block_size=4), 2, "block size 4"),
     (dict(dtype=7), 2, "dtype 7"),
     (dict(num_blocks=0), 1, "num_blocks"),
+    (dict(logits_soft_cap=float("nan")), 1, "logits_soft_cap"),
+    (dict(logits_soft_cap=float("inf")), 1, "logits_soft_cap"),
 ])
 def test_layer_validation(pa, kw, status, needle):
     lib = pa.library()

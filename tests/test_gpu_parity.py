@@ -1,8 +1,8 @@
 """GPU parity: libpa (through the C ABI) against the fp64 oracle on the same seeded inputs.
 
 Cache write, block copy and block swap: bit-exact over the whole pool (unused slots keep their NaN
-fill).  Attention:
-bf16 max-abs <= 2e-2 and mean-abs <= 2e-3, fp32 max-abs <= 1e-4.  Small grids are compared
+fill).  Attention (plain, ALiBi, windows, logits soft-cap, sink logits): bf16 max-abs <= 2e-2 and
+mean-abs <= 2e-3, fp32 max-abs <= 1e-4, fp16 max-abs <= 5e-3 and mean-abs <= 5e-4.  Small grids are compared
 element by element; the five full-size workloads run in the same launch configuration the
 benchmark times and are compared on sampled sequences / rows (the oracle computes those one by
 one)."""
@@ -24,9 +24,10 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _layer(H, Hkv, D, bs, dtype=wl.BF16, alibi=False, window=0, scale=None):
+def _layer(H, Hkv, D, bs, dtype=wl.BF16, alibi=False, window=0, scale=None, softcap=0.0, sinks=False):
     return wl.LayerSpec(H, Hkv, D, bs, 0, dtype, wl.fp32(scale if scale is not None else 1.0 / math.sqrt(D)),
-                        alibi_slopes=wl.alibi_slopes_geometric(H) if alibi else None, sliding_window=window)
+                        alibi_slopes=wl.alibi_slopes_geometric(H) if alibi else None, sliding_window=window,
+                        logits_soft_cap=wl.fp32(softcap), sinks=wl.sink_logits(H, seed=H + D) if sinks else None)
 
 
 def _check_full(batch, what):
@@ -159,6 +160,12 @@ DECODE_LAYERS = [
     _layer(6, 3, 64, 256, alibi=True),
     _layer(8, 2, 128, 16, scale=-0.09),     # negative scale
     _layer(8, 8, 64, 16, alibi=True, scale=0.0),   # zero scale: weights from ALiBi alone
+    # logits soft-cap (caps that bite: scaled scores of a few units) and sink logits
+    _layer(32, 8, 128, 16, scale=0.3, softcap=5.0, sinks=True),
+    _layer(8, 8, 64, 16, wl.F32, alibi=True, window=100, softcap=3.0, sinks=True),
+    _layer(64, 8, 128, 32, sinks=True),
+    _layer(16, 2, 64, 8, scale=-0.4, softcap=2.0),
+    _layer(32, 32, 128, 16, alibi=True, softcap=4.0, scale=0.25),
 ]
 DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
 
@@ -228,6 +235,13 @@ PREFILL_LAYERS = [
     _layer(4, 4, 128, 32, alibi=True, window=700),
     _layer(16, 2, 128, 64),                             # 8 heads per KV head: two workgroups of 4 heads
     _layer(8, 8, 128, 256, alibi=True, window=300),     # 256-token blocks
+    # logits soft-cap and sink logits
+    _layer(32, 8, 128, 16, scale=0.3, softcap=5.0, sinks=True),
+    _layer(32, 32, 128, 16, alibi=True, window=100, softcap=4.0, scale=0.25),
+    _layer(8, 2, 64, 32, sinks=True),
+    _layer(4, 2, 128, 16, wl.F32, alibi=True, window=50, softcap=3.0, sinks=True),
+    _layer(8, 2, 128, 16, scale=-0.3, softcap=2.0, sinks=True),
+    _layer(8, 8, 64, 16, alibi=True, softcap=2.5),
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
