@@ -320,7 +320,7 @@ def main(argv=None):
         value = secondary["prefill"]["TFLOP_per_s"]
         unit = "TFLOP/s"
         roofline = {"bound": "mfma", "achieved": value, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": value / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_bf16_kernel",
+                    "frac": value / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_mfma_kernel",
                     "algorithmic_flops_per_launch": prefill_flops(batch)}
 
     cpu = None

@@ -34,8 +34,9 @@
  * ALiBi bias and the mask apply after it; a sink sigma_h is one extra logit of query head h
  * that joins the softmax denominator only: out = sum_j e^(s_j) v_j / (e^(sigma_h) + sum_j e^(s_j)).
  *
- * Numerics: products and softmax in fp32; for bf16 layers the softmax weights are rounded to
- * bf16 (nearest even) before they multiply V, and outputs are rounded to nearest even.
+ * Numerics: products and softmax in fp32; for bf16 and fp16 layers the softmax weights are
+ * rounded to the element type (nearest even) before they multiply V, and outputs are rounded to
+ * nearest even.
  *
  * Errors: every entry point returns a pa_status and launches nothing when it fails.  Only
  * host-visible scalars and pointers are validated.  Device contents (slots, block ids,
@@ -63,7 +64,8 @@ typedef enum pa_status {
 
 typedef enum pa_dtype {
     PA_DTYPE_F32 = 0,
-    PA_DTYPE_BF16 = 1
+    PA_DTYPE_BF16 = 1,
+    PA_DTYPE_F16 = 2
 } pa_dtype;
 
 /*
@@ -74,7 +76,9 @@ typedef enum pa_dtype {
  *   head_size       D: 64 or 128 (others: PA_ERR_UNSUPPORTED)
  *   block_size      tokens per cache block: a power of two in [8, 256]
  *   num_blocks      physical blocks per plane, > 0
- *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16 (the cache, query, key, value and out)
+ *   dtype           PA_DTYPE_F32, PA_DTYPE_BF16 or PA_DTYPE_F16 (the cache, query, key, value
+ *                   and out; vLLM "cpu_attn", TorchSDPABackend.get_supported_dtypes lists all
+ *                   three)
  *   scale           fp32 multiplier of <q, k>
  *   alibi_slopes    device fp32 [H], or NULL for no ALiBi
  *   sliding_window  W; <= 0 disables the window

@@ -27,6 +27,7 @@ PA_ERR_HIP = 4
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
+PA_DTYPE_F16 = 2
 
 EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
             "pa_status_string", "pa_last_error_message", "pa_version")
@@ -107,7 +108,7 @@ class Layer:
     head_size: int
     block_size: int
     num_blocks: int
-    dtype: torch.dtype                               # torch.float32 or torch.bfloat16
+    dtype: torch.dtype                               # torch.float32, torch.bfloat16 or torch.float16
     scale: float
     alibi_slopes: Optional[torch.Tensor] = None      # fp32 [num_heads] on the GPU
     sliding_window: int = 0                          # <= 0: off
@@ -115,12 +116,9 @@ class Layer:
     sinks: Optional[torch.Tensor] = None             # fp32 [num_heads] sink logits on the GPU
 
     def _c(self) -> _CLayer:
-        if self.dtype == torch.float32:
-            dt = PA_DTYPE_F32
-        elif self.dtype == torch.bfloat16:
-            dt = PA_DTYPE_BF16
-        else:
-            raise PaError(PA_ERR_UNSUPPORTED, f"dtype {self.dtype} is not supported (float32, bfloat16)")
+        dt = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16, torch.float16: PA_DTYPE_F16}.get(self.dtype)
+        if dt is None:
+            raise PaError(PA_ERR_UNSUPPORTED, f"dtype {self.dtype} is not supported (float32, bfloat16, float16)")
         def heads_ptr(t, name):
             if t is None:
                 return None

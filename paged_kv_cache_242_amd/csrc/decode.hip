@@ -26,12 +26,12 @@
 // (lane keeps half of its values, adds the partner's matching half), so the reduction of GP
 // dot products costs GP - 1 DPP adds instead of GP * log2(C); lane c ends with the full score of
 // head A(c).  P.V runs in the same layout: each lane accumulates its 8 output elements for all
-// GP heads over the rows it loaded (pairs of rows feed v_dot2_f32_bf16), reading the softmax
+// GP heads over the rows it loaded (pairs of rows feed v_dot2), reading the softmax
 // weights that the score lanes left in LDS; row groups are summed once at the end.
 //
-// Numerics: fp32 dot products (bf16 pairs through v_dot2_f32_bf16), softmax in the base-2
-// domain with fp32 exp2, weights rounded to bf16 before they multiply V, fp32 accumulation,
-// output rounded to nearest even.
+// Numerics: fp32 dot products (bf16 or fp16 pairs through v_dot2_f32_bf16 / v_dot2_f32_f16),
+// softmax in the base-2 domain with fp32 exp2, weights rounded to the element type before they
+// multiply V, fp32 accumulation, output rounded to nearest even.
 #include <math.h>
 
 #include "pa_device.h"
@@ -129,6 +129,8 @@ template <>
 __device__ __forceinline__ void store_out<float>(float *dst, float v) { *dst = v; }
 template <>
 __device__ __forceinline__ void store_out<bf16_t>(bf16_t *dst, float v) { *dst = f32_to_bf16(v); }
+template <>
+__device__ __forceinline__ void store_out<f16_t>(f16_t *dst, float v) { *dst = f32_to_f16(v); }
 
 // Partial dot products of one 16-byte row chunk with GP query chunks.
 template <typename T, int GP>
@@ -139,7 +141,7 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
         float acc = 0.f;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) acc = dot2_bf16(kw[w], q[s][w], acc);
+            for (int w = 0; w < 4; ++w) acc = dot2<T>(kw[w], q[s][w], acc);
         } else {
 #pragma unroll
             for (int w = 0; w < 4; ++w) acc = fmaf(__uint_as_float(kw[w]), __uint_as_float(q[s][w]), acc);
@@ -153,7 +155,7 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
 // wide head groups (more accumulators) and fp32 rows (more registers per key) use fewer.
 // Bytes in flight per CU = waves per CU * (DEPTH - 1) * 2 * NI KB (for 16-byte lanes).
 #ifndef PA_DECODE_NI_S
-#define PA_DECODE_NI_S 8        // bf16, head groups of 1 or 2
+#define PA_DECODE_NI_S 8        // 16-bit elements, head groups of 1 or 2
 #endif
 #ifndef PA_DECODE_DEPTH_S
 #define PA_DECODE_DEPTH_S 2
@@ -162,7 +164,7 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
 #define PA_DECODE_OCC_S 2
 #endif
 #ifndef PA_DECODE_NI_M
-#define PA_DECODE_NI_M 8        // bf16, head groups of 4
+#define PA_DECODE_NI_M 8        // 16-bit elements, head groups of 4
 #endif
 #ifndef PA_DECODE_DEPTH_M
 #define PA_DECODE_DEPTH_M 2
@@ -171,7 +173,7 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
 #define PA_DECODE_OCC_M 2
 #endif
 #ifndef PA_DECODE_NI_B
-#define PA_DECODE_NI_B 4        // bf16, head groups of 8
+#define PA_DECODE_NI_B 4        // 16-bit elements, head groups of 8
 #endif
 #ifndef PA_DECODE_DEPTH_B
 #define PA_DECODE_DEPTH_B 2
@@ -193,7 +195,7 @@ constexpr int tile_occ() {
 }
 
 // The running max is only raised when a tile's max exceeds it by more than this (base-2 units):
-// until then weights are exp2(s - m) <= 2^8, exact enough in fp32 sums and bf16 weights, and the
+// until then weights are exp2(s - m) <= 2^8, exact enough in fp32 sums and 16-bit weights, and the
 // accumulators need no rescaling.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -462,8 +464,8 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             for (int i = 0; i < NI; ++i) {
                 const float pf = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
                 if constexpr (sizeof(T) == 2) {
-                    pv[i] = f32_to_bf16(pf);
-                    psum += bf16_to_f32(pv[i]);
+                    pv[i] = to_elt<T>(pf);
+                    psum += elt_to_f32(pv[i]);
                 } else {
                     pv[i] = pf;
                     psum += pf;
@@ -491,7 +493,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             if constexpr (sizeof(T) == 2) {
 #pragma unroll
                 for (int ip = 0; ip < NI / 2; ++ip) {
-                    // row pair (2ip, 2ip+1) -> per element e the bf16 pair (v_2ip[e], v_2ip+1[e])
+                    // row pair (2ip, 2ip+1) -> per element e the pair (v_2ip[e], v_2ip+1[e])
                     const uint4 a = vr[2 * ip], b = vr[2 * ip + 1];
                     const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
                     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
@@ -505,7 +507,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
                     for (int h = 0; h < GP; ++h) {
                         const uint32_t pp = reinterpret_cast<const uint32_t *>(&p_lds[h][r][0])[ip];
 #pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[h][e] = dot2_bf16(pp, vp[e], acc[h][e]);
+                        for (int e = 0; e < EPL; ++e) acc[h][e] = dot2<T>(pp, vp[e], acc[h][e]);
                     }
                 }
             } else {
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] * inv);
 }
 
-// KV heads per work unit: 2 for bf16 head groups of 1 or 2 (whole 512-byte runs of two adjacent
+// KV heads per work unit: 2 for 16-bit head groups of 1 or 2 (whole 512-byte runs of two adjacent
 // head rows per token instead of 256-byte slices), when the KV head count is even.
 #ifndef PA_DECODE_KVH_S
 #define PA_DECODE_KVH_S 2
@@ -858,6 +860,9 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     if (dtype == 1) {
         if (head_size == 128) instance_info<bf16_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
         else instance_info<bf16_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+    } else if (dtype == 2) {
+        if (head_size == 128) instance_info<f16_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+        else instance_info<f16_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
     } else {
         if (head_size == 128) instance_info<float, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
         else instance_info<float, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
@@ -894,6 +899,9 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
     if (dtype == 1) {
         if (head_size == 128) return launch_group<bf16_t, 128>(p, s, plan.padded_group, stream);
         if (head_size == 64) return launch_group<bf16_t, 64>(p, s, plan.padded_group, stream);
+    } else if (dtype == 2) {
+        if (head_size == 128) return launch_group<f16_t, 128>(p, s, plan.padded_group, stream);
+        if (head_size == 64) return launch_group<f16_t, 64>(p, s, plan.padded_group, stream);
     } else {
         if (head_size == 128) return launch_group<float, 128>(p, s, plan.padded_group, stream);
         if (head_size == 64) return launch_group<float, 64>(p, s, plan.padded_group, stream);

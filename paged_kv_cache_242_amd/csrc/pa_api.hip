@@ -45,8 +45,9 @@ pa_status check_layer(const pa_layer *L, const char *fn) {
     if (L->num_heads % L->num_kv_heads != 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_kv_heads (%d) must divide num_heads (%d)", fn, L->num_kv_heads,
                     L->num_heads);
-    if (L->dtype != PA_DTYPE_F32 && L->dtype != PA_DTYPE_BF16)
-        return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (fp32 = 0, bf16 = 1)", fn, L->dtype);
+    if (L->dtype != PA_DTYPE_F32 && L->dtype != PA_DTYPE_BF16 && L->dtype != PA_DTYPE_F16)
+        return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (fp32 = 0, bf16 = 1, fp16 = 2)", fn,
+                    L->dtype);
     if (L->head_size != 64 && L->head_size != 128)
         return fail(PA_ERR_UNSUPPORTED, "%s: head size %d is not supported; supported head sizes are 64 and 128", fn,
                     L->head_size);

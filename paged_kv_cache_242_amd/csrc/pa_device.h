@@ -38,6 +38,54 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
+// fp16 values travel as raw 16-bit patterns too, in a type of their own so that templates can
+// tell them from bf16; arithmetic is done in fp32.
+enum class f16_t : uint16_t {};
+typedef _Float16 halfx2_v __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8_v __attribute__((ext_vector_type(8)));
+
+template <typename T>
+inline constexpr bool kIsF16 = false;
+template <>
+inline constexpr bool kIsF16<f16_t> = true;
+
+__device__ __forceinline__ float f16_to_f32(f16_t x) { return float(__builtin_bit_cast(_Float16, x)); }
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 under the default rounding mode).
+__device__ __forceinline__ f16_t f32_to_f16(float x) { return __builtin_bit_cast(f16_t, static_cast<_Float16>(x)); }
+
+// Two fp32 -> packed fp16 pair (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    typedef float float2_v __attribute__((ext_vector_type(2)));
+    const float2_v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, halfx2_v));
+}
+
+// c + a.lo * b.lo + a.hi * b.hi with fp16 pairs (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(halfx2_v, a), __builtin_bit_cast(halfx2_v, b), c, false);
+}
+
+// The 16-bit element types by name: conversions and pair dot products.
+template <typename T>
+__device__ __forceinline__ T to_elt(float x);
+template <>
+__device__ __forceinline__ bf16_t to_elt<bf16_t>(float x) { return f32_to_bf16(x); }
+template <>
+__device__ __forceinline__ f16_t to_elt<f16_t>(float x) { return f32_to_f16(x); }
+__device__ __forceinline__ float elt_to_f32(bf16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float elt_to_f32(f16_t x) { return f16_to_f32(x); }
+template <typename T>
+__device__ __forceinline__ uint32_t pack_x2(float lo, float hi) {
+    if constexpr (kIsF16<T>) return pack_f16x2(lo, hi);
+    else return pack_bf16x2(lo, hi);
+}
+template <typename T>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (kIsF16<T>) return dot2_f16(a, b, c);
+    else return dot2_bf16(a, b, c);
+}
+
 // Byte permute: result byte k = byte sel[k] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);

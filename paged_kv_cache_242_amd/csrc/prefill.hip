@@ -8,7 +8,7 @@
 // the rest from the key/value rows of the call; sliding window, ALiBi, soft-cap and sinks as in
 // decode.
 //
-// bf16 kernel (MFMA).  A workgroup of 4 wavefronts owns 128 (query row, head) pairs of one
+// 16-bit kernel (MFMA; bf16 or fp16 elements).  A workgroup of 4 wavefronts owns 128 (query row, head) pairs of one
 // sequence and KV head: 32 consecutive rows of 4 query heads of the group when the group size is
 // a multiple of 4 (all four wavefronts then share one diagonal), 64 rows of 2 heads, or 128 rows
 // of one head.  Each wavefront owns 32 rows of one head (two 16-row MFMA blocks).  The workgroup
@@ -17,7 +17,7 @@
 //     operand read touches hit distinct banks);
 //   * V tile row-major [64][D] (32-byte units xor-swizzled by row), read transposed by
 //     ds_read_b64_tr_b16.
-// Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: the accumulator
+// Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_{bf16,f16}: the accumulator
 // layout then gives every lane 4 consecutive keys of ONE query row, so the row's max and sum
 // need only two cross-lane steps, and two key blocks of those lanes are exactly the 8-key
 // slice a lane must supply as the B operand of O^T = V^T P^T (the k index of A and B uses the
@@ -78,7 +78,7 @@ __device__ __forceinline__ void row_ptrs(const PrefillParams &p, const SeqInfo &
     }
 }
 
-// Grid of the bf16 kernel.  Workgroups that read the same K/V -- the G query heads of one KV head
+// Grid of the MFMA kernel.  Workgroups that read the same K/V -- the G query heads of one KV head
 // and `qtiles_per_group` neighbouring query tiles of one sequence -- form a group.  Workgroups
 // are dealt to the 8 XCDs round-robin by index, so the index is built as
 // ((group / 8) * group_size + member) * 8 + group % 8: the members of a group run back to back on
@@ -152,15 +152,32 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 //   * empty for the wavefront when every (row, key) pair is masked -- skipped entirely;
 //   * full when none is -- no per-score work besides the max and the exponent;
 //   * partial otherwise -- masked scores are set to -inf.
-// A negative scale is folded into a sign flip of Q (exact in bf16), a zero scale into Q = 0.
+// A negative scale is folded into a sign flip of Q (exact in both 16-bit formats), a zero scale
+// into Q = 0.
 //
 // With a logits soft-cap c (SOFTCAP) the raw scores become c log2(e) tanh(s |scale| / c) right
 // after the score MFMAs, the ALiBi key term is added to them in fp32 (it must stay outside the
-// cap, so the rank-1 MFMA is not used), and the exponent takes them with a unit multiplier.
-// Sink logits (p.sinks) join the row sums in the epilogue.
+// cap, so the rank-1 MFMA is not used), and the exponent takes them with a unit multiplier.  fp16
+// layers with ALiBi take the fp32 key term too (s |scale| log2(e) + term), since the rank-1
+// factor slope / |scale| need not fit fp16's range.  Sink logits (p.sinks) join the row sums in
+// the epilogue.
 
-template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams p, PrefillGrid grid) {
+template <typename T>
+struct Operand8 { typedef bf16x8_v type; };   // 8 elements of an MFMA operand
+template <>
+struct Operand8<f16_t> { typedef halfx8_v type; };
+
+__device__ __forceinline__ floatx4_v mfma16(bf16x8_v a, bf16x8_v b, floatx4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4_v mfma16(halfx8_v a, halfx8_v b, floatx4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T, int D, bool ALIBI, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams p, PrefillGrid grid) {
+    typedef typename Operand8<T>::type V8;
+    auto elt_bits = [](T x) -> uint32_t { return uint32_t(__builtin_bit_cast(uint16_t, x)); };
     constexpr int CH = D / 8;        // 16-byte chunks per row
     constexpr int DC = D / 32;       // k-chunks of S^T
     constexpr int DB = D / 16;       // d-blocks of O^T
@@ -202,16 +219,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 
     const float qk_scale = p.scale * kLog2e;
     const float qk_eff = qk_scale > 0.f ? qk_scale : (qk_scale < 0.f ? -qk_scale : 1.f);
-    const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // bf16 sign flips
+    const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // sign flips of both halves
     const uint32_t qand = qk_scale == 0.f ? 0u : 0xffffffffu;
-    // multiplier of the (transformed) scores in the exponent: |scale| log2(e), or 1 once the
-    // soft-cap has turned them into base-2 logits
-    const float s_mul = SOFTCAP ? 1.f : qk_eff;
+    // The ALiBi key term rides on the score MFMAs (rank-1 update in 16-bit hi/lo parts) for bf16
+    // without a soft-cap; with a soft-cap it must stay outside the cap, and in fp16 the factor
+    // slope / |scale| could overflow, so there it is added in fp32 after the scores are formed.
+    constexpr bool KBIAS_MFMA = ALIBI && !SOFTCAP && !kIsF16<T>;
+    constexpr bool KBIAS_F32 = ALIBI && !KBIAS_MFMA;
+    // multiplier of the (transformed) scores in the exponent: |scale| log2(e), or 1 once they
+    // have been turned into base-2 logits
+    constexpr bool LOGITS = SOFTCAP || KBIAS_F32;
+    const float s_mul = LOGITS ? 1.f : qk_eff;
     const float cap_in = SOFTCAP ? fabsf(p.scale) / p.softcap : 0.f;
     const float cap2 = SOFTCAP ? p.softcap * kLog2e : 0.f;
 
     // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qbk + l16), d = 32 dc + 8 lg .. +7.
-    bf16x8_v qf[2][DC];
+    V8 qf[2][DC];
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
         const int trow = min(t0 + 16 * qbk + l16, si.n - 1);
@@ -224,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             w.y = (w.y ^ qxor) & qand;
             w.z = (w.z ^ qxor) & qand;
             w.w = (w.w ^ qxor) & qand;
-            qf[qbk][dc] = __builtin_bit_cast(bf16x8_v, w);
+            qf[qbk][dc] = __builtin_bit_cast(V8, w);
         }
     }
 
@@ -235,27 +258,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
     const int kt_lo = key_lo / kBN, kt_hi = key_hi / kBN;
 
     // ALiBi: slope in base-2 units; the rank-1 MFMA term adds (key - half start) * slope2 / qk_eff
-    // to the raw scores, with the factor split into a bf16 high and low part (k slots 0 and 1).
+    // to the raw scores, with the factor split into a high and a low 16-bit part (k slots 0 and 1).
     float slope2 = 0.f;
-    bf16x8_v bslope = {}, arel[2] = {};
-    if constexpr (ALIBI) {
-        slope2 = p.alibi_slopes[h] * kLog2e;
+    V8 bslope = {}, arel[2] = {};
+    if constexpr (ALIBI) slope2 = p.alibi_slopes[h] * kLog2e;
+    if constexpr (KBIAS_MFMA) {
         const float ratio = slope2 / qk_eff;
-        const bf16_t hi = f32_to_bf16(ratio);
-        const bf16_t lo = f32_to_bf16(ratio - bf16_to_f32(hi));
-        const uint32_t hl = lane < 16 ? (uint32_t(hi) | (uint32_t(lo) << 16)) : 0u;
-        bslope = __builtin_bit_cast(bf16x8_v, make_uint4(hl, 0u, 0u, 0u));
+        const T hi = to_elt<T>(ratio);
+        const T lo = to_elt<T>(ratio - elt_to_f32(hi));
+        const uint32_t hl = lane < 16 ? (elt_bits(hi) | (elt_bits(lo) << 16)) : 0u;
+        bslope = __builtin_bit_cast(V8, make_uint4(hl, 0u, 0u, 0u));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16_t r = f32_to_bf16(float(16 * kk + l16));
-            const uint32_t rr = lane < 16 ? (uint32_t(r) | (uint32_t(r) << 16)) : 0u;
-            arel[kk] = __builtin_bit_cast(bf16x8_v, make_uint4(rr, 0u, 0u, 0u));
+            const uint32_t r = elt_bits(to_elt<T>(float(16 * kk + l16)));
+            const uint32_t rr = lane < 16 ? (r | (r << 16)) : 0u;
+            arel[kk] = __builtin_bit_cast(V8, make_uint4(rr, 0u, 0u, 0u));
         }
     }
 
-    // ALiBi key term of slot (kk, i) relative to the half's first key, for the soft-cap path
+    // ALiBi key term of slot (kk, i) relative to the half's first key, for the fp32 path
     float kbias[2][4] = {};
-    if constexpr (SOFTCAP && ALIBI) {
+    if constexpr (KBIAS_F32) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -385,20 +408,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qbk][db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
     }
-    const bf16x8_v ones = __builtin_bit_cast(bf16x8_v, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const uint32_t one2 = elt_bits(to_elt<T>(1.f)) * 0x10001u;
+    const V8 ones = __builtin_bit_cast(V8, make_uint4(one2, one2, one2, one2));
 
     // One 32-key half (keys k0h .. k0h + 31, key chunk kc of the tile in (ks, vs)).
     // LDS operand reads are issued one phase ahead of their MFMAs: the K operands of a half are
     // read while the previous half finishes (or right after the tile barrier for the first half
     // of a tile), the V operands right after the half's S^T MFMAs, before its softmax.
-    bf16x8_v ka[DC][2];          // K operands of the coming half
-    bf16x8_v vop[DB];            // V^T operands of the current half
+    V8 ka[DC][2];                // K operands of the coming half
+    V8 vop[DB];                  // V^T operands of the current half
     auto load_k = [&](const bf16_t *ks, int kc) __attribute__((always_inline)) {
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                ka[dc][kk] = *reinterpret_cast<const bf16x8_v *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
+                ka[dc][kk] = *reinterpret_cast<const V8 *>(ks + k_off[dc] + 16 * (2 * kc + kk) * D);
     };
     auto load_v = [&](const bf16_t *vs, int kc) __attribute__((always_inline)) {
 #pragma unroll
@@ -407,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
             const v4i16 both[2] = {lo, hi};
-            vop[db] = __builtin_bit_cast(bf16x8_v, both);
+            vop[db] = __builtin_bit_cast(V8, both);
         }
     };
 
@@ -440,13 +464,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int qbk = 0; qbk < 2; ++qbk)
-                    s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[dc][kk], qf[qbk][dc], s[kk][qbk], 0, 0, 0);
-        if constexpr (ALIBI && !SOFTCAP) {
+                    s[kk][qbk] = mfma16(ka[dc][kk], qf[qbk][dc], s[kk][qbk]);
+        if constexpr (KBIAS_MFMA) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int qbk = 0; qbk < 2; ++qbk)
-                    s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arel[kk], bslope, s[kk][qbk], 0, 0, 0);
+                    s[kk][qbk] = mfma16(arel[kk], bslope, s[kk][qbk]);
         }
         __builtin_amdgcn_s_setprio(0);
         load_v(vs, kc);
@@ -458,6 +482,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cap_in), kbias[kk][i]);
+        } else if constexpr (KBIAS_F32) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[kk][qbk][i] = fmaf(s[kk][qbk][i], qk_eff, kbias[kk][i]);
         }
 
         // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
@@ -509,10 +540,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 
         if (next_kc >= 0) load_k(ks, next_kc);
 
-        // ---- P (bf16) as the B operand of O^T = V^T P^T: slots 0-3 are keys k0h + 4 lg + i,
+        // ---- P (16-bit) as the B operand of O^T = V^T P^T: slots 0-3 are keys k0h + 4 lg + i,
         // slots 4-7 keys k0h + 16 + 4 lg + i.  A row whose max is still -inf has seen no visible
         // key; its weights are exp2(-inf) = 0 against a finite stand-in max.
-        bf16x8_v pb[2];
+        V8 pb[2];
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) {
             const float off = crow[qbk] - (m_run[qbk] == -INFINITY ? 0.f : m_run[qbk]);
@@ -522,10 +553,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
                 float pf[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pf[i] = fast_exp2(fmaf(s[kk][qbk][i], s_mul, off));
-                pk[kk][0] = pack_bf16x2(pf[0], pf[1]);
-                pk[kk][1] = pack_bf16x2(pf[2], pf[3]);
+                pk[kk][0] = pack_x2<T>(pf[0], pf[1]);
+                pk[kk][1] = pack_x2<T>(pf[2], pf[3]);
             }
-            pb[qbk] = __builtin_bit_cast(bf16x8_v, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+            pb[qbk] = __builtin_bit_cast(V8, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
         }
 
         // ---- O^T += V^T P^T (V^T read transposed from the row-major V tile), row sums += 1^T P^T
@@ -533,10 +564,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk)
-                o[qbk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[qbk], o[qbk][db], 0, 0, 0);
+                o[qbk][db] = mfma16(vop[db], pb[qbk], o[qbk][db]);
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk)
-            lsum[qbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qbk], lsum[qbk], 0, 0, 0);
+            lsum[qbk] = mfma16(ones, pb[qbk], lsum[qbk]);
     };
     // Tile kt from stage (ks, vs), second half first; the first half's K operands are read here.
     auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
@@ -592,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
         __syncthreads();
     }
 
-    // ---- epilogue: O = O^T / l, rounded to bf16; lane holds d = 16 db + 4 lg + i of its row
+    // ---- epilogue: O = O^T / l, rounded to the element type; lane holds d = 16 db + 4 lg + i of its row
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
         const int trow = t0 + 16 * qbk + l16;
@@ -605,8 +636,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 uint2 w;
-                w.x = pack_bf16x2(o[qbk][db][0] * inv, o[qbk][db][1] * inv);
-                w.y = pack_bf16x2(o[qbk][db][2] * inv, o[qbk][db][3] * inv);
+                w.x = pack_x2<T>(o[qbk][db][0] * inv, o[qbk][db][1] * inv);
+                w.y = pack_x2<T>(o[qbk][db][2] * inv, o[qbk][db][3] * inv);
                 *reinterpret_cast<uint2 *>(orow + 16 * db) = w;
             }
         }
@@ -683,46 +714,50 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
     for (int k = 0; k < PER; ++k) orow[lane + 64 * k] = acc[k] / l;
 }
 
+template <typename T>
+hipError_t launch_mfma(const PrefillParams &p, int head_size, hipStream_t stream) {
+    PrefillGrid grid;
+    const int group = p.num_heads / p.num_kv_heads;
+    grid.heads = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+    grid.rows = kRowsPerBlock / grid.heads;
+    grid.num_qtiles = (p.max_subquery_len + grid.rows - 1) / grid.rows;
+    const int hblocks = group / grid.heads;
+    grid.qtiles_per_group = hblocks >= 8 ? 1 : min(8 / hblocks, grid.num_qtiles);
+    if (grid.qtiles_per_group < 1) grid.qtiles_per_group = 1;
+    grid.num_qblocks = (grid.num_qtiles + grid.qtiles_per_group - 1) / grid.qtiles_per_group;
+    grid.group_size = hblocks * grid.qtiles_per_group;
+    const int64_t groups = int64_t(grid.num_qblocks) * p.num_seqs * p.num_kv_heads;
+    if (groups == 0) return hipSuccess;
+    const int64_t blocks = (groups + 7) / 8 * 8 * grid.group_size;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    grid.num_groups = int(groups);
+    const dim3 nb = dim3(unsigned(blocks)), nt = dim3(kThreads);
+    const int variant = (p.alibi_slopes != nullptr ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
+    if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, nb, nt, 0, stream, p, grid); };
+    if (head_size == 128) {
+        switch (variant) {
+            case 0: go(prefill_mfma_kernel<T, 128, false, false>); break;
+            case 1: go(prefill_mfma_kernel<T, 128, true, false>); break;
+            case 2: go(prefill_mfma_kernel<T, 128, false, true>); break;
+            default: go(prefill_mfma_kernel<T, 128, true, true>); break;
+        }
+    } else {
+        switch (variant) {
+            case 0: go(prefill_mfma_kernel<T, 64, false, false>); break;
+            case 1: go(prefill_mfma_kernel<T, 64, true, false>); break;
+            case 2: go(prefill_mfma_kernel<T, 64, false, true>); break;
+            default: go(prefill_mfma_kernel<T, 64, true, true>); break;
+        }
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipStream_t stream) {
-    if (dtype == 1) {
-        PrefillGrid grid;
-        const int group = p.num_heads / p.num_kv_heads;
-        grid.heads = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-        grid.rows = kRowsPerBlock / grid.heads;
-        grid.num_qtiles = (p.max_subquery_len + grid.rows - 1) / grid.rows;
-        const int hblocks = group / grid.heads;
-        grid.qtiles_per_group = hblocks >= 8 ? 1 : min(8 / hblocks, grid.num_qtiles);
-        if (grid.qtiles_per_group < 1) grid.qtiles_per_group = 1;
-        grid.num_qblocks = (grid.num_qtiles + grid.qtiles_per_group - 1) / grid.qtiles_per_group;
-        grid.group_size = hblocks * grid.qtiles_per_group;
-        const int64_t groups = int64_t(grid.num_qblocks) * p.num_seqs * p.num_kv_heads;
-        if (groups == 0) return hipSuccess;
-        const int64_t blocks = (groups + 7) / 8 * 8 * grid.group_size;
-        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        grid.num_groups = int(groups);
-        const dim3 nb = dim3(unsigned(blocks)), nt = dim3(kThreads);
-        const int variant = (p.alibi_slopes != nullptr ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
-        if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
-        auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, nb, nt, 0, stream, p, grid); };
-        if (head_size == 128) {
-            switch (variant) {
-                case 0: go(prefill_bf16_kernel<128, false, false>); break;
-                case 1: go(prefill_bf16_kernel<128, true, false>); break;
-                case 2: go(prefill_bf16_kernel<128, false, true>); break;
-                default: go(prefill_bf16_kernel<128, true, true>); break;
-            }
-        } else {
-            switch (variant) {
-                case 0: go(prefill_bf16_kernel<64, false, false>); break;
-                case 1: go(prefill_bf16_kernel<64, true, false>); break;
-                case 2: go(prefill_bf16_kernel<64, false, true>); break;
-                default: go(prefill_bf16_kernel<64, true, true>); break;
-            }
-        }
-        return hipGetLastError();
-    }
+    if (dtype == 1) return launch_mfma<bf16_t>(p, head_size, stream);
+    if (dtype == 2) return launch_mfma<f16_t>(p, head_size, stream);
     const int64_t blocks = p.num_tokens * p.num_heads;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

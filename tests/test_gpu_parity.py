@@ -49,7 +49,7 @@ def _check_full(batch, what):
 
 @pytest.mark.parametrize("H,Hkv,D,bs,dtype", [
     (8, 8, 64, 16, wl.F32), (32, 8, 128, 16, wl.BF16), (64, 8, 128, 32, wl.BF16), (4, 1, 64, 8, wl.BF16),
-    (6, 3, 128, 256, wl.F32),
+    (6, 3, 128, 256, wl.F32), (32, 8, 128, 16, wl.F16),
 ])
 def test_cache_write_bit_exact(H, Hkv, D, bs, dtype):
     layer = _layer(H, Hkv, D, bs, dtype)
@@ -83,18 +83,19 @@ def test_cache_write_strided_rows_and_padding():
 def _random_cache(layer, nb, rng, dev):
     """[2, nb, block elements] cache of random bit patterns (NaNs and infinities included)."""
     elems = layer.block_size * layer.num_kv_heads * layer.head_size
-    if layer.dtype == wl.BF16:
+    if layer.dtype in (wl.BF16, wl.F16):
         bits = rng.integers(0, 1 << 16, size=(2, nb, elems), dtype=np.uint16)
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(bits.view(np.int16)).view(layer.torch_dtype).to(dev)
     bits = rng.integers(0, 1 << 32, size=(2, nb, elems), dtype=np.uint32)
     return torch.from_numpy(bits.view(np.float32)).to(dev)
 
 
 def _bits(t):
-    return wl.host_bits(t).view(np.uint16 if t.dtype == torch.bfloat16 else np.uint32)
+    return wl.host_bits(t).view(np.uint16 if t.dtype in (torch.bfloat16, torch.float16) else np.uint32)
 
 
-@pytest.mark.parametrize("H,Hkv,D,bs,dtype", [(8, 2, 128, 16, wl.BF16), (4, 4, 64, 8, wl.F32), (16, 8, 128, 256, wl.BF16)])
+@pytest.mark.parametrize("H,Hkv,D,bs,dtype", [(8, 2, 128, 16, wl.BF16), (4, 4, 64, 8, wl.F32), (16, 8, 128, 256, wl.BF16),
+                                               (8, 8, 64, 32, wl.F16)])
 def test_copy_blocks_bit_exact(H, Hkv, D, bs, dtype):
     layer = _layer(H, Hkv, D, bs, dtype)
     nb = 64
@@ -166,6 +167,11 @@ DECODE_LAYERS = [
     _layer(64, 8, 128, 32, sinks=True),
     _layer(16, 2, 64, 8, scale=-0.4, softcap=2.0),
     _layer(32, 32, 128, 16, alibi=True, softcap=4.0, scale=0.25),
+    # fp16
+    _layer(32, 8, 128, 16, wl.F16),
+    _layer(64, 8, 128, 32, wl.F16, sinks=True),
+    _layer(32, 32, 128, 16, wl.F16, alibi=True, window=100),
+    _layer(16, 2, 64, 8, wl.F16, softcap=3.0, scale=0.3),
 ]
 DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
 
@@ -242,6 +248,12 @@ PREFILL_LAYERS = [
     _layer(4, 2, 128, 16, wl.F32, alibi=True, window=50, softcap=3.0, sinks=True),
     _layer(8, 2, 128, 16, scale=-0.3, softcap=2.0, sinks=True),
     _layer(8, 8, 64, 16, alibi=True, softcap=2.5),
+    # fp16
+    _layer(32, 8, 128, 16, wl.F16),
+    _layer(32, 32, 128, 16, wl.F16, alibi=True, window=100),
+    _layer(8, 2, 64, 32, wl.F16, sinks=True),
+    _layer(8, 4, 128, 16, wl.F16, alibi=True, softcap=4.0, scale=0.25),
+    _layer(8, 2, 128, 16, wl.F16, scale=-0.09),
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
