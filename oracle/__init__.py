@@ -26,6 +26,8 @@ _LIB = os.path.join(_HERE, "libpa_oracle.so")
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_F16 = 2
+KV_CACHE_AUTO = 0        # the cache holds elements of the layer dtype
+KV_CACHE_FP8_E4M3 = 1    # the cache holds FP8 E4M3 codes (uint8), scaled by k_scale / v_scale
 
 
 def build(force: bool = True) -> str:
@@ -52,6 +54,9 @@ class _Layer(ctypes.Structure):
         ("sliding_window", ctypes.c_int32),
         ("logits_soft_cap", ctypes.c_float),
         ("sinks", ctypes.c_void_p),
+        ("kv_cache_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -97,6 +102,9 @@ class OracleLayer:
     sliding_window: int = 0
     logits_soft_cap: float = 0.0               # <= 0: off
     sinks: Optional[np.ndarray] = None          # float32 [num_heads] sink logits
+    kv_cache_dtype: int = KV_CACHE_AUTO
+    k_scale: float = 1.0                        # fp8 cache scales (fp32)
+    v_scale: float = 1.0
 
     def _c(self):
         def f32_heads(a):
@@ -110,7 +118,8 @@ class OracleLayer:
                    self.num_blocks, self.dtype, float(np.float32(self.scale)),
                    slopes.ctypes.data if slopes is not None else None,
                    int(self.sliding_window), float(np.float32(self.logits_soft_cap)),
-                   sinks.ctypes.data if sinks is not None else None)
+                   sinks.ctypes.data if sinks is not None else None, int(self.kv_cache_dtype),
+                   float(np.float32(self.k_scale)), float(np.float32(self.v_scale)))
         return c, (slopes, sinks)   # keep the arrays alive while c is used
 
 
@@ -127,11 +136,16 @@ def _elt_dtype(layer: OracleLayer):
     return np.float32 if layer.dtype == DTYPE_F32 else np.uint16
 
 
+def cache_dtype(layer: OracleLayer):
+    """numpy dtype of the paged cache's elements (uint8 codes for an fp8 cache)."""
+    return np.uint8 if layer.kv_cache_dtype == KV_CACHE_FP8_E4M3 else _elt_dtype(layer)
+
+
 def cache_write(layer: OracleLayer, key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarray,
                 kv_cache: np.ndarray) -> None:
     """In place: scatter key/value rows [T, Hkv*D] into kv_cache through slot_mapping."""
     et = _elt_dtype(layer)
-    assert key.dtype == et and value.dtype == et and kv_cache.dtype == et
+    assert key.dtype == et and value.dtype == et and kv_cache.dtype == cache_dtype(layer)
     assert key.shape == value.shape and key.ndim == 2
     if key.shape[0] == 0:
         return
@@ -149,7 +163,7 @@ def cache_write(layer: OracleLayer, key: np.ndarray, value: np.ndarray, slot_map
 def copy_blocks(layer: OracleLayer, kv_caches, block_pairs: np.ndarray) -> None:
     """In place, every cache of the list: block src -> block dst for each (src, dst) pair
     (both planes; pairs outside [0, num_blocks) skipped; applied in order)."""
-    et = _elt_dtype(layer)
+    et = cache_dtype(layer)
     pairs = np.ascontiguousarray(block_pairs, dtype=np.int64).reshape(-1, 2)
     for c in kv_caches:
         assert c.dtype == et and c.flags.c_contiguous
@@ -162,7 +176,7 @@ def copy_blocks(layer: OracleLayer, kv_caches, block_pairs: np.ndarray) -> None:
 def swap_blocks(layer: OracleLayer, src_cache: np.ndarray, dst_cache: np.ndarray, block_pairs: np.ndarray) -> None:
     """In place: block src of src_cache -> block dst of dst_cache, both planes, for each pair.
     The caches are [2, n_blocks, block elements] with their own block counts."""
-    et = _elt_dtype(layer)
+    et = cache_dtype(layer)
     assert src_cache.dtype == et and dst_cache.dtype == et and dst_cache.flags.c_contiguous
     src_cache = np.ascontiguousarray(src_cache)
     pairs = np.ascontiguousarray(block_pairs, dtype=np.int64).reshape(-1, 2)
@@ -176,7 +190,7 @@ def decode(layer: OracleLayer, query: np.ndarray, kv_cache: np.ndarray, block_ta
            seq_lens: np.ndarray, num_threads: int = 0, return_threads: bool = False):
     """fp64 [B, H, D] decode output (see ``orc_decode`` in pa_oracle.c)."""
     et = _elt_dtype(layer)
-    assert query.dtype == et and kv_cache.dtype == et and kv_cache.flags.c_contiguous
+    assert query.dtype == et and kv_cache.dtype == cache_dtype(layer) and kv_cache.flags.c_contiguous
     assert query.ndim == 2
     query = np.ascontiguousarray(query)
     B = query.shape[0]
@@ -222,7 +236,7 @@ def prefill(layer: OracleLayer, query: np.ndarray, key: np.ndarray, value: np.nd
         assert block_tables.ndim == 2 and block_tables.shape[0] == N
         maxb = block_tables.shape[1]
     if kv_cache is not None:
-        assert kv_cache.dtype == et and kv_cache.flags.c_contiguous
+        assert kv_cache.dtype == cache_dtype(layer) and kv_cache.flags.c_contiguous
     sel = None
     if row_select is not None:
         sel = np.ascontiguousarray(row_select, dtype=np.uint8)

@@ -51,6 +51,16 @@
  *      sink sigma_h: one extra logit per query head that joins the softmax normalisation
  *      but carries no value, so out = sum_j e^(s_j) v_j / (e^(sigma_h) + sum_j e^(s_j)).
  *
+ *  - fp8 KV cache.  The pages pass a kv_cache_dtype and per-tensor scales to the cache write
+ *    and to the attention calls (aphrodite-engine "xformers.py", write_to_paged_cache and
+ *    forward_decode with kv_cache_dtype and kv_scale; vLLM "cpu_attn", write_to_paged_cache and
+ *    forward_decode with layer._k_scale and layer._v_scale) but never show the encoding.
+ *    Reading taken here: kv_cache_dtype 1 stores OCP FP8 E4M3 codes (1 sign, 4 exponent bits
+ *    with bias 7, 3 fraction bits, no infinities, S.1111.111 = NaN, largest finite 448); a key
+ *    element x is stored as the code nearest to the fp32 quotient fp32(x) / k_scale (ties to
+ *    the even code, magnitudes above 448 saturate to 448, NaN stays NaN), a value element with
+ *    v_scale; attention reads code_value * k_scale (or v_scale) in fp64.
+ *
  * Inputs are promoted exactly to double: fp32 directly, bf16 by placing its 16 bits in
  * the high half of an fp32, fp16 from its sign, exponent and fraction fields.  Outputs are
  * double.  Element types: 0 = fp32, 1 = bf16, 2 = fp16 (the pages list all three as
@@ -81,9 +91,46 @@ typedef struct {
     int32_t sliding_window; /* <= 0: no window */
     float logits_soft_cap;  /* <= 0: no soft-cap */
     const float *sinks;     /* [H] sink logits, or NULL */
+    int32_t kv_cache_dtype; /* 0: the cache holds dtype elements; 1: FP8 E4M3 codes */
+    float k_scale;          /* fp8 cache: key element = code value * k_scale */
+    float v_scale;          /* fp8 cache: value element = code value * v_scale */
 } orc_layer;
 
 static int elt_bytes(int32_t dtype) { return dtype == 0 ? 4 : 2; }
+
+/* Bytes of one element of the paged cache. */
+static int cache_elt_bytes(const orc_layer *L) { return L->kv_cache_dtype == 1 ? 1 : elt_bytes(L->dtype); }
+
+/* Value of an FP8 E4M3 code (OCP "e4m3fn"). */
+static double e4m3_to_double(uint8_t c)
+{
+    const int sign = c >> 7, e = (c >> 3) & 15, f = c & 7;
+    double v;
+    if (e == 15 && f == 7) v = NAN;
+    else if (e == 0) v = ldexp((double)f, -9);             /* subnormal: f/8 * 2^-6 */
+    else v = ldexp((double)(8 + f), e - 10);               /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* The E4M3 code nearest to x: ties go to the code with an even fraction, magnitudes above 448
+ * saturate to 448, NaN gives the NaN code.  Found by scanning the 127 finite non-negative codes. */
+static uint8_t float_to_e4m3(float x)
+{
+    if (x != x) return signbit(x) ? 0xFF : 0x7F;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs((double)x);
+    if (a >= 448.0) return sign | 0x7E;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c < 127; ++c) {
+        const double err = fabs(a - e4m3_to_double((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | (uint8_t)best;
+}
 
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 static double half_to_double(uint16_t h)
@@ -123,6 +170,10 @@ static int layer_ok(const orc_layer *L)
         return 0;
     if (L->num_heads % L->num_kv_heads != 0) return 0;
     if (L->dtype < 0 || L->dtype > 2) return 0;
+    if (L->kv_cache_dtype != 0 && L->kv_cache_dtype != 1) return 0;
+    if (L->kv_cache_dtype == 1 && !(L->k_scale > 0.0f && L->v_scale > 0.0f && isfinite(L->k_scale) &&
+                                    isfinite(L->v_scale)))
+        return 0;
     if (L->num_blocks < 0) return 0;
     return 1;
 }
@@ -140,7 +191,7 @@ static int layer_ok(const orc_layer *L)
  */
 static int64_t block_bytes(const orc_layer *L)
 {
-    return (int64_t)L->block_size * L->num_kv_heads * L->head_size * elt_bytes(L->dtype);
+    return (int64_t)L->block_size * L->num_kv_heads * L->head_size * cache_elt_bytes(L);
 }
 
 int orc_copy_blocks(const orc_layer *L, void *const *caches, int32_t num_layers, const int64_t *pairs,
@@ -192,10 +243,11 @@ int orc_cache_write(const orc_layer *L, const void *key, const void *value, int6
 {
     if (!layer_ok(L) || num_tokens < 0) return ORC_BAD_ARG;
     const int eb = elt_bytes(L->dtype);
+    const int cb = cache_elt_bytes(L);
     const int64_t plane = L->num_blocks * L->block_size * L->num_kv_heads * L->head_size;
     const int64_t row = (int64_t)L->num_kv_heads * L->head_size;
     char *kc = (char *)kv_cache;
-    char *vc = kc + plane * eb;
+    char *vc = kc + plane * cb;
     for (int64_t t = 0; t < num_tokens; ++t) {
         int64_t s = slot_mapping[t];
         if (s < 0) continue;
@@ -206,8 +258,16 @@ int orc_cache_write(const orc_layer *L, const void *key, const void *value, int6
             for (int64_t d = 0; d < L->head_size; ++d) {
                 int64_t src = t * row_stride + g * L->head_size + d;
                 int64_t dst = cache_index(L, block, offset, g, d);
-                memcpy(kc + dst * eb, (const char *)key + src * eb, eb);
-                memcpy(vc + dst * eb, (const char *)value + src * eb, eb);
+                if (L->kv_cache_dtype == 1) {
+                    /* quantize: the fp32 quotient, then the nearest code */
+                    const float kq = (float)elt_to_double(key, src, L->dtype) / L->k_scale;
+                    const float vq = (float)elt_to_double(value, src, L->dtype) / L->v_scale;
+                    ((uint8_t *)kc)[dst] = float_to_e4m3(kq);
+                    ((uint8_t *)vc)[dst] = float_to_e4m3(vq);
+                } else {
+                    memcpy(kc + dst * eb, (const char *)key + src * eb, eb);
+                    memcpy(vc + dst * eb, (const char *)value + src * eb, eb);
+                }
             }
         }
     }
@@ -225,15 +285,20 @@ static int unpage(const orc_layer *L, const void *kv_cache, const int32_t *table
 {
     const int64_t plane = L->num_blocks * L->block_size * L->num_kv_heads * L->head_size;
     const char *kc = (const char *)kv_cache;
-    const char *vc = kc + plane * elt_bytes(L->dtype);
+    const char *vc = kc + plane * cache_elt_bytes(L);
     for (int64_t j = 0; j < n; ++j) {
         int64_t block = table_row[j / L->block_size];
         int64_t offset = j % L->block_size;
         if (block < 0 || block >= L->num_blocks) return ORC_BAD_INDEX;
         for (int64_t d = 0; d < L->head_size; ++d) {
             int64_t idx = cache_index(L, block, offset, g, d);
-            K[j * L->head_size + d] = elt_to_double(kc, idx, L->dtype);
-            V[j * L->head_size + d] = elt_to_double(vc, idx, L->dtype);
+            if (L->kv_cache_dtype == 1) {
+                K[j * L->head_size + d] = e4m3_to_double(((const uint8_t *)kc)[idx]) * (double)L->k_scale;
+                V[j * L->head_size + d] = e4m3_to_double(((const uint8_t *)vc)[idx]) * (double)L->v_scale;
+            } else {
+                K[j * L->head_size + d] = elt_to_double(kc, idx, L->dtype);
+                V[j * L->head_size + d] = elt_to_double(vc, idx, L->dtype);
+            }
         }
     }
     return ORC_OK;

@@ -36,11 +36,18 @@ NAN_F16 = np.uint16(0x7E00)
 def oracle_layer(layer: wl.LayerSpec) -> oracle.OracleLayer:
     return oracle.OracleLayer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size,
                               layer.num_blocks, ORACLE_DTYPE[layer.dtype], layer.scale, layer.alibi_slopes,
-                              layer.sliding_window, layer.logits_soft_cap, layer.sinks)
+                              layer.sliding_window, layer.logits_soft_cap, layer.sinks,
+                              oracle.KV_CACHE_FP8_E4M3 if layer.fp8_cache else oracle.KV_CACHE_AUTO,
+                              layer.k_scale, layer.v_scale)
+
+
+NAN_E4M3 = np.uint8(0x7F)
 
 
 def nan_pool(layer: wl.LayerSpec) -> np.ndarray:
     shape = (2, layer.num_blocks, layer.block_size * layer.num_kv_heads * layer.head_size)
+    if layer.fp8_cache:
+        return np.full(shape, NAN_E4M3, dtype=np.uint8)
     if layer.dtype == wl.F32:
         return np.full(shape, np.nan, dtype=np.float32)
     return np.full(shape, NAN_F16 if layer.dtype == wl.F16 else NAN_BF16, dtype=np.uint16)
@@ -496,6 +503,83 @@ def pin_f16_inputs():
                       seed=1500)
 
 
+def _e4m3_values(codes: np.ndarray) -> np.ndarray:
+    """Values of FP8 E4M3 codes by torch's float8_e4m3fn type (the library's own decoding)."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+
+
+def _fp8_layer(**kw) -> oracle.OracleLayer:
+    base = dict(num_heads=1, num_kv_heads=1, head_size=256, block_size=1, num_blocks=1, dtype=oracle.DTYPE_F32,
+                scale=1.0, kv_cache_dtype=oracle.KV_CACHE_FP8_E4M3)
+    base.update(kw)
+    return oracle.OracleLayer(**base)
+
+
+def pin_e4m3_code_table():
+    """Every FP8 E4M3 code is read as torch's float8_e4m3fn value (NaN codes as NaN): a one-key
+    decode with q = 0 returns the value row, here all 256 codes, times v_scale = 1."""
+    ol = _fp8_layer()
+    pool = np.zeros((2, 1, 256), dtype=np.uint8)
+    pool[1, 0] = np.arange(256)
+    out = oracle.decode(ol, np.zeros((1, 256), dtype=np.float32), pool, np.array([[0]]), np.array([1]))[0, 0]
+    ref = _e4m3_values(np.arange(256))
+    assert np.array_equal(np.isnan(out), np.isnan(ref)), "NaN codes differ"
+    fin = ~np.isnan(ref)
+    assert np.array_equal(out[fin], ref[fin]), "E4M3 code values differ from torch float8_e4m3fn"
+
+
+def pin_e4m3_quantize():
+    """The fp8 cache write stores, for each element, torch's float8_e4m3fn rounding (nearest,
+    ties to even) of the fp32 quotient x / scale; quotients of magnitude 464 and above (which
+    torch turns into NaN) saturate to +-448, NaN stays NaN.  Checked on every midpoint between
+    neighbouring codes, the codes themselves, points just off the midpoints, and random values,
+    with scales 1 and 0.75."""
+    pos = _e4m3_values(np.arange(127))                      # finite non-negative code values
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([pos, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                           np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.random.default_rng(9).uniform(-470, 470, 2000)]).astype(np.float32)
+    vals = np.concatenate([vals, -vals, np.array([464.0, 1e6, np.inf, -np.inf, np.nan, -0.0], dtype=np.float32)])
+    n = vals.size
+    for scale in (1.0, 0.75):
+        ol = _fp8_layer(head_size=1, num_blocks=n, k_scale=scale, v_scale=scale)
+        pool = np.zeros((2, n, 1), dtype=np.uint8)
+        oracle.cache_write(ol, vals[:, None], vals[:, None], np.arange(n), pool)
+        q = (vals / np.float32(scale)).astype(np.float32)    # the fp32 quotient
+        expect = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        big = np.abs(q) >= 464
+        expect[big] = np.where(np.signbit(q[big]), 0xFE, 0x7E)
+        nan = np.isnan(q)
+        expect[nan] = np.where(np.signbit(q[nan]), 0xFF, 0x7F)
+        for plane in (0, 1):
+            got = pool[plane, :, 0]
+            bad = np.flatnonzero(got != expect)
+            assert bad.size == 0, (f"scale {scale}: code of {q[bad[0]]!r} is {got[bad[0]]:#x}, "
+                                   f"expected {expect[bad[0]]:#x}")
+
+
+def pin_fp8_cache_is_dequantized_cache():
+    """Attention over an fp8 cache equals attention over an fp32 cache holding code value *
+    scale (exact for the power-of-two scales used), decode and chunked prefill alike; the
+    dequantized pool is built from torch's float8 decoding, not from the oracle."""
+    for ks, vs in ((0.5, 2.0), (0.125, 0.25)):
+        layer = dataclasses.replace(_layer(8, 2, 16, 4, alibi=True, window=9), kv_cache_dtype="fp8_e4m3",
+                                    k_scale=ks, v_scale=vs)
+        batch = wl.make_batch(layer, seed=1600, prefill=[(5, 4), (0, 3)], decode=[1, 7, 14])
+        pool8 = oracle_cache(batch)
+        p8, d8 = run_oracle(batch, pool8)
+        f32_layer = dataclasses.replace(batch.layer, kv_cache_dtype="auto")
+        deq = _e4m3_values(pool8.reshape(-1)).reshape(pool8.shape)
+        deq[0] *= ks
+        deq[1] *= vs
+        pool32 = deq.astype(np.float32)
+        assert np.array_equal(pool32.astype(np.float64), deq, equal_nan=True), "scaled codes must be exact in fp32"
+        p32, d32 = run_oracle(dataclasses.replace(batch, layer=f32_layer), pool32)
+        _close(p8, p32, 0.0, f"fp8 vs dequantized fp32 cache, prefill (scales {ks}, {vs})")
+        _close(d8, d32, 0.0, f"fp8 vs dequantized fp32 cache, decode (scales {ks}, {vs})")
+
+
 def _numbered_cache(nb, elems, planes=2):
     """[planes, nb, elems] fp32 cache whose every element is distinct: 1000 * plane + 10 * block + index."""
     c = np.zeros((planes, nb, elems), dtype=np.float32)
@@ -555,5 +639,6 @@ PINS = [
     pin_single_key_closed_form, pin_zero_query_mean, pin_block_relabel_invariance, pin_gqa_equals_repeated_kv,
     pin_decode_is_last_prefill_row, pin_chunked_equals_full_rows, pin_padded_decode_row, pin_bf16_inputs,
     pin_copy_blocks_map, pin_swap_blocks_map, pin_soft_cap_saturation_and_order, pin_soft_cap_known_value,
-    pin_sinks_closed_forms, pin_f16_promotion, pin_f16_inputs,
+    pin_sinks_closed_forms, pin_f16_promotion, pin_f16_inputs, pin_e4m3_code_table, pin_e4m3_quantize,
+    pin_fp8_cache_is_dequantized_cache,
 ]

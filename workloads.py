@@ -53,6 +53,13 @@ class LayerSpec:
     sliding_window: int = 0                      # <= 0: off
     logits_soft_cap: float = 0.0                 # <= 0: off (already rounded to fp32)
     sinks: Optional[np.ndarray] = None           # float32 [num_heads] sink logits
+    kv_cache_dtype: str = "auto"                 # "auto" (layer dtype) or "fp8_e4m3"
+    k_scale: float = 1.0                         # fp8 cache scales (fp32)
+    v_scale: float = 1.0
+
+    @property
+    def fp8_cache(self) -> bool:
+        return self.kv_cache_dtype == "fp8_e4m3"
 
     @property
     def torch_dtype(self):
