@@ -69,6 +69,22 @@ typedef enum pa_dtype {
 } pa_dtype;
 
 /*
+ * Element type of the paged cache (the pages' kv_cache_dtype: aphrodite-engine "xformers.py",
+ * write_to_paged_cache / forward_decode with kv_cache_dtype and kv_scale; vLLM "cpu_attn", the
+ * same calls with layer._k_scale and layer._v_scale).  The pages do not define the fp8 encoding;
+ * this library's reading: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 fraction
+ * bits, no infinities, S.1111.111 = NaN, largest finite 448).  The cache write stores for a key
+ * element x the code nearest to the fp32 quotient x / k_scale (IEEE division; ties to the even
+ * code; magnitudes of 448 and above saturate to 448; NaN stays NaN), for a value element the
+ * same with v_scale; attention reads code value * k_scale (or v_scale).  New tokens of a prefill
+ * still come from the key/value rows of the call, at full precision.
+ */
+typedef enum pa_kv_cache_dtype {
+    PA_KV_CACHE_AUTO = 0,        /* the cache holds elements of the layer dtype */
+    PA_KV_CACHE_FP8_E4M3 = 1     /* the cache holds one-byte E4M3 codes */
+} pa_kv_cache_dtype;
+
+/*
  * Geometry of one attention layer; mirrors the backend constructor of the pages
  * (num_heads, head_size, scale, num_kv_heads, alibi_slopes, sliding_window).
  *   num_heads       H, > 0
@@ -84,6 +100,9 @@ typedef enum pa_dtype {
  *   sliding_window  W; <= 0 disables the window
  *   logits_soft_cap c; <= 0 disables the soft-cap (NaN or infinity: PA_ERR_INVALID_ARGUMENT)
  *   sinks           device fp32 [H] sink logits, or NULL for none
+ *   kv_cache_dtype  PA_KV_CACHE_AUTO or PA_KV_CACHE_FP8_E4M3 (then the cache is
+ *                   [2, num_blocks, block_size * num_kv_heads * head_size] bytes)
+ *   k_scale, v_scale  fp8 cache scales: finite and > 0 (ignored for PA_KV_CACHE_AUTO)
  */
 typedef struct pa_layer {
     int32_t num_heads;
@@ -97,6 +116,9 @@ typedef struct pa_layer {
     int32_t sliding_window;
     float logits_soft_cap;
     const float *sinks;
+    int32_t kv_cache_dtype;
+    float k_scale;
+    float v_scale;
 } pa_layer;
 
 /*

@@ -28,6 +28,8 @@ PA_ERR_HIP = 4
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_DTYPE_F16 = 2
+PA_KV_CACHE_AUTO = 0
+PA_KV_CACHE_FP8_E4M3 = 1
 
 EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
             "pa_status_string", "pa_last_error_message", "pa_version")
@@ -52,6 +54,9 @@ class _CLayer(ctypes.Structure):
         ("sliding_window", ctypes.c_int32),
         ("logits_soft_cap", ctypes.c_float),
         ("sinks", ctypes.c_void_p),
+        ("kv_cache_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -114,6 +119,14 @@ class Layer:
     sliding_window: int = 0                          # <= 0: off
     logits_soft_cap: float = 0.0                     # <= 0: off
     sinks: Optional[torch.Tensor] = None             # fp32 [num_heads] sink logits on the GPU
+    kv_cache_dtype: str = "auto"                     # "auto" (the layer dtype) or "fp8_e4m3"
+    k_scale: float = 1.0                             # fp8 cache scales
+    v_scale: float = 1.0
+
+    @property
+    def cache_dtype(self) -> torch.dtype:
+        """torch dtype of the paged cache tensor (uint8 codes for an fp8 cache)."""
+        return torch.uint8 if self.kv_cache_dtype == "fp8_e4m3" else self.dtype
 
     def _c(self) -> _CLayer:
         dt = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16, torch.float16: PA_DTYPE_F16}.get(self.dtype)
@@ -125,9 +138,14 @@ class Layer:
             if t.dtype != torch.float32 or not t.is_cuda or t.numel() != self.num_heads or not t.is_contiguous():
                 raise PaError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous fp32 GPU tensor [num_heads]")
             return t.data_ptr()
+        kvd = {"auto": PA_KV_CACHE_AUTO, "fp8_e4m3": PA_KV_CACHE_FP8_E4M3}.get(self.kv_cache_dtype)
+        if kvd is None:
+            raise PaError(PA_ERR_UNSUPPORTED, f"kv_cache_dtype {self.kv_cache_dtype!r} is not supported "
+                                              "('auto', 'fp8_e4m3')")
         return _CLayer(self.num_heads, self.num_kv_heads, self.head_size, self.block_size, self.num_blocks, dt,
                        float(self.scale), heads_ptr(self.alibi_slopes, "alibi_slopes"), int(self.sliding_window or 0),
-                       float(self.logits_soft_cap or 0.0), heads_ptr(self.sinks, "sinks"))
+                       float(self.logits_soft_cap or 0.0), heads_ptr(self.sinks, "sinks"), kvd,
+                       float(self.k_scale), float(self.v_scale))
 
 
 def _stream(device: torch.device) -> int:
@@ -158,9 +176,9 @@ def _index(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape=None)
 
 def _cache(kv_cache: torch.Tensor, layer: Layer):
     want = (2, layer.num_blocks, layer.block_size * layer.num_kv_heads * layer.head_size)
-    if tuple(kv_cache.shape) != want or not kv_cache.is_contiguous() or kv_cache.dtype != layer.dtype \
+    if tuple(kv_cache.shape) != want or not kv_cache.is_contiguous() or kv_cache.dtype != layer.cache_dtype \
             or not kv_cache.is_cuda:
-        raise PaError(PA_ERR_INVALID_ARGUMENT, f"kv_cache must be a contiguous {layer.dtype} GPU tensor {want}, "
+        raise PaError(PA_ERR_INVALID_ARGUMENT, f"kv_cache must be a contiguous {layer.cache_dtype} GPU tensor {want}, "
                                                f"got {tuple(kv_cache.shape)} {kv_cache.dtype}")
     return kv_cache.data_ptr()
 
@@ -205,8 +223,10 @@ def swap_blocks(src_cache: torch.Tensor, dst_cache: torch.Tensor, block_pairs, l
     may live in (pinned) host memory; the copies go on the current stream of the GPU side."""
     elems = layer.block_size * layer.num_kv_heads * layer.head_size
     for name, t in (("src_cache", src_cache), ("dst_cache", dst_cache)):
-        if t.dim() != 3 or t.shape[0] != 2 or t.shape[2] != elems or not t.is_contiguous() or t.dtype != layer.dtype:
-            raise PaError(PA_ERR_INVALID_ARGUMENT, f"{name} must be a contiguous {layer.dtype} tensor [2, blocks, {elems}]")
+        if t.dim() != 3 or t.shape[0] != 2 or t.shape[2] != elems or not t.is_contiguous() or \
+                t.dtype != layer.cache_dtype:
+            raise PaError(PA_ERR_INVALID_ARGUMENT,
+                          f"{name} must be a contiguous {layer.cache_dtype} tensor [2, blocks, {elems}]")
     pairs = torch.as_tensor(block_pairs, dtype=torch.int64).reshape(-1, 2).contiguous()
     if pairs.is_cuda:
         raise PaError(PA_ERR_INVALID_ARGUMENT, "block_pairs must be on the host")

@@ -37,6 +37,11 @@ int log2_exact(int x) {
 
 int elt_bytes(int32_t dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
 
+bool fp8_cache(const pa_layer *L) { return L->kv_cache_dtype == PA_KV_CACHE_FP8_E4M3; }
+
+// Bytes of one element of the paged cache.
+int cache_elt_bytes(const pa_layer *L) { return fp8_cache(L) ? 1 : elt_bytes(L->dtype); }
+
 pa_status check_layer(const pa_layer *L, const char *fn) {
     if (!L) return fail(PA_ERR_INVALID_ARGUMENT, "%s: layer is NULL", fn);
     if (L->num_heads <= 0 || L->num_kv_heads <= 0)
@@ -62,6 +67,12 @@ pa_status check_layer(const pa_layer *L, const char *fn) {
     if (!(L->scale == L->scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
     if (!(L->logits_soft_cap == L->logits_soft_cap) || L->logits_soft_cap > 3.0e38f)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: logits_soft_cap must be finite", fn);
+    if (L->kv_cache_dtype != PA_KV_CACHE_AUTO && L->kv_cache_dtype != PA_KV_CACHE_FP8_E4M3)
+        return fail(PA_ERR_UNSUPPORTED, "%s: kv_cache_dtype %d is not supported (auto = 0, fp8 e4m3 = 1)", fn,
+                    L->kv_cache_dtype);
+    if (fp8_cache(L) && !(L->k_scale > 0.f && L->k_scale <= 3.0e38f && L->v_scale > 0.f && L->v_scale <= 3.0e38f))
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: fp8 cache scales must be finite and > 0 (k_scale %g, v_scale %g)",
+                    fn, double(L->k_scale), double(L->v_scale));
     return PA_OK;
 }
 
@@ -101,6 +112,7 @@ pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *val
     if (!aligned16(key) || !aligned16(value) || !aligned16(kv_cache) || (kv_row_stride * eb) % 16 != 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: key/value/kv_cache must be 16-byte aligned with 16-byte row strides",
                     fn);
+    const int cb = cache_elt_bytes(layer);
     pa::CacheWriteParams p;
     p.key = static_cast<const char *>(key);
     p.value = static_cast<const char *>(value);
@@ -109,8 +121,12 @@ pa_status pa_cache_write(const pa_layer *layer, const void *key, const void *val
     p.slot_mapping = slot_mapping;
     p.kv_cache = static_cast<char *>(kv_cache);
     p.num_slots = layer->num_blocks * layer->block_size;
-    p.row_bytes = int32_t(row * eb);
+    p.row_bytes = int32_t(row * cb);
     p.plane_bytes = p.num_slots * p.row_bytes;
+    p.fp8 = fp8_cache(layer) ? 1 : 0;
+    p.src_dtype = layer->dtype;
+    p.k_scale = layer->k_scale;
+    p.v_scale = layer->v_scale;
     hipError_t e = pa::launch_cache_write(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
@@ -133,7 +149,7 @@ pa_status pa_copy_blocks(const pa_layer *layer, void *const *kv_caches, int32_t 
     p.pairs = block_pairs;
     p.num_pairs = num_pairs;
     p.num_blocks = layer->num_blocks;
-    p.block_bytes = int64_t(layer->block_size) * layer->num_kv_heads * layer->head_size * elt_bytes(layer->dtype);
+    p.block_bytes = int64_t(layer->block_size) * layer->num_kv_heads * layer->head_size * cache_elt_bytes(layer);
     p.plane_bytes = p.num_blocks * p.block_bytes;
     hipError_t e = pa::launch_copy_blocks(p, num_layers, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -157,7 +173,7 @@ pa_status pa_swap_blocks(const pa_layer *layer, const void *src_cache, int64_t s
                         (long long)i, (long long)s, (long long)d, (long long)src_num_blocks,
                         (long long)dst_num_blocks);
     }
-    const int64_t bb = int64_t(layer->block_size) * layer->num_kv_heads * layer->head_size * elt_bytes(layer->dtype);
+    const int64_t bb = int64_t(layer->block_size) * layer->num_kv_heads * layer->head_size * cache_elt_bytes(layer);
     const char *src = static_cast<const char *>(src_cache);
     char *dst = static_cast<char *>(dst_cache);
     hipStream_t s_ = static_cast<hipStream_t>(stream);
@@ -189,6 +205,7 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     const char *fn = "pa_decode";
     pa_status st = check_layer(layer, fn);
     if (st != PA_OK) return st;
+    if (fp8_cache(layer)) return fail(PA_ERR_UNSUPPORTED, "%s: fp8 caches are not supported yet", fn);
     if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_seqs, max_seq_len and max_blocks_per_seq must be >= 0", fn);
     if (num_seqs == 0) return ok();
@@ -218,8 +235,9 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     p.query = query;
     p.q_stride = q_row_stride;
     p.k_cache = kv_cache;
-    p.v_cache = static_cast<const char *>(kv_cache) +
-                layer->num_blocks * layer->block_size * int64_t(layer->num_kv_heads) * layer->head_size * eb;
+    p.v_cache = static_cast<const char *>(kv_cache) + layer->num_blocks * layer->block_size *
+                                                          int64_t(layer->num_kv_heads) * layer->head_size *
+                                                          cache_elt_bytes(layer);
     p.block_tables = block_tables;
     p.max_blocks = max_blocks_per_seq;
     p.seq_lens = seq_lens;
@@ -252,6 +270,7 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
     const char *fn = "pa_prefill_varlen";
     pa_status st = check_layer(layer, fn);
     if (st != PA_OK) return st;
+    if (fp8_cache(layer)) return fail(PA_ERR_UNSUPPORTED, "%s: fp8 caches are not supported yet", fn);
     if (num_seqs < 0 || num_tokens < 0 || max_subquery_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: sizes must be >= 0", fn);
     if (num_seqs == 0 || num_tokens == 0) return ok();
@@ -281,7 +300,7 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
     p.kv_stride = kv_row_stride;
     p.k_cache = kv_cache;
     p.v_cache = kv_cache ? static_cast<const char *>(kv_cache) +
-                               layer->num_blocks * layer->block_size * kvrow * eb
+                               layer->num_blocks * layer->block_size * kvrow * cache_elt_bytes(layer)
                          : nullptr;
     const bool has_ctx = max_context_len > 0;
     p.block_tables = has_ctx ? block_tables : nullptr;

@@ -16,7 +16,10 @@ struct CacheWriteParams {
     char *kv_cache;           // plane 0 (K) then plane 1 (V)
     int64_t plane_bytes;      // num_blocks * block_size * row_bytes
     int64_t num_slots;        // num_blocks * block_size
-    int32_t row_bytes;        // num_kv_heads * head_size * elt, multiple of 16
+    int32_t row_bytes;        // cache row: num_kv_heads * head_size * cache element bytes, multiple of 8
+    int32_t fp8;              // 1: quantize to FP8 E4M3 codes (cache element = 1 byte)
+    int32_t src_dtype;        // element type of key/value (pa_dtype) when quantizing
+    float k_scale, v_scale;   // quantization scales (fp8 only)
 };
 hipError_t launch_cache_write(const CacheWriteParams &p, hipStream_t stream);
 

@@ -32,13 +32,15 @@ def player(layer: wl.LayerSpec, dev=None):
     heads = lambda a: torch.tensor(a, dtype=torch.float32, device=dev) if a is not None else None
     return pa().Layer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size, layer.num_blocks,
                       layer.torch_dtype, layer.scale, heads(layer.alibi_slopes), layer.sliding_window,
-                      layer.logits_soft_cap, heads(layer.sinks))
+                      layer.logits_soft_cap, heads(layer.sinks), layer.kv_cache_dtype, layer.k_scale, layer.v_scale)
 
 
 def olayer(layer: wl.LayerSpec) -> oracle.OracleLayer:
     return oracle.OracleLayer(layer.num_heads, layer.num_kv_heads, layer.head_size, layer.block_size,
                               layer.num_blocks, ORACLE_DTYPE[layer.dtype], layer.scale, layer.alibi_slopes,
-                              layer.sliding_window, layer.logits_soft_cap, layer.sinks)
+                              layer.sliding_window, layer.logits_soft_cap, layer.sinks,
+                              oracle.KV_CACHE_FP8_E4M3 if layer.fp8_cache else oracle.KV_CACHE_AUTO,
+                              layer.k_scale, layer.v_scale)
 
 
 def i32(a, dev=None):
@@ -54,7 +56,11 @@ def gpu_pool(batch: wl.PagedBatch, pl=None) -> torch.Tensor:
     L = batch.layer
     pl = pl or player(L)
     dev = batch.query.device
-    cache = torch.full((2, L.num_blocks, L.block_size * L.row_elems), float("nan"), dtype=L.torch_dtype, device=dev)
+    shape = (2, L.num_blocks, L.block_size * L.row_elems)
+    if L.fp8_cache:
+        cache = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)      # the E4M3 NaN code
+    else:
+        cache = torch.full(shape, float("nan"), dtype=L.torch_dtype, device=dev)
     if batch.ctx_key.shape[0]:
         pa().cache_write(batch.ctx_key, batch.ctx_value, cache, i64(batch.ctx_slots, dev), pl)
     pa().cache_write(batch.key, batch.value, cache, i64(batch.slot_mapping, dev), pl)
@@ -97,10 +103,12 @@ def oracle_pool(batch: wl.PagedBatch, prefill_seqs: Optional[Iterable[int]] = No
     L = batch.layer
     ol = olayer(L)
     shape = (2, L.num_blocks, L.block_size * L.row_elems)
-    et = np.float32 if L.dtype == wl.F32 else np.uint16
+    et = np.uint8 if L.fp8_cache else (np.float32 if L.dtype == wl.F32 else np.uint16)
     subset = prefill_seqs is not None or decode_seqs is not None
     if subset or not fill_nan:
         pool = np.zeros(shape, dtype=et)
+    elif L.fp8_cache:
+        pool = np.full(shape, 0x7F, dtype=et)
     else:
         pool = np.full(shape, np.nan if et == np.float32 else (NAN_F16 if L.dtype == wl.F16 else NAN_BF16), dtype=et)
     off = ctx_offsets(batch)

@@ -44,7 +44,8 @@ def test_version_and_status_strings(pa):
 
 def _layer(pa, **kw):
     base = dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=4, dtype=1, scale=0.1,
-                alibi_slopes=None, sliding_window=0, logits_soft_cap=0.0, sinks=None)
+                alibi_slopes=None, sliding_window=0, logits_soft_cap=0.0, sinks=None, kv_cache_dtype=0, k_scale=1.0,
+                v_scale=1.0)
     base.update(kw)
     return pa._CLayer(*base.values())
 
@@ -58,6 +59,9 @@ def _layer(pa, **kw):
     (dict(num_blocks=0), 1, "num_blocks"),
     (dict(logits_soft_cap=float("nan")), 1, "logits_soft_cap"),
     (dict(logits_soft_cap=float("inf")), 1, "logits_soft_cap"),
+    (dict(kv_cache_dtype=5), 2, "kv_cache_dtype 5"),
+    (dict(kv_cache_dtype=1, k_scale=0.0), 1, "scales"),
+    (dict(kv_cache_dtype=1, v_scale=float("nan")), 1, "scales"),
 ])
 def test_layer_validation(pa, kw, status, needle):
     lib = pa.library()

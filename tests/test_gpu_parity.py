@@ -62,6 +62,27 @@ def test_cache_write_bit_exact(H, Hkv, D, bs, dtype):
     assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype,k_scale,v_scale", [(wl.BF16, 1.0, 1.0), (wl.BF16, 0.0371, 0.0029), (wl.F16, 0.5, 3.0),
+                                                   (wl.F32, 0.013, 0.21)])
+def test_cache_write_fp8_bit_exact(dtype, k_scale, v_scale):
+    """Quantizing cache write into an fp8 (E4M3) cache: every code equals the oracle's, including
+    saturated codes (small scales push many quotients past 448) and special values."""
+    layer = dataclasses.replace(_layer(16, 4, 128, 16, dtype), kv_cache_dtype="fp8_e4m3",
+                                k_scale=wl.fp32(k_scale), v_scale=wl.fp32(v_scale))
+    batch = wl.make_batch(layer, seed=33, prefill=[(3, 5), (0, 40)], decode=[1, 17, 0, 35], device=gh.device())
+    specials = torch.tensor([float("nan"), float("inf"), -float("inf"), 0.0, -0.0, 1e30, -1e-30, 448.0, 464.0],
+                            dtype=torch.float32).to(batch.key.dtype).to(gh.device())
+    batch.key[0, :specials.numel()] = specials
+    batch.value[1, -specials.numel():] = specials
+    _say(f"fp8 cache write {dtype} scales {k_scale} {v_scale}")
+    cache = gh.gpu_pool(batch)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    got = cache.cpu().numpy()
+    bad = np.argwhere(got != pool)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0].tolist()}: {got[tuple(bad[0])]:#x} vs {pool[tuple(bad[0])]:#x}"
+
+
 def test_cache_write_strided_rows_and_padding():
     """key/value as column slices of a wider [T, 3 * Hkv * D] tensor; slot -1 rows are skipped."""
     layer = _layer(8, 2, 128, 16)
