@@ -34,6 +34,8 @@
 // multiply V, fp32 accumulation, output rounded to nearest even.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -131,6 +133,10 @@ template <>
 __device__ __forceinline__ void store_out<bf16_t>(bf16_t *dst, float v) { *dst = f32_to_bf16(v); }
 template <>
 __device__ __forceinline__ void store_out<f16_t>(f16_t *dst, float v) { *dst = f32_to_f16(v); }
+template <>
+__device__ __forceinline__ void store_out<bf16_c8_t>(bf16_c8_t *dst, float v) { *dst = to_elt<bf16_c8_t>(v); }
+template <>
+__device__ __forceinline__ void store_out<f16_c8_t>(f16_c8_t *dst, float v) { *dst = to_elt<f16_c8_t>(v); }
 
 // Partial dot products of one 16-byte row chunk with GP query chunks.
 template <typename T, int GP>
@@ -350,7 +356,15 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     const int nh = shape.heads_per_group;
     const int ups = shape.units_per_seq;
     const int bmask = (1 << p.block_shift) - 1;
-    const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * sizeof(T);           // one token, all heads
+    // cache bytes per element: one for an FP8 cache (each lane then loads 8 codes, 8 bytes, and
+    // widens them to the same four 16-bit pairs a bf16 / fp16 cache delivers)
+    constexpr int CB = kFp8Cache<T> ? 1 : int(sizeof(T));
+    typedef typename std::conditional<kFp8Cache<T>, uint2, uint4>::type LoadT;
+    auto widen = [](const LoadT &x) -> uint4 {
+        if constexpr (kFp8Cache<T>) return widen_e4m3<T>(x);
+        else return x;
+    };
+    const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * CB;                   // one token, all heads
     const int64_t block_bytes = int64_t(row_bytes) << p.block_shift;
     const char *kcache = reinterpret_cast<const char *>(p.k_cache);
     const char *vcache = reinterpret_cast<const char *>(p.v_cache);
@@ -404,7 +418,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
         const int kfirst = (lo / TILE + tile0) * TILE;
         const int kend = min(L, (lo / TILE + tile1) * TILE);
         // Lane part of every K/V address: row group r's token inside the instruction, KV head g, chunk c.
-        const uint32_t lane_off = uint32_t(tr) * row_bytes + (uint32_t(g) * D + c * EPL) * sizeof(T);
+        const uint32_t lane_off = uint32_t(tr) * row_bytes + (uint32_t(g) * D + c * EPL) * CB;
 
         float m_run = -INFINITY;      // head my_head, this row group
         float l_run = 0.f;            // sum of rounded weights, head my_head, this row group
@@ -414,12 +428,12 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 
-        auto scores = [&](int tb, const uint4 (&kr)[NI], float (&sc)[NI]) {
+        auto scores = [&](int tb, const LoadT (&kr)[NI], float (&sc)[NI]) {
             const bool edge = tb < lo || tb + TILE - 1 > pos;           // uniform
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 float part_dot[GP];
-                chunk_dots<T, GP>(kr[i], q, part_dot);
+                chunk_dots<T, GP>(widen(kr[i]), q, part_dot);
                 butterfly<C, GP, 0>(part_dot);
                 sc[i] = part_dot[0] * qk_scale;
             }
@@ -439,7 +453,10 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
                 }
             }
         };
-        auto softmax_pv = [&](int tb, const float (&sc)[NI], uint4 (&vr)[NI]) {
+        auto softmax_pv = [&](int tb, const float (&sc)[NI], const LoadT (&vraw)[NI]) {
+            uint4 vr[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vr[i] = widen(vraw[i]);
             // Lazily raised max: rescale only when some tile max exceeds the running max by more
             // than kRescaleSlack (always on the first tile, rarely afterwards); uniform over the wave.
             float tmax = sc[0];
@@ -555,18 +572,18 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
                     return 0;
                 }
             };
-            auto load_rows = [&](const char *cache, int tb, uint4 (&x)[NI]) {
+            auto load_rows = [&](const char *cache, int tb, LoadT (&x)[NI]) {
                 const int blk = tile_block(tb);
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
-                    x[i] = *reinterpret_cast<const uint4 *>(cache + inst_base(tb, i, blk) + lane_off);
+                    x[i] = *reinterpret_cast<const LoadT *>(cache + inst_base(tb, i, blk) + lane_off);
             };
             // DEPTH register sets in a ring: while tile t is scored and summed from set t % DEPTH,
             // tiles t + 1 .. t + DEPTH - 1 are in flight.  Loads past the chunk's last tile
             // re-read it (cache hits), keeping every load unconditional.
             const int tfirst = max(kfirst, ch * shape.chunk);
             const int tlast = ((cend - 1) / TILE) * TILE;
-            uint4 kr[DEPTH][NI], vr[DEPTH][NI];
+            LoadT kr[DEPTH][NI], vr[DEPTH][NI];
 #pragma unroll
             for (int d = 0; d < DEPTH - 1; ++d) {
                 const int tt = min(tfirst + d * TILE, tlast);
@@ -614,7 +631,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
                 if (tr == 0 && h < nh) {
                     // a sink logit joins the denominator only
                     if (p.sinks) lh += fast_exp2(p.sinks[head0 + h] * kLog2e - mh);
-                    const float inv = 1.f / lh;
+                    const float inv = p.out_scale / lh;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) store_out<T>(out_row + h * D + c * EPL + e, acc[h][e] * inv);
                 }
@@ -727,7 +744,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
     if (p.sinks) den += fast_exp2(p.sinks[head] * kLog2e - M);
-    const float inv = 1.f / den;
+    const float inv = p.out_scale / den;
 #pragma unroll
     for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] * inv);
 }
@@ -857,7 +874,13 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     // Block-id chunk: 128 blocks (two id registers per lane), at most 4096 keys.
     plan.chunk = (128 << block_shift) < 4096 ? (128 << block_shift) : 4096;
     int kvh = 1, tile = 32, waves = 2048;
-    if (dtype == 1) {
+    if (dtype == 3) {
+        if (head_size == 128) instance_info<bf16_c8_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+        else instance_info<bf16_c8_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+    } else if (dtype == 4) {
+        if (head_size == 128) instance_info<f16_c8_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+        else instance_info<f16_c8_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
+    } else if (dtype == 1) {
         if (head_size == 128) instance_info<bf16_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
         else instance_info<bf16_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
     } else if (dtype == 2) {
@@ -896,7 +919,13 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
     s.tile = plan.tile;
     s.max_len = p.max_seq_len;
     s.kvh = plan.kv_per_unit;
-    if (dtype == 1) {
+    if (dtype == 3) {
+        if (head_size == 128) return launch_group<bf16_c8_t, 128>(p, s, plan.padded_group, stream);
+        if (head_size == 64) return launch_group<bf16_c8_t, 64>(p, s, plan.padded_group, stream);
+    } else if (dtype == 4) {
+        if (head_size == 128) return launch_group<f16_c8_t, 128>(p, s, plan.padded_group, stream);
+        if (head_size == 64) return launch_group<f16_c8_t, 64>(p, s, plan.padded_group, stream);
+    } else if (dtype == 1) {
         if (head_size == 128) return launch_group<bf16_t, 128>(p, s, plan.padded_group, stream);
         if (head_size == 64) return launch_group<bf16_t, 64>(p, s, plan.padded_group, stream);
     } else if (dtype == 2) {

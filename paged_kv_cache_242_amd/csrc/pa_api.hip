@@ -42,6 +42,9 @@ bool fp8_cache(const pa_layer *L) { return L->kv_cache_dtype == PA_KV_CACHE_FP8_
 // Bytes of one element of the paged cache.
 int cache_elt_bytes(const pa_layer *L) { return fp8_cache(L) ? 1 : elt_bytes(L->dtype); }
 
+// Kernel element code: the dtype, or 3 / 4 for bf16 / fp16 layers with an FP8 cache.
+int kernel_dtype(const pa_layer *L) { return fp8_cache(L) ? L->dtype + 2 : L->dtype; }
+
 pa_status check_layer(const pa_layer *L, const char *fn) {
     if (!L) return fail(PA_ERR_INVALID_ARGUMENT, "%s: layer is NULL", fn);
     if (L->num_heads <= 0 || L->num_kv_heads <= 0)
@@ -194,7 +197,7 @@ pa_status pa_swap_blocks(const pa_layer *layer, const void *src_cache, int64_t s
 
 size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len) {
     if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0) return 0;
-    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, layer->dtype,
+    return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, kernel_dtype(layer),
                            num_seqs, max_seq_len)
         .workspace_bytes;
 }
@@ -205,7 +208,8 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     const char *fn = "pa_decode";
     pa_status st = check_layer(layer, fn);
     if (st != PA_OK) return st;
-    if (fp8_cache(layer)) return fail(PA_ERR_UNSUPPORTED, "%s: fp8 caches are not supported yet", fn);
+    if (fp8_cache(layer) && layer->dtype == PA_DTYPE_F32)
+        return fail(PA_ERR_UNSUPPORTED, "%s: an fp8 cache needs a bf16 or fp16 layer", fn);
     if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_seqs, max_seq_len and max_blocks_per_seq must be >= 0", fn);
     if (num_seqs == 0) return ok();
@@ -222,7 +226,7 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: out/query/kv_cache must be 16-byte aligned with 16-byte row strides",
                     fn);
     const pa::DecodePlan plan = pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size,
-                                                layer->block_size, layer->dtype, num_seqs, max_seq_len);
+                                                layer->block_size, kernel_dtype(layer), num_seqs, max_seq_len);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes)
             return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", fn, plan.workspace_bytes,
@@ -246,7 +250,9 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     p.num_kv_heads = layer->num_kv_heads;
     p.block_shift = log2_exact(layer->block_size);
     p.num_blocks = layer->num_blocks;
-    p.scale = layer->scale;
+    // an FP8 cache's k_scale folds into the score scale, its v_scale into the output
+    p.scale = fp8_cache(layer) ? layer->scale * layer->k_scale : layer->scale;
+    p.out_scale = fp8_cache(layer) ? layer->v_scale : 1.f;
     p.alibi_slopes = layer->alibi_slopes;
     p.window = layer->sliding_window;
     p.softcap = layer->logits_soft_cap > 0.f ? layer->logits_soft_cap : 0.f;
@@ -257,7 +263,7 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     p.ws_wseq = reinterpret_cast<int32_t *>(ws + plan.ws_wseq_off);
     p.ws_acc = reinterpret_cast<float *>(ws + plan.ws_acc_off);
     p.ws_ml = reinterpret_cast<float *>(ws + plan.ws_ml_off);
-    hipError_t e = pa::launch_decode(p, plan, layer->dtype, layer->head_size, static_cast<hipStream_t>(stream));
+    hipError_t e = pa::launch_decode(p, plan, kernel_dtype(layer), layer->head_size, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }

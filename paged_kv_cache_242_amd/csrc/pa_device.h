@@ -86,6 +86,40 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     else return dot2_bf16(a, b, c);
 }
 
+// Query / output element types (bf16, fp16) of layers whose paged cache holds FP8 E4M3 codes: the
+// kernels take them as their element type and read the cache as one byte per element.
+enum class bf16_c8_t : uint16_t {};
+enum class f16_c8_t : uint16_t {};
+template <>
+inline constexpr bool kIsF16<f16_c8_t> = true;
+template <typename T>
+inline constexpr bool kFp8Cache = false;
+template <>
+inline constexpr bool kFp8Cache<bf16_c8_t> = true;
+template <>
+inline constexpr bool kFp8Cache<f16_c8_t> = true;
+template <>
+__device__ __forceinline__ bf16_c8_t to_elt<bf16_c8_t>(float x) { return bf16_c8_t(f32_to_bf16(x)); }
+template <>
+__device__ __forceinline__ f16_c8_t to_elt<f16_c8_t>(float x) { return f16_c8_t(uint16_t(f32_to_f16(x))); }
+__device__ __forceinline__ float elt_to_f32(bf16_c8_t x) { return bf16_to_f32(uint16_t(x)); }
+__device__ __forceinline__ float elt_to_f32(f16_c8_t x) { return f16_to_f32(f16_t(uint16_t(x))); }
+
+// Eight E4M3 codes (bytes 0..7 of c) -> four pairs of the 16-bit type T (element 2k in the low
+// half of word k), exactly: every E4M3 value is representable in bf16 and in fp16.
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t widen_e4m3_pair(uint32_t src) {
+    if constexpr (kIsF16<T>)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.f, HI));
+}
+template <typename T>
+__device__ __forceinline__ uint4 widen_e4m3(uint2 c) {
+    return make_uint4(widen_e4m3_pair<T, false>(c.x), widen_e4m3_pair<T, true>(c.x), widen_e4m3_pair<T, false>(c.y),
+                      widen_e4m3_pair<T, true>(c.y));
+}
+
 // Byte permute: result byte k = byte sel[k] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);

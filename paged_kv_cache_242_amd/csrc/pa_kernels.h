@@ -46,6 +46,8 @@ struct DecodePlan {
     size_t ws_prefix_off, ws_wseq_off, ws_acc_off, ws_ml_off;   // workspace layout (bytes)
     size_t workspace_bytes;
 };
+// Kernel element codes (the `dtype` of plan_decode / launch_decode / launch_prefill): 0 fp32,
+// 1 bf16, 2 fp16, 3 bf16 with an FP8 E4M3 cache, 4 fp16 with an FP8 E4M3 cache.
 DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                        int32_t dtype, int32_t num_seqs, int32_t max_seq_len);
 
@@ -69,6 +71,7 @@ struct DecodeParams {
     int32_t window;
     float softcap;            // <= 0: off
     const float *sinks;       // [H] natural-log sink logits, or null
+    float out_scale;          // multiplies the normalized output (an FP8 cache's v_scale, else 1)
     int64_t *ws_prefix;       // [B + 1] tiles of the work units of sequences before q
     int32_t *ws_wseq;         // [num_waves] sequence of each wavefront's first tile
     float *ws_acc;            // [slots, D] partial weighted V

@@ -24,10 +24,14 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _layer(H, Hkv, D, bs, dtype=wl.BF16, alibi=False, window=0, scale=None, softcap=0.0, sinks=False):
+def _layer(H, Hkv, D, bs, dtype=wl.BF16, alibi=False, window=0, scale=None, softcap=0.0, sinks=False, fp8=False):
+    """fp8=True: an FP8 E4M3 cache with k_scale 0.02 and v_scale 0.015 (N(0, 1) rows then use
+    codes up to about 250, well inside the format's range)."""
     return wl.LayerSpec(H, Hkv, D, bs, 0, dtype, wl.fp32(scale if scale is not None else 1.0 / math.sqrt(D)),
                         alibi_slopes=wl.alibi_slopes_geometric(H) if alibi else None, sliding_window=window,
-                        logits_soft_cap=wl.fp32(softcap), sinks=wl.sink_logits(H, seed=H + D) if sinks else None)
+                        logits_soft_cap=wl.fp32(softcap), sinks=wl.sink_logits(H, seed=H + D) if sinks else None,
+                        kv_cache_dtype="fp8_e4m3" if fp8 else "auto", k_scale=wl.fp32(0.02) if fp8 else 1.0,
+                        v_scale=wl.fp32(0.015) if fp8 else 1.0)
 
 
 def _check_full(batch, what):
@@ -193,6 +197,12 @@ DECODE_LAYERS = [
     _layer(64, 8, 128, 32, wl.F16, sinks=True),
     _layer(32, 32, 128, 16, wl.F16, alibi=True, window=100),
     _layer(16, 2, 64, 8, wl.F16, softcap=3.0, scale=0.3),
+    # fp8 (E4M3) cache
+    _layer(32, 8, 128, 16, fp8=True),
+    _layer(64, 8, 128, 32, fp8=True, sinks=True),
+    _layer(32, 32, 128, 16, wl.F16, fp8=True, alibi=True, window=100),
+    _layer(16, 2, 64, 8, fp8=True, softcap=3.0, scale=0.3),
+    _layer(12, 2, 128, 64, wl.F16, fp8=True),
 ]
 DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
 

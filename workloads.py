@@ -288,10 +288,10 @@ def workload(k: int) -> Workload:
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:
-    """Exact bytes of a tensor as numpy (bf16, fp16 -> uint16 bit patterns, fp32 -> float32)."""
+    """Exact bytes of a tensor as numpy (bf16, fp16 -> uint16 bit patterns, fp32 -> float32, uint8 codes)."""
     t = t.detach().to("cpu").contiguous()
     if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.uint8):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
