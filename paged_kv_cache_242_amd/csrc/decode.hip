@@ -187,16 +187,43 @@ __device__ __forceinline__ void chunk_dots(const uint4 &k, const uint32_t (&q)[G
 #ifndef PA_DECODE_OCC_B
 #define PA_DECODE_OCC_B 1
 #endif
+// FP8 caches: each load instruction carries half the bytes (8 codes per lane), so the tile
+// shapes are set separately to keep enough bytes in flight.
+#ifndef PA_DECODE_NI_S8
+#define PA_DECODE_NI_S8 8
+#endif
+#ifndef PA_DECODE_NI_M8
+#define PA_DECODE_NI_M8 8
+#endif
+#ifndef PA_DECODE_NI_B8
+#define PA_DECODE_NI_B8 4
+#endif
+#ifndef PA_DECODE_DEPTH_S8
+#define PA_DECODE_DEPTH_S8 3
+#endif
+#ifndef PA_DECODE_DEPTH_M8
+#define PA_DECODE_DEPTH_M8 3
+#endif
+#ifndef PA_DECODE_DEPTH_B8
+#define PA_DECODE_DEPTH_B8 3
+#endif
 template <typename T, int GP>
 constexpr int tile_loads() {
+    if constexpr (kFp8Cache<T>) return GP <= 2 ? PA_DECODE_NI_S8 : (GP == 4 ? PA_DECODE_NI_M8 : PA_DECODE_NI_B8);
     return sizeof(T) == 4 ? 4 : (GP <= 2 ? PA_DECODE_NI_S : (GP == 4 ? PA_DECODE_NI_M : PA_DECODE_NI_B));
 }
 template <typename T, int GP>
 constexpr int tile_depth() {
+    if constexpr (kFp8Cache<T>)
+        return GP <= 2 ? PA_DECODE_DEPTH_S8 : (GP == 4 ? PA_DECODE_DEPTH_M8 : PA_DECODE_DEPTH_B8);
     return sizeof(T) == 4 ? 2 : (GP <= 2 ? PA_DECODE_DEPTH_S : (GP == 4 ? PA_DECODE_DEPTH_M : PA_DECODE_DEPTH_B));
 }
+#ifndef PA_DECODE_OCC_B8
+#define PA_DECODE_OCC_B8 2
+#endif
 template <typename T, int GP>
 constexpr int tile_occ() {
+    if constexpr (kFp8Cache<T>) return GP <= 2 ? PA_DECODE_OCC_S : (GP == 4 ? PA_DECODE_OCC_M : PA_DECODE_OCC_B8);
     return sizeof(T) == 4 ? 2 : (GP <= 2 ? PA_DECODE_OCC_S : (GP == 4 ? PA_DECODE_OCC_M : PA_DECODE_OCC_B));
 }
 

@@ -276,7 +276,8 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
     const char *fn = "pa_prefill_varlen";
     pa_status st = check_layer(layer, fn);
     if (st != PA_OK) return st;
-    if (fp8_cache(layer)) return fail(PA_ERR_UNSUPPORTED, "%s: fp8 caches are not supported yet", fn);
+    if (fp8_cache(layer) && layer->dtype == PA_DTYPE_F32)
+        return fail(PA_ERR_UNSUPPORTED, "%s: an fp8 cache needs a bf16 or fp16 layer", fn);
     if (num_seqs < 0 || num_tokens < 0 || max_subquery_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: sizes must be >= 0", fn);
     if (num_seqs == 0 || num_tokens == 0) return ok();
@@ -326,7 +327,9 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
     p.sinks = layer->sinks;
     p.max_subquery_len = max_subquery_len;
     p.max_context_len = max_context_len;
-    hipError_t e = pa::launch_prefill(p, layer->dtype, layer->head_size, static_cast<hipStream_t>(stream));
+    p.k_scale = layer->k_scale;
+    p.v_scale = layer->v_scale;
+    hipError_t e = pa::launch_prefill(p, kernel_dtype(layer), layer->head_size, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }

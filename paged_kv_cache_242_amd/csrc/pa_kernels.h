@@ -106,6 +106,7 @@ struct PrefillParams {
     const float *sinks;       // [H] natural-log sink logits, or null
     int32_t max_subquery_len;
     int32_t max_context_len;
+    float k_scale, v_scale;   // FP8 cache scales (element types 3 and 4)
 };
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipStream_t stream);
 

@@ -166,6 +166,8 @@ template <typename T>
 struct Operand8 { typedef bf16x8_v type; };   // 8 elements of an MFMA operand
 template <>
 struct Operand8<f16_t> { typedef halfx8_v type; };
+template <>
+struct Operand8<f16_c8_t> { typedef halfx8_v type; };
 
 __device__ __forceinline__ floatx4_v mfma16(bf16x8_v a, bf16x8_v b, floatx4_v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -329,6 +331,72 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
         }
         return id;
     };
+    // ---- FP8 cache (element types with kFp8Cache): cached rows cannot go through the load-to-LDS
+    // path, which copies bytes unchanged.  Each lane instead loads 16 codes of a row (one 16-byte
+    // load per slot, slot s = lane + 64 j: tile row 16 w + s / (D / 16), codes 16 (s % (D / 16)) ..
+    // + 15) for K and for V when the tile's copies are issued, and a tile later, when they have
+    // long arrived, turns them into code * scale in the element type and writes them into the
+    // same swizzled places the copies would have filled.  New-token rows still use the copies.
+    constexpr bool C8 = kFp8Cache<T>;
+    constexpr int NS8 = C8 ? D / 64 : 1;    // slots per lane per operand and tile
+    constexpr int SPR8 = D / 16;            // slots per row
+    uint4 raw8[2][NS8];
+    uint32_t raw8_mask = 0;                 // bit j: slot j holds codes to write
+    const int64_t row8 = int64_t(p.num_kv_heads) * D;          // bytes per cached token (all heads)
+    const int64_t block8 = row8 << p.block_shift;
+    auto fp8_issue = [&](int kt, int id0, int id1) __attribute__((always_inline)) {
+        const int w0 = kt * kBN + wrow0;
+        raw8_mask = 0;
+#pragma unroll
+        for (int j = 0; j < NS8; ++j) {
+            const int sl = lane + 64 * j, r = sl / SPR8, m = sl % SPR8;
+            const int key = w0 + r;
+            if (key < si.c) {
+                const int64_t blk = clamp_block(((key >> p.block_shift) == (w0 >> p.block_shift)) ? id0 : id1);
+                const int64_t off = blk * block8 + int64_t(key & bmask) * row8 + int64_t(g) * D + 16 * m;
+                raw8[0][j] = *reinterpret_cast<const uint4 *>(kc_bytes + off);
+                raw8[1][j] = *reinterpret_cast<const uint4 *>(vc_bytes + off);
+                raw8_mask |= 1u << j;
+            }
+        }
+    };
+    auto fp8_commit = [&](bf16_t *kdst, bf16_t *vdst) __attribute__((always_inline)) {
+        if constexpr (C8) {
+#pragma unroll
+            for (int j = 0; j < NS8; ++j) {
+                if ((raw8_mask >> j) & 1u) {
+                    const int sl = lane + 64 * j, r = sl / SPR8, m = sl % SPR8;
+                    const int rr = wrow0 + r;
+#pragma unroll
+                    for (int o = 0; o < 2; ++o) {
+                        const float sc = o ? p.v_scale : p.k_scale;
+                        const uint32_t cw[4] = {raw8[o][j].x, raw8[o][j].y, raw8[o][j].z, raw8[o][j].w};
+                        uint32_t w[8];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw[q]), false);
+                            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw[q]), true);
+                            w[2 * q] = pack_x2<T>(lo[0] * sc, lo[1] * sc);
+                            w[2 * q + 1] = pack_x2<T>(hi[0] * sc, hi[1] * sc);
+                        }
+                        int off0, off1;
+                        if (o == 0) {                       // K: 16-byte chunk c of row rr at c ^ (rr % CH)
+                            off0 = rr * D + (((2 * m) ^ (rr % CH)) << 3);
+                            off1 = rr * D + (((2 * m + 1) ^ (rr % CH)) << 3);
+                        } else {                            // V: 32-byte unit u of row rr at u ^ vswz(rr)
+                            off0 = rr * D + ((m ^ vswz<D>(rr)) << 4);
+                            off1 = off0 + 8;
+                        }
+                        bf16_t *dst = o ? vdst : kdst;
+                        *reinterpret_cast<uint4 *>(dst + off0) = make_uint4(w[0], w[1], w[2], w[3]);
+                        *reinterpret_cast<uint4 *>(dst + off1) = make_uint4(w[4], w[5], w[6], w[7]);
+                    }
+                }
+            }
+            raw8_mask = 0;
+        }
+    };
+
     // Copy this wavefront's 16 rows of tile kt into (kdst, vdst); id0 / id1 are the blocks of its
     // first and last cached row (wave-uniform).  The rows are all cached, all new and at or below
     // key_hi (one descriptor per block, scalar offsets per instruction), or -- at most twice per
@@ -338,7 +406,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
         const int w0 = kt * kBN + wrow0;                  // first key of this wavefront (uniform)
         int lrow, pc;
         lane_terms(lrow, pc);
-        if (w0 + 15 < si.c) {
+        if constexpr (C8) {
+            if (w0 < si.c) fp8_issue(kt, id0_raw, id1_raw);
+            if (w0 + 15 < si.c) return;                   // all cached: nothing for the copies
+        }
+        if (!C8 && w0 + 15 < si.c) {
             const int64_t off0 = clamp_block(id0_raw) * block_bytes + head_off + int64_t(w0 & bmask) * cache_row_bytes;
             const int64_t off1 = clamp_block(id1_raw) * block_bytes + head_off;
             const uint32_t lro = uint32_t(lrow) * uint32_t(cache_row_bytes);
@@ -372,7 +444,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
                 bf16_t *kd = kdst + (NJ * wave + j) * 512;
                 bf16_t *vd = vdst + (NJ * wave + j) * 512;
                 // (a branch rather than a select of the two bases keeps the bases in scalar registers)
-                if (cached) {
+                if (C8 && cached) {
+                    // an FP8 cache row: written by fp8_commit
+                } else if (cached) {
                     dma16_lane(kc_bytes + off + k_chunk(lrow, pc, j), kd);
                     dma16_lane(vc_bytes + off + v_chunk(lrow, pc, j), vd);
                 } else {
@@ -597,6 +671,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
     }
     int ids = kt_hi > kt_lo ? fetch_ids(kt_hi - 1) : 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wavefront's copies, ids and Q landed
+    fp8_commit(Ks0, Vs0);
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk)
 #pragma unroll
@@ -610,6 +685,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
         }
         compute_tile(kt, Ks0, Vs0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        fp8_commit(Ks1, Vs1);
         asm volatile("" : "+v"(ids));
         __syncthreads();
         if (kt - 1 < kt_lo) break;
@@ -619,6 +695,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
         }
         compute_tile(kt - 1, Ks1, Vs1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        fp8_commit(Ks0, Vs0);
         asm volatile("" : "+v"(ids));
         __syncthreads();
     }
@@ -758,6 +835,8 @@ hipError_t launch_mfma(const PrefillParams &p, int head_size, hipStream_t stream
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipStream_t stream) {
     if (dtype == 1) return launch_mfma<bf16_t>(p, head_size, stream);
     if (dtype == 2) return launch_mfma<f16_t>(p, head_size, stream);
+    if (dtype == 3) return launch_mfma<bf16_c8_t>(p, head_size, stream);
+    if (dtype == 4) return launch_mfma<f16_c8_t>(p, head_size, stream);
     const int64_t blocks = p.num_tokens * p.num_heads;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

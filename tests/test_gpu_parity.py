@@ -285,6 +285,11 @@ PREFILL_LAYERS = [
     _layer(8, 2, 64, 32, wl.F16, sinks=True),
     _layer(8, 4, 128, 16, wl.F16, alibi=True, softcap=4.0, scale=0.25),
     _layer(8, 2, 128, 16, wl.F16, scale=-0.09),
+    # fp8 (E4M3) cache: cached rows dequantized into the tiles, new rows at full precision
+    _layer(32, 8, 128, 16, fp8=True),
+    _layer(32, 32, 128, 16, wl.F16, fp8=True, alibi=True, window=100),
+    _layer(8, 2, 64, 8, fp8=True, sinks=True),
+    _layer(8, 4, 128, 32, fp8=True, softcap=4.0, scale=0.25),
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
@@ -311,11 +316,12 @@ def test_prefill_without_context_arguments():
     gh.assert_close(gh.to_f64(out), ref, batch.layer, "context-free prefill")
 
 
-def test_mixed_batch_small():
-    layer = _layer(16, 4, 128, 16, alibi=True, window=200)
+@pytest.mark.parametrize("fp8", [False, True])
+def test_mixed_batch_small(fp8):
+    layer = _layer(16, 4, 128, 16, alibi=True, window=200, fp8=fp8)
     batch = wl.make_batch(layer, seed=71, prefill=[(100, 150), (0, 90), (333, 1)], decode=[1, 250, 700, 0],
                           device=gh.device())
-    _check_full(batch, "mixed small")
+    _check_full(batch, f"mixed small{' fp8' if fp8 else ''}")
 
 
 @pytest.mark.parametrize("k,layer", [(4, _layer(32, 8, 128, 16)), (2, _layer(8, 8, 64, 32, alibi=True, window=500))])
