@@ -75,6 +75,9 @@ def _load():
         lib.orc_decode.argtypes = [ctypes.POINTER(_Layer), P, P, ctypes.c_int64, P, P, ctypes.c_int32,
                                    P, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         lib.orc_decode.restype = ctypes.c_int
+        lib.orc_decode_multi.argtypes = [ctypes.POINTER(_Layer), P, P, ctypes.c_int64, P, P, ctypes.c_int32,
+                                         P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        lib.orc_decode_multi.restype = ctypes.c_int
         lib.orc_prefill.argtypes = [ctypes.POINTER(_Layer), P, P, ctypes.c_int64, P, P, ctypes.c_int64, P,
                                     P, ctypes.c_int32, P, P, ctypes.c_int32, P, ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_int)]
@@ -205,6 +208,26 @@ def decode(layer: OracleLayer, query: np.ndarray, kv_cache: np.ndarray, block_ta
                             num_threads, ctypes.byref(used))
     _check(st, "decode")
     return (out, used.value) if return_threads else out
+
+
+def decode_multi(layer: OracleLayer, query: np.ndarray, kv_cache: np.ndarray, block_tables: np.ndarray,
+                 seq_lens: np.ndarray, query_len: int, num_threads: int = 0):
+    """fp64 [B * query_len, H, D] multi-token decode output (see ``orc_decode_multi``)."""
+    et = _elt_dtype(layer)
+    assert query.dtype == et and kv_cache.dtype == cache_dtype(layer) and kv_cache.flags.c_contiguous
+    query = np.ascontiguousarray(query)
+    block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = seq_lens.shape[0]
+    assert query.shape[0] == B * query_len and block_tables.shape[0] == B
+    out = np.empty((B * query_len, layer.num_heads, layer.head_size), dtype=np.float64)
+    c, keep = layer._c()
+    used = ctypes.c_int(0)
+    st = _load().orc_decode_multi(ctypes.byref(c), _ptr(out), _ptr(query), query.shape[1], _ptr(kv_cache),
+                                  _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, int(query_len),
+                                  num_threads, ctypes.byref(used))
+    _check(st, "decode_multi")
+    return out
 
 
 def prefill(layer: OracleLayer, query: np.ndarray, key: np.ndarray, value: np.ndarray,

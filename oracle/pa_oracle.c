@@ -413,6 +413,65 @@ int orc_decode(const orc_layer *L, double *out, const void *query, int64_t q_str
 }
 
 /*
+ * Multi-token decode (the utils page's uniform batches of 1 + speculative tokens treated as
+ * decodes): sequence i has query_len query rows (rows i * query_len + t of query), all of whose
+ * K/V are already in the cache; row t sits at position seq_lens[i] - query_len + t and attends
+ * to the cached keys up to it.  seq_lens[i] == 0 is a padded sequence (zero rows); otherwise
+ * seq_lens[i] >= query_len.  out is [num_seqs * query_len, H, D] doubles.  query_len == 1 is
+ * orc_decode.
+ */
+int orc_decode_multi(const orc_layer *L, double *out, const void *query, int64_t q_stride,
+                     const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *seq_lens, int32_t num_seqs, int32_t query_len, int num_threads,
+                     int *threads_used)
+{
+    if (!layer_ok(L) || num_seqs < 0 || query_len < 1) return ORC_BAD_ARG;
+    int nt = set_threads(num_threads);
+    if (threads_used) *threads_used = nt;
+    const int64_t H = L->num_heads, Hkv = L->num_kv_heads, D = L->head_size, Q = query_len;
+    const int64_t G = H / Hkv;
+    int status = ORC_OK;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        if (seq_lens[i] < 0 || (int64_t)seq_lens[i] > (int64_t)max_blocks_per_seq * L->block_size) return ORC_BAD_INDEX;
+        if (seq_lens[i] != 0 && seq_lens[i] < query_len) return ORC_BAD_ARG;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t work = 0; work < (int64_t)num_seqs * Hkv; ++work) {
+        const int64_t i = work / Hkv, g = work % Hkv;
+        const int64_t n = seq_lens[i];
+        if (n == 0) {
+            for (int64_t t = 0; t < Q; ++t)
+                for (int64_t h = g * G; h < (g + 1) * G; ++h)
+                    for (int64_t d = 0; d < D; ++d) out[((i * Q + t) * H + h) * D + d] = 0.0;
+            continue;
+        }
+        double *K = (double *)malloc((size_t)(n * D) * sizeof(double));
+        double *V = (double *)malloc((size_t)(n * D) * sizeof(double));
+        double *q = (double *)malloc((size_t)D * sizeof(double));
+        if (!K || !V || !q) {
+#pragma omp atomic write
+            status = ORC_NO_MEMORY;
+            free(K); free(V); free(q);
+            continue;
+        }
+        int st = unpage(L, kv_cache, block_tables + i * max_blocks_per_seq, n, g, K, V);
+        if (st != ORC_OK) {
+#pragma omp atomic write
+            status = st;
+        } else {
+            for (int64_t t = 0; t < Q; ++t)
+                for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                    for (int64_t d = 0; d < D; ++d)
+                        q[d] = elt_to_double(query, (i * Q + t) * q_stride + h * D + d, L->dtype);
+                    attend_row(L, q, K, V, n - Q + t, h, out + ((i * Q + t) * H + h) * D);
+                }
+        }
+        free(K); free(V); free(q);
+    }
+    return status;
+}
+
+/*
  * Variable-length causal prefill with a cached context.  Sequence i has context_lens[i]
  * cached tokens (reached through its block-table row) followed by the
  * n_i = cu_subquery[i+1] - cu_subquery[i] new tokens whose query/key/value rows are

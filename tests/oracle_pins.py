@@ -580,6 +580,41 @@ def pin_fp8_cache_is_dequantized_cache():
         _close(d8, d32, 0.0, f"fp8 vs dequantized fp32 cache, decode (scales {ks}, {vs})")
 
 
+def pin_decode_multi():
+    """Multi-token decode: one query row equals decode exactly; k rows equal the rows of a
+    chunked prefill over the first L - k tokens with the k tokens new (decode reads the new
+    tokens' K/V from the cache, prefill from the rows, the same bits after a cache write)."""
+    layer = _layer(8, 2, 16, 4, alibi=True, window=7)
+    lens = [9, 3, 0, 14]
+    for k in (1, 3):
+        b = wl.make_batch(layer, seed=1700 + k, prefill=[(max(L - k, 0), k if L else 0) for L in lens])
+        pool = oracle_cache(b)
+        ol = oracle_layer(b.layer)
+        q, kk, vv = wl.host_bits(b.query), wl.host_bits(b.key), wl.host_bits(b.value)
+        # padded sequence (L = 0): the generator gives it no rows, multi-token decode wants k rows
+        rows = []
+        pos = 0
+        for L in lens:
+            n = k if L else 0
+            rows.append(q[pos:pos + n] if n else np.zeros((k, q.shape[1]), dtype=q.dtype))
+            pos += n
+        qm = np.concatenate(rows)
+        tables = b.prefill_block_tables
+        got = oracle.decode_multi(ol, qm, pool, tables, np.array(lens), k)
+        ref = oracle.prefill(ol, q, kk, vv, pool, tables, b.prefill_context_lens, b.prefill_cu)
+        pos = 0
+        for i, L in enumerate(lens):
+            if L == 0:
+                assert np.all(got[i * k:(i + 1) * k] == 0.0), "padded sequence rows must be zeros"
+                continue
+            _close(got[i * k:(i + 1) * k], ref[pos:pos + k], 0.0, f"decode_multi vs chunked prefill (k={k}, L={L})")
+            pos += k
+        if k == 1:
+            live = [i for i, L in enumerate(lens) if L]
+            dec = oracle.decode(ol, qm, pool, tables, np.array(lens))
+            _close(got[live], dec[live], 0.0, "decode_multi with one row vs decode")
+
+
 def _numbered_cache(nb, elems, planes=2):
     """[planes, nb, elems] fp32 cache whose every element is distinct: 1000 * plane + 10 * block + index."""
     c = np.zeros((planes, nb, elems), dtype=np.float32)
@@ -640,5 +675,5 @@ PINS = [
     pin_decode_is_last_prefill_row, pin_chunked_equals_full_rows, pin_padded_decode_row, pin_bf16_inputs,
     pin_copy_blocks_map, pin_swap_blocks_map, pin_soft_cap_saturation_and_order, pin_soft_cap_known_value,
     pin_sinks_closed_forms, pin_f16_promotion, pin_f16_inputs, pin_e4m3_code_table, pin_e4m3_quantize,
-    pin_fp8_cache_is_dequantized_cache,
+    pin_fp8_cache_is_dequantized_cache, pin_decode_multi,
 ]

@@ -46,6 +46,8 @@ MUTANTS = [
     ("fp8_value_scale", "e4m3_to_double(((const uint8_t *)vc)[idx]) * (double)L->v_scale;",
      "e4m3_to_double(((const uint8_t *)vc)[idx]) * (double)L->k_scale;"),
     ("fp8_quantize_unscaled", "(float)elt_to_double(key, src, L->dtype) / L->k_scale;", "(float)elt_to_double(key, src, L->dtype);"),
+    ("multi_position", "attend_row(L, q, K, V, n - Q + t, h,", "attend_row(L, q, K, V, n - 1, h,"),
+    ("multi_query_row", "elt_to_double(query, (i * Q + t) * q_stride + h * D + d", "elt_to_double(query, (i * Q) * q_stride + h * D + d"),
     ("swap_plane_stride", "(char *)dst_cache + (pl * dst_blocks + dst) * bb", "(char *)dst_cache + (pl * src_blocks + dst) * bb"),
 ]
 
