@@ -176,6 +176,30 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
                     size_t workspace_bytes, void *stream);
 
 /*
+ * Multi-token decode: the uniform batches of 1 + speculative tokens that the pages let a backend
+ * treat as decodes (vLLM "utils", AttentionCGSupport.UNIFORM_BATCH and
+ * _init_reorder_batch_threshold).  Every sequence has query_len query rows, rows
+ * i * query_len .. i * query_len + query_len - 1 of query, whose K/V are already in the cache;
+ * row t of sequence i sits at position seq_lens[i] - query_len + t and attends causally (with
+ * the window, ALiBi, soft-cap and sinks as in decode) to the cached keys up to it.  The query
+ * rows of a sequence and the query heads of a KV head share every K/V byte read.
+ *   out              device [num_seqs * query_len, num_heads * head_size], contiguous, written
+ *   query            device [num_seqs * query_len, ...], rows q_row_stride elements apart
+ *   seq_lens         device int32 [num_seqs], counting every query row; 0 marks a padded
+ *                    sequence (zero output rows); otherwise it must be >= query_len (rows
+ *                    without a visible key have unspecified output)
+ *   query_len        1 .. 64 (1 is pa_decode); other values: PA_ERR_INVALID_ARGUMENT
+ *   workspace        pa_decode_multi_workspace_size(layer, num_seqs, query_len, max_seq_len) bytes
+ * Other arguments as in pa_decode.
+ */
+size_t pa_decode_multi_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t query_len,
+                                      int32_t max_seq_len);
+pa_status pa_decode_multi(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                          const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *seq_lens, int32_t num_seqs, int32_t query_len, int32_t max_seq_len,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Variable-length causal prefill with an optional cached context (chunked prefill).
  * Sequence i owns query/key/value rows cu_subquery[i] .. cu_subquery[i+1]-1 (its subquery
  * tokens) and has context_lens[i] tokens already in the cache before them.  Subquery token

@@ -31,8 +31,9 @@ PA_DTYPE_F16 = 2
 PA_KV_CACHE_AUTO = 0
 PA_KV_CACHE_FP8_E4M3 = 1
 
-EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
-            "pa_status_string", "pa_last_error_message", "pa_version")
+EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_decode_multi", "pa_decode_multi_workspace_size",
+            "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string", "pa_last_error_message",
+            "pa_version")
 
 
 class PaError(RuntimeError):
@@ -73,6 +74,10 @@ def _load_library(path: str = LIB_PATH):
     lib.pa_decode_workspace_size.restype = SZ
     lib.pa_decode.argtypes = [LP, P, P, I64, P, P, I32, P, I32, I32, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_multi_workspace_size.argtypes = [LP, I32, I32, I32]
+    lib.pa_decode_multi_workspace_size.restype = SZ
+    lib.pa_decode_multi.argtypes = [LP, P, P, I64, P, P, I32, P, I32, I32, I32, P, SZ, P]
+    lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [LP, P, P, I64, P, P, I64, P, P, I32, P, P, I32, I64, I32, I32, P]
     lib.pa_prefill_varlen.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [LP, P, I32, P, I64, P]
@@ -238,36 +243,47 @@ def swap_blocks(src_cache: torch.Tensor, dst_cache: torch.Tensor, block_pairs, l
                                dst_cache.shape[1], pairs.data_ptr(), pairs.shape[0], _stream(dev)))
 
 
-def decode_workspace_size(layer: Layer, num_seqs: int, max_seq_len: int) -> int:
+def decode_workspace_size(layer: Layer, num_seqs: int, max_seq_len: int, query_len: int = 1) -> int:
     c = layer._c()
-    return int(_lib.pa_decode_workspace_size(ctypes.byref(c), num_seqs, max_seq_len))
+    if query_len == 1:
+        return int(_lib.pa_decode_workspace_size(ctypes.byref(c), num_seqs, max_seq_len))
+    return int(_lib.pa_decode_multi_workspace_size(ctypes.byref(c), num_seqs, query_len, max_seq_len))
 
 
 def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
            layer: Layer, max_seq_len: int, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Single-token decode: query [B, H*D] -> out [B, H*D]."""
+           workspace: Optional[torch.Tensor] = None, query_len: int = 1) -> torch.Tensor:
+    """Decode: query [B * query_len, H*D] -> out [B * query_len, H*D] for B = len(seq_lens) sequences
+    (query_len > 1: multi-token decode through pa_decode_multi)."""
     width = layer.num_heads * layer.head_size
     qs = _rows(query, "query", width, layer.dtype)
-    B = query.shape[0]
+    B = seq_lens.numel()
+    if query.shape[0] != B * query_len:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, f"query has {query.shape[0]} rows, expected {B} * {query_len}")
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise PaError(PA_ERR_INVALID_ARGUMENT, "block_tables must be int32 [num_seqs, max_blocks_per_seq]")
     bt = _index(block_tables, "block_tables", torch.int32)
     sl = _index(seq_lens, "seq_lens", torch.int32, (B,))
+    rows = B * query_len
     if out is None:
-        out = torch.empty((B, width), dtype=layer.dtype, device=query.device)
-    elif tuple(out.shape) != (B, width) or not out.is_contiguous() or out.dtype != layer.dtype:
-        raise PaError(PA_ERR_INVALID_ARGUMENT, "out must be a contiguous [num_seqs, H*D] tensor of the layer dtype")
+        out = torch.empty((rows, width), dtype=layer.dtype, device=query.device)
+    elif tuple(out.shape) != (rows, width) or not out.is_contiguous() or out.dtype != layer.dtype:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, "out must be a contiguous [rows, H*D] tensor of the layer dtype")
     c = layer._c()
-    need = int(_lib.pa_decode_workspace_size(ctypes.byref(c), B, max_seq_len)) if B > 0 else 0
+    need = decode_workspace_size(layer, B, max_seq_len, query_len) if B > 0 else 0
     ws_ptr, ws_bytes = None, 0
     if need > 0:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(_lib.pa_decode(ctypes.byref(c), out.data_ptr(), query.data_ptr(), qs, _cache(kv_cache, layer), bt,
-                          block_tables.shape[1], sl, B, int(max_seq_len), ws_ptr, ws_bytes,
-                          _stream(query.device)))
+    if query_len == 1:
+        _check(_lib.pa_decode(ctypes.byref(c), out.data_ptr(), query.data_ptr(), qs, _cache(kv_cache, layer), bt,
+                              block_tables.shape[1], sl, B, int(max_seq_len), ws_ptr, ws_bytes,
+                              _stream(query.device)))
+    else:
+        _check(_lib.pa_decode_multi(ctypes.byref(c), out.data_ptr(), query.data_ptr(), qs, _cache(kv_cache, layer),
+                                    bt, block_tables.shape[1], sl, B, int(query_len), int(max_seq_len), ws_ptr,
+                                    ws_bytes, _stream(query.device)))
     return out
 
 

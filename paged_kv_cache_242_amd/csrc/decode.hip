@@ -245,10 +245,10 @@ __device__ __forceinline__ int clamp_len(int L, const DecodeParams &p, const Dec
 }
 
 // Tiles (of s.tile keys, absolute alignment) that one work unit of sequence seq covers: keys
-// lo .. L - 1, lo = L - W with a sliding window.
+// lo .. L - 1, with a sliding window lo = L - qlen + 1 - W (the first query row's window start).
 __device__ __forceinline__ int seq_tiles(const DecodeParams &p, const DecodeShape &s, int seq, int &L, int &lo) {
     L = clamp_len(p.seq_lens[seq], p, s);
-    lo = p.window > 0 ? max(0, L - p.window) : 0;
+    lo = p.window > 0 ? max(0, L - p.qlen + 1 - p.window) : 0;
     return L > 0 ? (L + s.tile - 1) / s.tile - lo / s.tile : 0;
 }
 
@@ -379,6 +379,9 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     const int hk = r % KVH;                  // KV head of this row group within the unit
     const int tr = r / KVH;                  // token of this row group within an instruction
     const int my_head = head_of_lane<C, GP>(c);
+    // A unit's query heads are "virtual heads" v = t * G + h of its KV head: query row t of the
+    // sequence (t < qlen, position L - qlen + t), query head g * G + h.  With one query row they
+    // are simply the group's query heads.
     const int group = p.num_heads / p.num_kv_heads;
     const int nh = shape.heads_per_group;
     const int ups = shape.units_per_seq;
@@ -425,23 +428,31 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
         const int gu = u_in / shape.head_groups;
         const int hgrp = u_in - gu * shape.head_groups;
         const int g = gu * KVH + hk;                       // this lane's KV head
-        const int head0 = g * group + hgrp * nh;           // this lane's first query head
+        const int v0 = hgrp * nh;                          // first virtual head of the unit
+        // query row (sequence row seq * qlen + t) and query head of virtual head v0 + h
+        auto vrow = [&](int h) -> int64_t { return int64_t(seq) * p.qlen + (v0 + h) / group; };
+        auto vhead = [&](int h) -> int { return g * group + (v0 + h) % group; };
 
         // ---- one segment: tiles tile0 .. tile1 - 1 of unit (seq, KV heads gu KVH.., hgrp)
         uint32_t q[GP][4];      // query chunks, head-permuted: slot s holds head s ^ my_head
         {
-            const T *qrow =
-                reinterpret_cast<const T *>(p.query) + int64_t(seq) * p.q_stride + int64_t(head0) * D + c * EPL;
+            const T *qbase = reinterpret_cast<const T *>(p.query) + c * EPL;
 #pragma unroll
             for (int s = 0; s < GP; ++s) {
                 const int hs = s ^ my_head;
                 uint4 v = make_uint4(0, 0, 0, 0);
-                if (hs < nh) v = *reinterpret_cast<const uint4 *>(qrow + int64_t(hs) * D);
+                if (hs < nh)
+                    v = *reinterpret_cast<const uint4 *>(qbase + vrow(hs) * p.q_stride + int64_t(vhead(hs)) * D);
                 q[s][0] = v.x; q[s][1] = v.y; q[s][2] = v.z; q[s][3] = v.w;
             }
         }
-        const float slope2 = (has_alibi && my_head < nh) ? p.alibi_slopes[head0 + my_head] * kLog2e : 0.f;
-        const int pos = L - 1;
+        const float slope2 = (has_alibi && my_head < nh) ? p.alibi_slopes[vhead(my_head)] * kLog2e : 0.f;
+        // positions: this lane's score head (row t) sits at L - qlen + t; the unit's rows span
+        // pos_min .. L - 1, and the window start of the last row is lo_max
+        const int pos = L - p.qlen + (my_head < nh ? (v0 + my_head) / group : 0);
+        const int pos_min = L - p.qlen;
+        const int lo_lane = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+        const int lo_max = p.window > 0 ? max(0, L - p.window) : 0;
         const int kfirst = (lo / TILE + tile0) * TILE;
         const int kend = min(L, (lo / TILE + tile1) * TILE);
         // Lane part of every K/V address: row group r's token inside the instruction, KV head g, chunk c.
@@ -456,7 +467,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 
         auto scores = [&](int tb, const LoadT (&kr)[NI], float (&sc)[NI]) {
-            const bool edge = tb < lo || tb + TILE - 1 > pos;           // uniform
+            const bool edge = tb < lo_max || tb + TILE - 1 > pos_min;   // uniform
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 float part_dot[GP];
@@ -476,7 +487,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int j = tb + i * TR + tr;
-                    sc[i] = (j >= lo && j <= pos) ? sc[i] : -INFINITY;
+                    sc[i] = (j >= lo_lane && j <= pos) ? sc[i] : -INFINITY;
                 }
             }
         };
@@ -522,10 +533,10 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             }
             // Rows past the sequence's end hold unwritten cache bytes: zero them so that their
             // zero weights cannot meet a NaN.
-            if (tb + TILE - 1 > pos) {
+            if (tb + TILE - 1 > L - 1) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    const bool past = tb + i * TR + tr > pos;
+                    const bool past = tb + i * TR + tr > L - 1;
                     vr[i].x = past ? 0u : vr[i].x;
                     vr[i].y = past ? 0u : vr[i].y;
                     vr[i].z = past ? 0u : vr[i].z;
@@ -650,17 +661,17 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
         const float l_sum = sum_row_groups<C * KVH>(l_run * f_own);
         if (tile0 == 0 && tile1 == ts) {
             // The whole (windowed) unit is this segment: write the normalized output.
-            T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head0) * D;
 #pragma unroll
             for (int h = 0; h < GP; ++h) {
                 float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
                 const float mh = __shfl(m_all, r * C + lane_of_head<C, GP>(h), 64);
                 if (tr == 0 && h < nh) {
+                    T *out_row = reinterpret_cast<T *>(p.out) + (vrow(h) * p.num_heads + vhead(h)) * D;
                     // a sink logit joins the denominator only
-                    if (p.sinks) lh += fast_exp2(p.sinks[head0 + h] * kLog2e - mh);
+                    if (p.sinks) lh += fast_exp2(p.sinks[vhead(h)] * kLog2e - mh);
                     const float inv = p.out_scale / lh;
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) store_out<T>(out_row + h * D + c * EPL + e, acc[h][e] * inv);
+                    for (int e = 0; e < EPL; ++e) store_out<T>(out_row + c * EPL + e, acc[h][e] * inv);
                 }
             }
         } else {
@@ -709,8 +720,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     const int gu = u_in / shape.head_groups;
     const int hgrp = u_in - gu * shape.head_groups;
     const int g = gu * shape.kvh + hh / nh;
-    const int head = g * (p.num_heads / p.num_kv_heads) + hgrp * nh + hh % nh;
-    T *out_row = reinterpret_cast<T *>(p.out) + (int64_t(seq) * p.num_heads + head) * D;
+    const int group = p.num_heads / p.num_kv_heads;
+    const int v = hgrp * nh + hh % nh;                     // virtual head: query row v / G, head v % G
+    const int head = g * group + v % group;
+    T *out_row = reinterpret_cast<T *>(p.out) + ((int64_t(seq) * p.qlen + v / group) * p.num_heads + head) * D;
     int L, lo;
     const int ts = seq_tiles(p, shape, seq, L, lo);
     if (ts == 0) {                          // empty sequence: zero output
@@ -889,11 +902,12 @@ void instance_info(int padded_group, int num_kv_heads, int block_shift, int &kvh
 }  // namespace
 
 DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                       int32_t dtype, int32_t num_seqs, int32_t max_seq_len) {
+                       int32_t dtype, int32_t num_seqs, int32_t max_seq_len, int32_t query_len) {
     int block_shift = 0;
     while ((1 << block_shift) < block_size) ++block_shift;
     DecodePlan plan{};
-    const int group = num_heads / num_kv_heads;
+    // the query heads of one KV head times the query rows per sequence share its K/V bytes
+    const int group = num_heads / num_kv_heads * (query_len > 1 ? query_len : 1);
     plan.head_groups = (group + kMaxGroup - 1) / kMaxGroup;
     plan.heads_per_group = (group + plan.head_groups - 1) / plan.head_groups;
     plan.padded_group = 1;

@@ -79,6 +79,14 @@ pa_status check_layer(const pa_layer *L, const char *fn) {
     return PA_OK;
 }
 
+// Query rows per sequence that multi-token decode takes (1 + speculative tokens).
+constexpr int32_t kMaxQueryLen = 64;
+
+pa_status decode_impl(const char *fn, const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                      const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *seq_lens, int32_t num_seqs, int32_t query_len, int32_t max_seq_len,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -196,18 +204,45 @@ pa_status pa_swap_blocks(const pa_layer *layer, const void *src_cache, int64_t s
 }
 
 size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t max_seq_len) {
-    if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0) return 0;
+    return pa_decode_multi_workspace_size(layer, num_seqs, 1, max_seq_len);
+}
+
+size_t pa_decode_multi_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t query_len, int32_t max_seq_len) {
+    if (check_layer(layer, "pa_decode_workspace_size") != PA_OK || num_seqs <= 0 || max_seq_len < 0 || query_len < 1 ||
+        query_len > kMaxQueryLen)
+        return 0;
     return pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size, layer->block_size, kernel_dtype(layer),
-                           num_seqs, max_seq_len)
+                           num_seqs, max_seq_len, query_len)
         .workspace_bytes;
 }
 
 pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride, const void *kv_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *seq_lens,
                     int32_t num_seqs, int32_t max_seq_len, void *workspace, size_t workspace_bytes, void *stream) {
-    const char *fn = "pa_decode";
+    return decode_impl("pa_decode", layer, out, query, q_row_stride, kv_cache, block_tables, max_blocks_per_seq,
+                       seq_lens, num_seqs, 1, max_seq_len, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_multi(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                          const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *seq_lens, int32_t num_seqs, int32_t query_len, int32_t max_seq_len,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_impl("pa_decode_multi", layer, out, query, q_row_stride, kv_cache, block_tables, max_blocks_per_seq,
+                       seq_lens, num_seqs, query_len, max_seq_len, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status decode_impl(const char *fn, const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                      const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *seq_lens, int32_t num_seqs, int32_t query_len, int32_t max_seq_len,
+                      void *workspace, size_t workspace_bytes, void *stream) {
     pa_status st = check_layer(layer, fn);
     if (st != PA_OK) return st;
+    if (query_len < 1 || query_len > kMaxQueryLen)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: query_len %d outside [1, %d]", fn, query_len, kMaxQueryLen);
     if (fp8_cache(layer) && layer->dtype == PA_DTYPE_F32)
         return fail(PA_ERR_UNSUPPORTED, "%s: an fp8 cache needs a bf16 or fp16 layer", fn);
     if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
@@ -226,7 +261,8 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: out/query/kv_cache must be 16-byte aligned with 16-byte row strides",
                     fn);
     const pa::DecodePlan plan = pa::plan_decode(layer->num_heads, layer->num_kv_heads, layer->head_size,
-                                                layer->block_size, kernel_dtype(layer), num_seqs, max_seq_len);
+                                                layer->block_size, kernel_dtype(layer), num_seqs, max_seq_len,
+                                                query_len);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes)
             return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", fn, plan.workspace_bytes,
@@ -258,6 +294,7 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     p.softcap = layer->logits_soft_cap > 0.f ? layer->logits_soft_cap : 0.f;
     p.sinks = layer->sinks;
     p.max_seq_len = max_seq_len;
+    p.qlen = query_len;
     char *ws = static_cast<char *>(workspace);
     p.ws_prefix = reinterpret_cast<int64_t *>(ws + plan.ws_prefix_off);
     p.ws_wseq = reinterpret_cast<int32_t *>(ws + plan.ws_wseq_off);
@@ -267,6 +304,10 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
                             const void *key, const void *value, int64_t kv_row_stride, const void *kv_cache,

@@ -49,7 +49,7 @@ struct DecodePlan {
 // Kernel element codes (the `dtype` of plan_decode / launch_decode / launch_prefill): 0 fp32,
 // 1 bf16, 2 fp16, 3 bf16 with an FP8 E4M3 cache, 4 fp16 with an FP8 E4M3 cache.
 DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                       int32_t dtype, int32_t num_seqs, int32_t max_seq_len);
+                       int32_t dtype, int32_t num_seqs, int32_t max_seq_len, int32_t query_len);
 
 struct DecodeParams {
     void *out;                // [B, H*D]
@@ -72,6 +72,7 @@ struct DecodeParams {
     float softcap;            // <= 0: off
     const float *sinks;       // [H] natural-log sink logits, or null
     float out_scale;          // multiplies the normalized output (an FP8 cache's v_scale, else 1)
+    int32_t qlen;             // query rows per sequence (1: plain decode; more: multi-token decode)
     int64_t *ws_prefix;       // [B + 1] tiles of the work units of sequences before q
     int32_t *ws_wseq;         // [num_waves] sequence of each wavefront's first tile
     float *ws_acc;            // [slots, D] partial weighted V

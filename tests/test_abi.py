@@ -23,6 +23,7 @@ def pa():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["pa_cache_write", "pa_decode", "pa_decode_workspace_size",
+                                           "pa_decode_multi", "pa_decode_multi_workspace_size",
                                            "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
                                            "pa_status_string", "pa_last_error_message", "pa_version"])
 

@@ -337,6 +337,45 @@ def test_multi_token_decode_as_chunked_prefill(k, layer):
 
 # ------------------------------------------------------------------------------ full-size workloads
 
+MULTI_CASES = [
+    (2, _layer(32, 8, 128, 16)),
+    (4, _layer(32, 8, 128, 16)),                               # 16 virtual heads per KV head: two groups
+    (3, _layer(32, 32, 128, 16, alibi=True, window=300)),      # 3 rows of one head: padded group of 4
+    (2, _layer(64, 8, 128, 32, fp8=True)),
+    (4, _layer(16, 2, 64, 8, wl.F16, sinks=True, softcap=3.0, scale=0.3)),
+    (2, _layer(8, 8, 64, 16, wl.F32, alibi=True, window=40)),
+    (8, _layer(8, 1, 128, 16, alibi=True)),                    # 64 virtual heads of one KV head
+]
+
+
+@pytest.mark.parametrize("ci", range(len(MULTI_CASES)))
+def test_decode_multi(ci):
+    """Multi-token decode (pa_decode_multi): k query rows per sequence, every K/V already in the
+    cache, against the oracle's multi-token decode; a padded sequence (length 0) gives zero rows."""
+    k, layer = MULTI_CASES[ci]
+    rng = np.random.default_rng(80 + ci)
+    lens = [k, k + 1, 31, 129, 1000, 0, 2049, 4100] + rng.integers(k, 3000, size=8).tolist()
+    live = [L for L in lens if L]
+    batch = wl.make_batch(layer, seed=81 + ci, prefill=[(L - k, k) for L in live], device=gh.device())
+    _say(f"decode_multi k={k} layer {ci}: {batch.layer}")
+    pl = gh.player(batch.layer)
+    cache = gh.gpu_pool(batch, pl)
+    width = layer.num_heads * layer.head_size
+    q = torch.zeros(len(lens) * k, width, dtype=batch.query.dtype, device=gh.device())
+    tables = np.zeros((len(lens), batch.prefill_block_tables.shape[1]), dtype=np.int32)
+    j = 0
+    for i, L in enumerate(lens):
+        if L:
+            q[i * k:(i + 1) * k] = batch.query[j * k:(j + 1) * k]
+            tables[i] = batch.prefill_block_tables[j]
+            j += 1
+    out = gh.pa().decode(q, cache, gh.i32(tables), gh.i32(np.array(lens)), pl, max(lens), query_len=k)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    ref = oracle.decode_multi(gh.olayer(batch.layer), wl.host_bits(q), pool, tables, np.array(lens), k)
+    gh.assert_close(gh.to_f64(out), ref, batch.layer, f"decode_multi k={k} layer {ci}")
+
+
 def _sample(n, k, rng, must=()):
     pick = set(int(x) for x in must)
     pick.update(int(x) for x in rng.choice(n, size=min(k, n), replace=False))
