@@ -182,7 +182,10 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
  * i * query_len .. i * query_len + query_len - 1 of query, whose K/V are already in the cache;
  * row t of sequence i sits at position seq_lens[i] - query_len + t and attends causally (with
  * the window, ALiBi, soft-cap and sinks as in decode) to the cached keys up to it.  The query
- * rows of a sequence and the query heads of a KV head share every K/V byte read.
+ * rows of a sequence and the query heads of a KV head share every K/V byte read as long as
+ * query_len * (num_heads / num_kv_heads) <= 8; beyond that the K/V bytes are read once per
+ * group of 8, and pa_prefill_varlen over the same rows (context seq_lens[i] - query_len, the
+ * query_len rows new) is the faster form.
  *   out              device [num_seqs * query_len, num_heads * head_size], contiguous, written
  *   query            device [num_seqs * query_len, ...], rows q_row_stride elements apart
  *   seq_lens         device int32 [num_seqs], counting every query row; 0 marks a padded
