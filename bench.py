@@ -1,6 +1,7 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline] [--no-block-moves]
+                    [--no-fp8]
 
 One step is one pass of the whole hot path over one synthetic batch, all inputs resident in HBM:
 pa_cache_write of the step's new K/V rows, pa_prefill_varlen over the prefill rows and pa_decode
@@ -18,7 +19,8 @@ Prints ONE JSON line:
                 cache-write GB/s (bytes read + written), each with its fraction of peak; and,
                 outside the timed steps, pa_copy_blocks GB/s (1024 scattered blocks of the
                 workload's geometry in a scratch cache, bytes read + written) and pa_swap_blocks
-                GB/s to and from pinned host memory (--no-block-moves skips them)
+                GB/s to and from pinned host memory (--no-block-moves skips them); and, also outside
+                the timed steps, decode and prefill over an FP8 (E4M3) copy of the cache (--no-fp8)
   roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s;
                 traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
                 (profiles/decode_traffic.json), null when the decode source changed since
@@ -203,6 +205,45 @@ def block_moves(pa, L, dev, num_pairs: int = 1024, reps: int = 10):
     return out
 
 
+def fp8_cache_leg(pa, L, layer, cache, dev, dec_args, pre_args, reps: int = 10):
+    """Outside the timed steps: the same batch over an FP8 (E4M3) copy of the cache, quantized
+    from it by pa_cache_write (k_scale 0.02, v_scale 0.015 for N(0, 1) rows).  Decode GB/s counts
+    the fp8 bytes read; prefill TFLOP/s the same flops as the bf16 run."""
+    import dataclasses
+    l8 = dataclasses.replace(layer, kv_cache_dtype="fp8_e4m3", k_scale=0.02, v_scale=0.015)
+    rows = cache.view(2, -1, L.row_elems)
+    c8 = torch.empty(cache.shape, dtype=torch.uint8, device=dev)
+    pa.cache_write(rows[0], rows[1], c8, torch.arange(rows.shape[1], device=dev), l8)
+    res = {"k_scale": 0.02, "v_scale": 0.015}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    if dec_args is not None:
+        q, bt, sl, mx, nbytes = dec_args
+        out = torch.empty_like(q)
+        ws = torch.empty(max(pa.decode_workspace_size(l8, sl.numel(), mx), 1), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: pa.decode(q, c8, bt, sl, l8, mx, out=out, workspace=ws))
+        res["decode"] = {"ms": ms, "GB_per_s": nbytes / 2 / (ms * 1e-3) / 1e9,
+                         "frac_hbm_peak": nbytes / 2 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    if pre_args is not None:
+        q, k, v, bt, ctx, cu, mq, mc, flops = pre_args
+        out = torch.empty_like(q)
+        ms = timed(lambda: pa.prefill_varlen(q, k, v, c8, bt, ctx, cu, l8, mq, mc, out=out))
+        res["prefill"] = {"ms": ms, "TFLOP_per_s": flops / (ms * 1e-3) / 1e12}
+    del c8
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +252,7 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-moves", action="store_true", help="skip the copy_blocks / swap_blocks timing")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache timing")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (counter calibration) and exit")
@@ -296,6 +338,11 @@ def main(argv=None):
     secondary = {"cache_write": {"ms": cw_ms, "GB_per_s": cw_gbps, "frac_hbm_peak": cw_gbps / HBM_PEAK_GBPS}}
     if not args.no_block_moves:
         secondary.update(block_moves(pa, L, dev))
+    if not args.no_fp8 and L.dtype != wl.F32:
+        secondary["fp8_cache"] = fp8_cache_leg(
+            pa, L, layer, cache, dev,
+            (q_dec, d_bt, d_sl, d_max, decode_bytes(batch)) if has_dec else None,
+            (q_pre, k_pre, v_pre, p_bt, p_ctx, p_cu, p_maxq, p_maxc, prefill_flops(batch)) if has_pre else None)
     value = None
     unit = "GB/s"
     roofline = None
