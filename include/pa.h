@@ -89,7 +89,7 @@ typedef enum pa_kv_cache_dtype {
  * (num_heads, head_size, scale, num_kv_heads, alibi_slopes, sliding_window).
  *   num_heads       H, > 0
  *   num_kv_heads    Hkv, > 0, divides H
- *   head_size       D: 64 or 128 (others: PA_ERR_UNSUPPORTED)
+ *   head_size       D: 64, 128 or 256 (others: PA_ERR_UNSUPPORTED)
  *   block_size      tokens per cache block: a power of two in [8, 256]
  *   num_blocks      physical blocks per plane, > 0
  *   dtype           PA_DTYPE_F32, PA_DTYPE_BF16 or PA_DTYPE_F16 (the cache, query, key, value

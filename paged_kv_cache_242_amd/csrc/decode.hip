@@ -899,6 +899,27 @@ void instance_info(int padded_group, int num_kv_heads, int block_shift, int &kvh
     }
 }
 
+template <typename T>
+struct TypeTag { typedef T type; };
+
+// Calls f(TypeTag<element type>, integral_constant<head size>) for a kernel element code and a
+// head size of 64, 128 or 256.
+template <typename F>
+auto dispatch_type_size(int dtype, int head_size, F &&f) {
+    auto by_size = [&](auto t) {
+        if (head_size == 64) return f(t, std::integral_constant<int, 64>());
+        if (head_size == 128) return f(t, std::integral_constant<int, 128>());
+        return f(t, std::integral_constant<int, 256>());
+    };
+    switch (dtype) {
+        case 1: return by_size(TypeTag<bf16_t>());
+        case 2: return by_size(TypeTag<f16_t>());
+        case 3: return by_size(TypeTag<bf16_c8_t>());
+        case 4: return by_size(TypeTag<f16_c8_t>());
+        default: return by_size(TypeTag<float>());
+    }
+}
+
 }  // namespace
 
 DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
@@ -915,22 +936,11 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     // Block-id chunk: 128 blocks (two id registers per lane), at most 4096 keys.
     plan.chunk = (128 << block_shift) < 4096 ? (128 << block_shift) : 4096;
     int kvh = 1, tile = 32, waves = 2048;
-    if (dtype == 3) {
-        if (head_size == 128) instance_info<bf16_c8_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-        else instance_info<bf16_c8_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-    } else if (dtype == 4) {
-        if (head_size == 128) instance_info<f16_c8_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-        else instance_info<f16_c8_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-    } else if (dtype == 1) {
-        if (head_size == 128) instance_info<bf16_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-        else instance_info<bf16_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-    } else if (dtype == 2) {
-        if (head_size == 128) instance_info<f16_t, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-        else instance_info<f16_t, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-    } else {
-        if (head_size == 128) instance_info<float, 128>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-        else instance_info<float, 64>(plan.padded_group, num_kv_heads, block_shift, kvh, tile, waves);
-    }
+    dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
+        instance_info<typename decltype(t)::type, decltype(d)::value>(plan.padded_group, num_kv_heads, block_shift, kvh,
+                                                                      tile, waves);
+        return 0;
+    });
     plan.kv_per_unit = kvh;
     plan.units_per_seq = num_kv_heads / kvh * plan.head_groups;
     plan.tile = tile;
@@ -960,23 +970,9 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
     s.tile = plan.tile;
     s.max_len = p.max_seq_len;
     s.kvh = plan.kv_per_unit;
-    if (dtype == 3) {
-        if (head_size == 128) return launch_group<bf16_c8_t, 128>(p, s, plan.padded_group, stream);
-        if (head_size == 64) return launch_group<bf16_c8_t, 64>(p, s, plan.padded_group, stream);
-    } else if (dtype == 4) {
-        if (head_size == 128) return launch_group<f16_c8_t, 128>(p, s, plan.padded_group, stream);
-        if (head_size == 64) return launch_group<f16_c8_t, 64>(p, s, plan.padded_group, stream);
-    } else if (dtype == 1) {
-        if (head_size == 128) return launch_group<bf16_t, 128>(p, s, plan.padded_group, stream);
-        if (head_size == 64) return launch_group<bf16_t, 64>(p, s, plan.padded_group, stream);
-    } else if (dtype == 2) {
-        if (head_size == 128) return launch_group<f16_t, 128>(p, s, plan.padded_group, stream);
-        if (head_size == 64) return launch_group<f16_t, 64>(p, s, plan.padded_group, stream);
-    } else {
-        if (head_size == 128) return launch_group<float, 128>(p, s, plan.padded_group, stream);
-        if (head_size == 64) return launch_group<float, 64>(p, s, plan.padded_group, stream);
-    }
-    return hipErrorInvalidValue;
+    return dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
+        return launch_group<typename decltype(t)::type, decltype(d)::value>(p, s, plan.padded_group, stream);
+    });
 }
 
 }  // namespace pa

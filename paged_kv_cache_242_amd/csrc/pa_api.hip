@@ -56,9 +56,9 @@ pa_status check_layer(const pa_layer *L, const char *fn) {
     if (L->dtype != PA_DTYPE_F32 && L->dtype != PA_DTYPE_BF16 && L->dtype != PA_DTYPE_F16)
         return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (fp32 = 0, bf16 = 1, fp16 = 2)", fn,
                     L->dtype);
-    if (L->head_size != 64 && L->head_size != 128)
-        return fail(PA_ERR_UNSUPPORTED, "%s: head size %d is not supported; supported head sizes are 64 and 128", fn,
-                    L->head_size);
+    if (L->head_size != 64 && L->head_size != 128 && L->head_size != 256)
+        return fail(PA_ERR_UNSUPPORTED, "%s: head size %d is not supported; supported head sizes are 64, 128 and 256",
+                    fn, L->head_size);
     const int bs_shift = log2_exact(L->block_size);
     if (L->block_size < 8 || L->block_size > 256 || bs_shift < 0)
         return fail(PA_ERR_UNSUPPORTED, "%s: block size %d is not supported (powers of two from 8 to 256)", fn,

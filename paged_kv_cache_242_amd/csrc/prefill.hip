@@ -104,7 +104,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // bank window.
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
-    return D == 128 ? (r & 7) : ((r >> 1) & 3);
+    return D >= 128 ? (r & 7) : ((r >> 1) & 3);
 }
 
 // max(x, x of lane ^ 16) and max(x, x of lane ^ 32) with the gfx950 row-swap moves (VALU, no
@@ -137,7 +137,7 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 // (buffer/global_load_lds_dwordx4: lane l of an instruction fills 16-byte unit l of a 1 KB LDS
 // stretch), so they never pass through registers.  Swizzles are applied by choosing, per lane,
 // which 16-byte chunk of the source row to fetch:
-//   K: row-major [64][D], chunk c of row r stored at chunk c ^ (r % CH); the S^T operand read
+//   K: row-major [64][D], chunk c of row r stored at chunk c ^ ((r mod 16) mod CH); the S^T operand read
 //      (16 rows, same chunk) then hits distinct banks.
 //   V: row-major [64][D], 32-byte unit u of key k stored at unit u ^ vswz(k); the transposing
 //      operand read (ds_read_b64_tr_b16: 4 keys x 32 bytes per 16 lanes, 8 keys per 32 lanes)
@@ -176,8 +176,10 @@ __device__ __forceinline__ floatx4_v mfma16(halfx8_v a, halfx8_v b, floatx4_v c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Head size 256 doubles the O accumulators and the operands per wavefront and the LDS stages
+// (128 KB): one workgroup per CU then, with the register file of a single wavefront per SIMD.
 template <typename T, int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams p, PrefillGrid grid) {
+__global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel(PrefillParams p, PrefillGrid grid) {
     typedef typename Operand8<T>::type V8;
     auto elt_bits = [](T x) -> uint32_t { return uint32_t(__builtin_bit_cast(uint16_t, x)); };
     constexpr int CH = D / 8;        // 16-byte chunks per row
@@ -380,9 +382,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
                             w[2 * q + 1] = pack_x2<T>(hi[0] * sc, hi[1] * sc);
                         }
                         int off0, off1;
-                        if (o == 0) {                       // K: 16-byte chunk c of row rr at c ^ (rr % CH)
-                            off0 = rr * D + (((2 * m) ^ (rr % CH)) << 3);
-                            off1 = rr * D + (((2 * m + 1) ^ (rr % CH)) << 3);
+                        if (o == 0) {
+                            // K: 16-byte chunk c of row rr at c ^ ((rr mod 16) mod CH), the swizzle the
+                            // copies and the operand reads use (they see rows 16 w .. 16 w + 15)
+                            const int sw = (rr & 15) % CH;
+                            off0 = rr * D + (((2 * m) ^ sw) << 3);
+                            off1 = rr * D + (((2 * m + 1) ^ sw) << 3);
                         } else {                            // V: 32-byte unit u of row rr at u ^ vswz(rr)
                             off0 = rr * D + ((m ^ vswz<D>(rr)) << 4);
                             off1 = off0 + 8;
@@ -457,8 +462,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillParams
         }
     };
 
-    // ---- operand read offsets (elements), fixed for the whole loop.  Row 16 kb + l16 of K has
-    // row % CH == l16 % CH, so the swizzle depends on the lane only and kb adds a constant.
+    // ---- operand read offsets (elements), fixed for the whole loop.  The K swizzle of row 16 kb +
+    // l16 is l16 mod CH (the copies use the row's offset inside its wavefront's 16 rows, the same
+    // value), so it depends on the lane only and kb adds a constant.
     int k_off[DC];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) k_off[dc] = l16 * D + (((4 * dc + lg) ^ (l16 % CH)) << 3);
@@ -810,9 +816,16 @@ hipError_t launch_mfma(const PrefillParams &p, int head_size, hipStream_t stream
     grid.num_groups = int(groups);
     const dim3 nb = dim3(unsigned(blocks)), nt = dim3(kThreads);
     const int variant = (p.alibi_slopes != nullptr ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
-    if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
+    if (head_size != 128 && head_size != 64 && head_size != 256) return hipErrorInvalidValue;
     auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, nb, nt, 0, stream, p, grid); };
-    if (head_size == 128) {
+    if (head_size == 256) {
+        switch (variant) {
+            case 0: go(prefill_mfma_kernel<T, 256, false, false>); break;
+            case 1: go(prefill_mfma_kernel<T, 256, true, false>); break;
+            case 2: go(prefill_mfma_kernel<T, 256, false, true>); break;
+            default: go(prefill_mfma_kernel<T, 256, true, true>); break;
+        }
+    } else if (head_size == 128) {
         switch (variant) {
             case 0: go(prefill_mfma_kernel<T, 128, false, false>); break;
             case 1: go(prefill_mfma_kernel<T, 128, true, false>); break;
@@ -840,7 +853,9 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipS
     const int64_t blocks = p.num_tokens * p.num_heads;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (head_size == 128)
+    if (head_size == 256)
+        hipLaunchKernelGGL(prefill_f32_kernel<256>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+    else if (head_size == 128)
         hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     else if (head_size == 64)
         hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);

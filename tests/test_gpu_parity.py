@@ -203,6 +203,11 @@ DECODE_LAYERS = [
     _layer(32, 32, 128, 16, wl.F16, fp8=True, alibi=True, window=100),
     _layer(16, 2, 64, 8, fp8=True, softcap=3.0, scale=0.3),
     _layer(12, 2, 128, 64, wl.F16, fp8=True),
+    # head size 256
+    _layer(16, 8, 256, 16),
+    _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
+    _layer(16, 4, 256, 32, fp8=True, softcap=30.0, scale=0.15),
+    _layer(4, 2, 256, 16, wl.F32, sinks=True),
 ]
 DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
 
@@ -290,6 +295,11 @@ PREFILL_LAYERS = [
     _layer(32, 32, 128, 16, wl.F16, fp8=True, alibi=True, window=100),
     _layer(8, 2, 64, 8, fp8=True, sinks=True),
     _layer(8, 4, 128, 32, fp8=True, softcap=4.0, scale=0.25),
+    # head size 256
+    _layer(16, 8, 256, 16),
+    _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
+    _layer(16, 4, 256, 32, fp8=True, softcap=30.0, scale=0.15, sinks=True),
+    _layer(4, 2, 256, 16, wl.F32, alibi=True),
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
