@@ -386,6 +386,55 @@ def test_decode_multi(ci):
     gh.assert_close(gh.to_f64(out), ref, batch.layer, f"decode_multi k={k} layer {ci}")
 
 
+def test_graph_capture_replays():
+    """The library neither allocates, nor synchronizes, nor clears memory with memset, so a whole
+    step -- cache write, prefill, decode, multi-token decode -- can be captured in a HIP graph:
+    three replays, with eager work in between, each reproduce the eager outputs bit for bit."""
+    layer = _layer(16, 4, 128, 16, alibi=True, window=200, sinks=True)
+    batch = wl.make_batch(layer, seed=95, prefill=[(100, 150), (0, 90)], decode=[1, 250, 700, 0],
+                          device=gh.device())
+    pa = gh.pa()
+    pl = gh.player(batch.layer)
+    cache = gh.gpu_pool(batch, pl)
+    tp = batch.num_prefill_tokens
+    slots = gh.i64(batch.slot_mapping)
+    p_args = (batch.query[:tp], batch.key[:tp], batch.value[:tp], cache, gh.i32(batch.prefill_block_tables),
+              gh.i32(batch.prefill_context_lens), gh.i32(batch.prefill_cu), pl, int(batch.prefill_query_lens.max()),
+              int(batch.prefill_context_lens.max()))
+    d_bt, d_sl = gh.i32(batch.decode_block_tables), gh.i32(batch.decode_seq_lens)
+    q_dec = batch.query[tp:]
+    # multi-token decode over the two prefill sequences, their last 2 rows as the query rows
+    m_bt = gh.i32(batch.prefill_block_tables)
+    m_sl = gh.i32(batch.prefill_context_lens + batch.prefill_query_lens)
+    q_multi = torch.stack([batch.query[int(batch.prefill_cu[i + 1]) - 2:int(batch.prefill_cu[i + 1])]
+                           for i in range(2)]).reshape(4, -1).contiguous()
+    out_pre, out_dec, out_multi = torch.empty_like(p_args[0]), torch.empty_like(q_dec), torch.empty_like(q_multi)
+    ws_d = torch.empty(pa.decode_workspace_size(pl, 4, 700), dtype=torch.uint8, device=gh.device())
+    ws_m = torch.empty(pa.decode_workspace_size(pl, 2, 400, 2), dtype=torch.uint8, device=gh.device())
+
+    def step():
+        pa.cache_write(batch.key, batch.value, cache, slots, pl)
+        pa.prefill_varlen(*p_args, out=out_pre)
+        pa.decode(q_dec, cache, d_bt, d_sl, pl, 700, out=out_dec, workspace=ws_d)
+        pa.decode(q_multi, cache, m_bt, m_sl, pl, 400, out=out_multi, workspace=ws_m, query_len=2)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out_pre, out_dec, out_multi)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (out_pre, out_dec, out_multi):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("prefill", "decode", "multi-token decode"), (out_pre, out_dec, out_multi), ref):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {rep}: {name} differs"
+
+
 def _sample(n, k, rng, must=()):
     pick = set(int(x) for x in must)
     pick.update(int(x) for x in rng.choice(n, size=min(k, n), replace=False))
