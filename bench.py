@@ -1,7 +1,7 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline] [--no-block-moves]
-                    [--no-fp8]
+                    [--no-fp8] [--no-long-prefill]
 
 One step is one pass of the whole hot path over one synthetic batch, all inputs resident in HBM:
 pa_cache_write of the step's new K/V rows, pa_prefill_varlen over the prefill rows and pa_decode
@@ -20,7 +20,9 @@ Prints ONE JSON line:
                 outside the timed steps, pa_copy_blocks GB/s (1024 scattered blocks of the
                 workload's geometry in a scratch cache, bytes read + written) and pa_swap_blocks
                 GB/s to and from pinned host memory (--no-block-moves skips them); and, also outside
-                the timed steps, decode and prefill over an FP8 (E4M3) copy of the cache (--no-fp8)
+                the timed steps, decode and prefill over an FP8 (E4M3) copy of the cache (--no-fp8);
+                and prefill on long prompts (4 x 8192 new tokens, workload 2's head geometry), where
+                per-workgroup fixed costs are amortized (--no-long-prefill)
   roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s;
                 traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
                 (profiles/decode_traffic.json), null when the decode source changed since
@@ -205,6 +207,40 @@ def block_moves(pa, L, dev, num_pairs: int = 1024, reps: int = 10):
     return out
 
 
+def long_prefill_leg(pa, dev, reps: int = 5):
+    """Outside the timed steps: causal prefill of 4 prompts of 8192 tokens with no cached context
+    (32 query / 8 KV heads, head size 128, block size 16, bf16, seed 12).  Each wavefront then
+    walks ~128 key tiles instead of the ~5-15 of the configured prompts."""
+    lay = wl.LayerSpec(32, 8, 128, 16, 0, wl.BF16, wl.fp32(1.0 / np.sqrt(128)))
+    batch = wl.make_batch(lay, seed=12, prefill=[(0, 8192)] * 4, device=dev)
+    L = batch.layer
+    layer = pa.Layer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks, L.torch_dtype, L.scale,
+                     None, 0)
+    cache = torch.zeros((2, L.num_blocks, L.block_size * L.row_elems), dtype=L.torch_dtype, device=dev)
+    i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
+    args = (batch.query, batch.key, batch.value, cache, i32(batch.prefill_block_tables),
+            i32(batch.prefill_context_lens), i32(batch.prefill_cu), layer, int(batch.prefill_query_lens.max()), 0)
+    out = torch.empty_like(batch.query)
+    for _ in range(2):
+        pa.prefill_varlen(*args, out=out)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pa.prefill_varlen(*args, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    flops = prefill_flops(batch)
+    ms = float(np.median(ts))
+    tflops = flops / (ms * 1e-3) / 1e12
+    del batch, cache, out
+    torch.cuda.empty_cache()
+    return {"shape": "4 x 8192 new tokens, H=32, Hkv=8, D=128, bs=16, causal, no context", "ms": ms,
+            "gflop_per_call": flops / 1e9, "TFLOP_per_s": tflops, "frac_mfma_peak": tflops / MFMA_BF16_PEAK_TFLOPS}
+
+
 def fp8_cache_leg(pa, L, layer, cache, dev, dec_args, pre_args, reps: int = 10):
     """Outside the timed steps: the same batch over an FP8 (E4M3) copy of the cache, quantized
     from it by pa_cache_write (k_scale 0.02, v_scale 0.015 for N(0, 1) rows).  Decode GB/s counts
@@ -253,6 +289,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-moves", action="store_true", help="skip the copy_blocks / swap_blocks timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache timing")
+    ap.add_argument("--no-long-prefill", action="store_true", help="skip the long-prompt prefill timing")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (counter calibration) and exit")
@@ -343,6 +380,8 @@ def main(argv=None):
             pa, L, layer, cache, dev,
             (q_dec, d_bt, d_sl, d_max, decode_bytes(batch)) if has_dec else None,
             (q_pre, k_pre, v_pre, p_bt, p_ctx, p_cu, p_maxq, p_maxc, prefill_flops(batch)) if has_pre else None)
+    if not args.no_long_prefill and L.dtype != wl.F32:
+        secondary["prefill_long_prompts"] = long_prefill_leg(pa, dev)
     value = None
     unit = "GB/s"
     roofline = None
