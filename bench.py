@@ -122,7 +122,7 @@ def copy_probe(gib: float):
 
 
 def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20.0):
-    """Time the oracle's decode on the GPU machine's host cores over a bounded sample of the
+    """Time the oracle's decode on this machine's host cores over a bounded sample of the
     decode sequences of the same batch (longest-first is not used: a seeded random subset)."""
     import oracle
     L = batch.layer
@@ -296,7 +296,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"

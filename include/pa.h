@@ -57,7 +57,7 @@ extern "C" {
 typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARGUMENT = 1, /* a NULL pointer, a negative size, a misaligned buffer, a bad geometry */
-    PA_ERR_UNSUPPORTED = 2,      /* a head size, block size or dtype this build has no kernel for */
+    PA_ERR_UNSUPPORTED = 2,      /* a head size, block size or dtype the library has no kernel for */
     PA_ERR_WORKSPACE = 3,        /* decode workspace missing or smaller than pa_decode_workspace_size() */
     PA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } pa_status;
