@@ -464,6 +464,26 @@ def test_workload2_full_cache_and_sampled_rows():
     gh.assert_close(gh.to_f64(pre)[sel], ref[sel].reshape(int(sel.sum()), -1), batch.layer, W.name)
 
 
+def test_long_prompt_prefill_sampled_rows():
+    """The long-prompt prefill shape bench.py times (4 x 8192 new tokens, 32 / 8 heads, head size 128,
+    block size 16, seed 12): the cache write bit-exact, sampled rows against the oracle."""
+    lay = wl.LayerSpec(32, 8, 128, 16, 0, wl.BF16, wl.fp32(1.0 / np.sqrt(128)))
+    batch = wl.make_batch(lay, seed=12, prefill=[(0, 8192)] * 4, device=gh.device())
+    _say("long prompts: 4 x 8192 tokens, H=32, Hkv=8, D=128, bs=16")
+    cache, pre, _ = gh.gpu_run(batch)
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8)), "cache write differs"
+    T = batch.num_prefill_tokens
+    sel = np.zeros(T, dtype=bool)
+    sel[::97] = True
+    sel[batch.prefill_cu[:-1]] = True
+    sel[batch.prefill_cu[1:] - 1] = True
+    ref = gh.oracle_prefill(batch, pool, row_select=sel)
+    gh.assert_close(gh.to_f64(pre)[sel], ref[sel].reshape(int(sel.sum()), -1), batch.layer, "long prompts")
+    del batch, cache, pre
+    torch.cuda.empty_cache()
+
+
 def test_workload3_sampled_sequences():
     W = wl.workload(3)
     _say(W.description)
