@@ -34,6 +34,7 @@
 // multiply V, fp32 accumulation, output rounded to nearest even.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -818,22 +819,24 @@ const void *split_kernel_fn() {
 }
 
 // Resident wavefronts of the split kernel instance on the current device (occupancy x CUs),
-// cached per device and instance.
+// cached per device and instance.  Host threads may race to fill an entry; they compute the same
+// value, and the atomic makes the race well defined.
 template <typename T, int D, int GP, int KVH>
 int split_waves(int block_shift) {
     constexpr int TILE = tile_keys<T, D, GP, KVH>();
     const bool one = (1 << block_shift) >= TILE;
-    static int cache[64][2];
+    static std::atomic<int> cache[64][2];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int &slot = cache[dev][one ? 1 : 0];
-    if (slot > 0) return slot;
+    std::atomic<int> &slot = cache[dev][one ? 1 : 0];
+    const int known = slot.load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     const void *fn = one ? split_kernel_fn<T, D, GP, true, KVH>() : split_kernel_fn<T, D, GP, false, KVH>();
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 8;
-    slot = cus * per_cu;
-    return slot;
+    slot.store(cus * per_cu, std::memory_order_relaxed);
+    return cus * per_cu;
 }
 
 template <typename T, int D, int GP, bool ONE, int KVH>
