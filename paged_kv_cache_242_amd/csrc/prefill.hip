@@ -302,8 +302,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     const int wrow0 = 16 * wave;                            // first tile row this wavefront copies
     // Lane terms of the copy addresses: the lane's row among its instruction's rows and the
     // logical chunk its physical LDS unit holds (the residues of the row mod CH and mod 4 depend
-    // only on j and the lane).  They are rebuilt from the lane id at every copy -- a few ALU ops --
-    // rather than held in registers across the loop.
+    // only on j and the lane).  They come from the lane id (an asm read, so the compiler neither
+    // hoists nor merges them on its own); where they are held across the loop is decided below.
     auto lane_terms = [&](int &lrow, int &pc) __attribute__((always_inline)) {
         int l;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
@@ -319,6 +319,25 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     auto v_chunk = [&](int lrow, int pc, int j) __attribute__((always_inline)) -> uint32_t {
         return uint32_t((((pc >> 1) ^ vswz<D>(j * RPI + lrow)) * 2 + (pc & 1)) * 16);
     };
+    // Up to head size 128 the lane offsets of the two fast copy paths (whole cached or whole new
+    // runs of rows) are computed once and held in registers: 4 NJ values, against ~40 ALU ops per
+    // tile to rebuild them.  At head size 256 the registers are needed elsewhere.
+    constexpr bool HOLD = D <= 128;
+    constexpr int NH = HOLD ? NJ : 1;
+    uint32_t koc[NH], voc[NH], kon[NH], von[NH];
+    if constexpr (HOLD) {
+        int lrow, pc;
+        lane_terms(lrow, pc);
+        const uint32_t lc = uint32_t(lrow) * uint32_t(cache_row_bytes);
+        const uint32_t ln = uint32_t(lrow) * uint32_t(new_row_bytes);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            koc[j] = lc + k_chunk(lrow, pc, j);
+            voc[j] = lc + v_chunk(lrow, pc, j);
+            kon[j] = ln + k_chunk(lrow, pc, j);
+            von[j] = ln + v_chunk(lrow, pc, j);
+        }
+    }
     auto clamp_block = [&](int64_t bl) __attribute__((always_inline)) -> int64_t {
         return bl < 0 ? 0 : (bl >= p.num_blocks ? p.num_blocks - 1 : bl);
     };
@@ -409,8 +428,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // query row masks them.
     auto copy_tile = [&](int kt, int id0_raw, int id1_raw, bf16_t *kdst, bf16_t *vdst) __attribute__((always_inline)) {
         const int w0 = kt * kBN + wrow0;                  // first key of this wavefront (uniform)
-        int lrow, pc;
-        lane_terms(lrow, pc);
         if constexpr (C8) {
             if (w0 < si.c) fp8_issue(kt, id0_raw, id1_raw);
             if (w0 + 15 < si.c) return;                   // all cached: nothing for the copies
@@ -418,6 +435,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         if (!C8 && w0 + 15 < si.c) {
             const int64_t off0 = clamp_block(id0_raw) * block_bytes + head_off + int64_t(w0 & bmask) * cache_row_bytes;
             const int64_t off1 = clamp_block(id1_raw) * block_bytes + head_off;
+            int lrow = 0, pc = 0;
+            if constexpr (!HOLD) lane_terms(lrow, pc);
             const uint32_t lro = uint32_t(lrow) * uint32_t(cache_row_bytes);
             const bool one_block = (1 << p.block_shift) >= 16;
 #pragma unroll
@@ -425,19 +444,27 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                 const bool second = !one_block && j >= NJ / 2;
                 const int64_t off = second ? off1 : off0;
                 const uint32_t soff = uint32_t((second ? j - NJ / 2 : j) * RPI) * uint32_t(cache_row_bytes);
-                dma16(kc_bytes + off, lro + k_chunk(lrow, pc, j), soff, kdst + (NJ * wave + j) * 512);
-                dma16(vc_bytes + off, lro + v_chunk(lrow, pc, j), soff, vdst + (NJ * wave + j) * 512);
+                const uint32_t kl = HOLD ? koc[j % NH] : lro + k_chunk(lrow, pc, j);
+                const uint32_t vl = HOLD ? voc[j % NH] : lro + v_chunk(lrow, pc, j);
+                dma16(kc_bytes + off, kl, soff, kdst + (NJ * wave + j) * 512);
+                dma16(vc_bytes + off, vl, soff, vdst + (NJ * wave + j) * 512);
             }
         } else if (w0 >= si.c && w0 + 15 <= key_hi) {
             const int64_t off = int64_t(si.start + (w0 - si.c)) * new_row_bytes + head_off;
+            int lrow = 0, pc = 0;
+            if constexpr (!HOLD) lane_terms(lrow, pc);
             const uint32_t lro = uint32_t(lrow) * uint32_t(new_row_bytes);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const uint32_t soff = uint32_t(j * RPI) * uint32_t(new_row_bytes);
-                dma16(kn_bytes + off, lro + k_chunk(lrow, pc, j), soff, kdst + (NJ * wave + j) * 512);
-                dma16(vn_bytes + off, lro + v_chunk(lrow, pc, j), soff, vdst + (NJ * wave + j) * 512);
+                const uint32_t kl = HOLD ? kon[j % NH] : lro + k_chunk(lrow, pc, j);
+                const uint32_t vl = HOLD ? von[j % NH] : lro + v_chunk(lrow, pc, j);
+                dma16(kn_bytes + off, kl, soff, kdst + (NJ * wave + j) * 512);
+                dma16(vn_bytes + off, vl, soff, vdst + (NJ * wave + j) * 512);
             }
         } else {
+            int lrow, pc;
+            lane_terms(lrow, pc);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int kk = min(w0 + j * RPI + lrow, key_hi);
