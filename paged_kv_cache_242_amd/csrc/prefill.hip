@@ -505,6 +505,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     for (int u = 0; u < DB; ++u) v_off[u] = (4 * lg + va) * D + ((u ^ vswz<D>(4 * lg + va)) << 4) + 4 * (l16 & 3);
 
     float m_run[2] = {-INFINITY, -INFINITY};   // row max (base 2), uniform over the row's 4 lanes
+    // kept beside it, changed only when it is raised: the raise threshold m_run + kRescaleSlack and
+    // the exponent's finite stand-in for m_run (0 while no visible key has been seen)
+    float m_thr[2] = {-INFINITY, -INFINITY};
+    float m_fin[2] = {0.f, 0.f};
     floatx4_v o[2][DB];
     // Row sums of the rounded weights, accumulated by the MFMA unit: an all-ones block times P^T
     // gives sum_k P[q][k] in every element of lane (q, .).
@@ -627,11 +631,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) {
             crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
-            float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), fmaxf(s[0][qbk][2], s[0][qbk][3]));
-            mx = fmaxf(mx, fmaxf(fmaxf(s[1][qbk][0], s[1][qbk][1]), fmaxf(s[1][qbk][2], s[1][qbk][3])));
+            // a chain of three-way maxima (exact in any order)
+            float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), s[0][qbk][2]);
+            mx = fmaxf(fmaxf(mx, s[0][qbk][3]), s[1][qbk][0]);
+            mx = fmaxf(fmaxf(mx, s[1][qbk][1]), s[1][qbk][2]);
+            mx = fmaxf(mx, s[1][qbk][3]);
             tmax[qbk] = fmaf(mx, s_mul, crow[qbk]);
         }
-        const bool raise = tmax[0] > m_run[0] + kRescaleSlack || tmax[1] > m_run[1] + kRescaleSlack;
+        const bool raise = tmax[0] > m_thr[0] || tmax[1] > m_thr[1];
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) {
@@ -639,6 +646,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                 const float m_new = fmaxf(m_run[qbk], r);
                 const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
                 m_run[qbk] = m_new;
+                m_thr[qbk] = m_new + kRescaleSlack;
+                m_fin[qbk] = m_new == -INFINITY ? 0.f : m_new;
                 lsum[qbk] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         V8 pb[2];
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) {
-            const float off = crow[qbk] - (m_run[qbk] == -INFINITY ? 0.f : m_run[qbk]);
+            const float off = crow[qbk] - m_fin[qbk];
             uint32_t pk[2][2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
