@@ -22,7 +22,8 @@ Prints ONE JSON line:
                 GB/s to and from pinned host memory (--no-block-moves skips them); and, also outside
                 the timed steps, decode and prefill over an FP8 (E4M3) copy of the cache (--no-fp8);
                 and prefill on long prompts (4 x 8192 new tokens, workload 2's head geometry), where
-                per-workgroup fixed costs are amortized (--no-long-prefill)
+                per-workgroup fixed costs are amortized (--no-long-prefill); and the cache write with
+                a cold Infinity Cache (512 MB written just before each timed call)
   roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s;
                 traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
                 (profiles/decode_traffic.json), null when the decode source changed since
@@ -207,6 +208,27 @@ def block_moves(pa, L, dev, num_pairs: int = 1024, reps: int = 10):
     return out
 
 
+def cold_cache_write_leg(pa, batch, cache, slots, layer, dev, reps: int = 10):
+    """Outside the timed steps: pa_cache_write timed after writing a 512 MB scratch buffer, so that
+    its ~70 MB of key/value rows and cache lines come from HBM rather than the 256 MB Infinity
+    Cache."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ts = []
+    for r in range(reps):
+        scratch.fill_(r & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pa.cache_write(batch.key, batch.value, cache, slots, layer)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del scratch
+    torch.cuda.empty_cache()
+    ms = float(np.median(ts))
+    gbps = cache_write_bytes(batch) / (ms * 1e-3) / 1e9
+    return {"ms": ms, "GB_per_s": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "flush_bytes": 512 << 20}
+
+
 def long_prefill_leg(pa, dev, reps: int = 5):
     """Outside the timed steps: causal prefill of 4 prompts of 8192 tokens with no cached context
     (32 query / 8 KV heads, head size 128, block size 16, bf16, seed 12).  Each wavefront then
@@ -373,6 +395,7 @@ def main(argv=None):
     cw_ms, _ = avg_ms("cw")
     cw_gbps = cache_write_bytes(batch) / (cw_ms * 1e-3) / 1e9
     secondary = {"cache_write": {"ms": cw_ms, "GB_per_s": cw_gbps, "frac_hbm_peak": cw_gbps / HBM_PEAK_GBPS}}
+    secondary["cache_write_cold"] = cold_cache_write_leg(pa, batch, cache, slots, layer, dev)
     if not args.no_block_moves:
         secondary.update(block_moves(pa, L, dev))
     if not args.no_fp8 and L.dtype != wl.F32:
