@@ -14,9 +14,13 @@ Each call is bracketed by HIP events on the stream it runs on (torch's current s
 per-call times are kernel times; the K timed steps are bracketed by torch.cuda.synchronize().
 
 Prints ONE JSON line:
-  value         decode KV-read throughput, GB/s = visible K+V bytes / decode time
+  value         decode KV-read throughput of the headline workload, GB/s = visible K+V bytes /
+                decode time (median over the timed steps)
   secondary     prefill attention TFLOP/s (4 * head_size flops per visible (row, key, head)),
-                cache-write GB/s (bytes read + written), each with its fraction of peak; and,
+                cache-write GB/s (bytes read + written), each with its fraction of peak and the
+                median / min / mean call times; `configs`: the other four workloads, each built,
+                timed (W warm-up + K timed calls of its own step) and freed in turn, with the same
+                rates and fractions (--no-configs skips them); and,
                 outside the timed steps, pa_copy_blocks GB/s (1024 scattered blocks of the
                 workload's geometry in a scratch cache, bytes read + written) and pa_swap_blocks
                 GB/s to and from pinned host memory (--no-block-moves skips them); and, also outside
@@ -28,7 +32,8 @@ Prints ONE JSON line:
                 traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
                 (profiles/decode_traffic.json), null when the decode source changed since
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample of the same
-                workload (decode sequences), in the same GB/s unit
+                workload: decode sequences (GB/s of visible K+V, `value`) and prefill rows
+                (GFLOP/s, `prefill`), with the thread count and the CPU model
 """
 from __future__ import annotations
 
@@ -122,15 +127,65 @@ def copy_probe(gib: float):
     return 0
 
 
-def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def oracle_layer(L):
+    import oracle
+    return oracle.OracleLayer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks,
+                              oracle.DTYPE_F32 if L.dtype == wl.F32 else oracle.DTYPE_BF16, L.scale,
+                              L.alibi_slopes, L.sliding_window)
+
+
+def cpu_prefill_baseline(batch: wl.PagedBatch, pool: np.ndarray, budget_s: float = 12.0):
+    """Time the oracle's prefill on this machine's host cores over a bounded sample of the prefill
+    rows of the same batch (every k-th row, k sized for ~budget_s of CPU work), in GFLOP/s of the
+    same algorithmic count as the GPU figure (4 * head_size per visible (row, key, head))."""
+    import oracle
+    L = batch.layer
+    ol = oracle_layer(L)
+    tp = batch.num_prefill_tokens
+    q, k, v = (wl.host_bits(x[:tp]) for x in (batch.query, batch.key, batch.value))
+    W = L.sliding_window
+    # visible keys of every prefill row
+    vis = np.zeros(tp, dtype=np.int64)
+    for i, (c, n) in enumerate(zip(batch.prefill_context_lens, batch.prefill_query_lens)):
+        a = int(batch.prefill_cu[i])
+        pos = int(c) + np.arange(int(n), dtype=np.int64)
+        vis[a:a + int(n)] = np.minimum(pos + 1, W) if W and W > 0 else pos + 1
+    per_vis = L.num_heads * 4 * L.head_size
+    stride = max(1, tp // 16)
+    used = 0
+    while True:
+        sel = np.zeros(tp, dtype=bool)
+        sel[::stride] = True
+        t0 = time.perf_counter()
+        _, used = oracle.prefill(ol, q, k, v, pool, batch.prefill_block_tables, batch.prefill_context_lens,
+                                 batch.prefill_cu, row_select=sel, return_threads=True)
+        dt = time.perf_counter() - t0
+        flops = int(vis[sel].sum()) * per_vis
+        if dt >= 0.5 * budget_s or stride == 1:
+            break
+        stride = max(1, int(stride * dt / budget_s))
+    return {"value": flops / dt / 1e9, "unit": "GFLOP/s", "cores": int(used),
+            "sample": f"fp64 oracle prefill of {int(sel.sum())} of the {tp} prefill rows of the same batch "
+                      f"(every {stride}th row; {flops / 1e9:.1f} GFLOP, {dt:.1f} s)"}
+
+
+def cpu_baseline(batch: wl.PagedBatch, pool: np.ndarray, budget_s: float = 20.0):
     """Time the oracle's decode on this machine's host cores over a bounded sample of the
     decode sequences of the same batch (longest-first is not used: a seeded random subset)."""
     import oracle
     L = batch.layer
-    ol = oracle.OracleLayer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks,
-                            oracle.DTYPE_F32 if L.dtype == wl.F32 else oracle.DTYPE_BF16, L.scale,
-                            L.alibi_slopes, L.sliding_window)
-    pool = wl.host_bits(cache)                                  # exact bytes the GPU used
+    ol = oracle_layer(L)
     tp = batch.num_prefill_tokens
     q = wl.host_bits(batch.query[tp:])
     lens = batch.decode_seq_lens
@@ -168,8 +223,8 @@ def cpu_baseline(batch: wl.PagedBatch, cache: torch.Tensor, budget_s: float = 20
         "kind": "oracle",
         "sample": f"fp64 oracle decode of {calls} sequences ({calls / len(lens):.1f} passes over the {len(lens)} "
                   f"decode sequences of the same batch, seeded order; {done_bytes / 1e9:.2f} GB of visible K+V, "
-                  f"{done_time:.1f} s), cpu "
-                  f"{platform.processor() or platform.machine()}",
+                  f"{done_time:.1f} s) on {cpu_model()}",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -302,12 +357,155 @@ def fp8_cache_leg(pa, L, layer, cache, dev, dec_args, pre_args, reps: int = 10):
     return res
 
 
+def ms_stats(ts):
+    ts = [float(t) for t in ts]
+    return {"ms": float(np.median(ts)), "ms_min": float(np.min(ts)), "ms_mean": float(np.mean(ts))}
+
+
+def decode_side_bytes(batch: wl.PagedBatch) -> dict:
+    """Bytes a decode call moves beside the visible K+V (not part of the algorithmic count):
+    query rows read, output rows written, block-table entries of the visible blocks read."""
+    L = batch.layer
+    B = len(batch.decode_seq_lens)
+    lens = batch.decode_seq_lens.astype(np.int64)
+    return {"query_bytes": B * L.num_heads * L.head_size * L.elt_bytes,
+            "out_bytes": B * L.num_heads * L.head_size * L.elt_bytes,
+            "block_table_bytes": int(((lens + L.block_size - 1) // L.block_size).sum()) * 4}
+
+
+class StepRunner:
+    """One workload's step (cache write, prefill, decode; each present part) on the GPU with HIP
+    events around every call on the stream the calls run on."""
+
+    def __init__(self, pa, W, dev, layer_kw=None):
+        self.pa, self.W, self.dev = pa, W, dev
+        t0 = time.perf_counter()
+        batch = W.batch(dev)
+        L = batch.layer
+        self.L = L
+        slopes = torch.tensor(L.alibi_slopes, device=dev) if L.alibi_slopes is not None else None
+        self.layer = pa.Layer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks, L.torch_dtype,
+                              L.scale, slopes, L.sliding_window)
+        self.cache = torch.full((2, L.num_blocks, L.block_size * L.row_elems), float("nan"), dtype=L.torch_dtype,
+                                device=dev)
+        if batch.ctx_key.shape[0]:
+            pa.cache_write(batch.ctx_key, batch.ctx_value, self.cache, torch.as_tensor(batch.ctx_slots, device=dev),
+                           self.layer)
+        batch.ctx_key = batch.ctx_value = None                       # context is in the cache now
+        self.batch = batch
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        self.setup_s = time.perf_counter() - t0
+        i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
+        self.slots = torch.as_tensor(batch.slot_mapping, device=dev)
+        tp = batch.num_prefill_tokens
+        self.tp = tp
+        self.has_pre = len(batch.prefill_context_lens) > 0
+        self.has_dec = len(batch.decode_seq_lens) > 0
+        if self.has_pre:
+            self.p_bt, self.p_ctx, self.p_cu = (i32(batch.prefill_block_tables), i32(batch.prefill_context_lens),
+                                                i32(batch.prefill_cu))
+            self.p_maxq, self.p_maxc = int(batch.prefill_query_lens.max()), int(batch.prefill_context_lens.max())
+            self.q_pre, self.k_pre, self.v_pre = batch.query[:tp], batch.key[:tp], batch.value[:tp]
+            self.out_pre = torch.empty_like(self.q_pre)
+        if self.has_dec:
+            self.d_bt, self.d_sl = i32(batch.decode_block_tables), i32(batch.decode_seq_lens)
+            self.d_max = int(batch.decode_seq_lens.max())
+            self.q_dec = batch.query[tp:]
+            self.out_dec = torch.empty_like(self.q_dec)
+            ws_bytes = pa.decode_workspace_size(self.layer, len(batch.decode_seq_lens), self.d_max)
+            self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def prefill(self):
+        self.pa.prefill_varlen(self.q_pre, self.k_pre, self.v_pre, self.cache, self.p_bt, self.p_ctx, self.p_cu,
+                               self.layer, self.p_maxq, self.p_maxc, out=self.out_pre)
+
+    def decode(self):
+        self.pa.decode(self.q_dec, self.cache, self.d_bt, self.d_sl, self.layer, self.d_max, out=self.out_dec,
+                       workspace=self.ws)
+
+    def run(self, steps: int, warmup: int):
+        """warmup + steps steps; returns per-call times (ms) of the timed steps and the wall time of
+        the timed steps (bracketed by torch.cuda.synchronize())."""
+        parts = [("cw", lambda: self.pa.cache_write(self.batch.key, self.batch.value, self.cache, self.slots,
+                                                      self.layer))]
+        if self.has_pre:
+            parts.append(("pre", self.prefill))
+        if self.has_dec:
+            parts.append(("dec", self.decode))
+        n = steps + warmup
+        ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+              for k, _ in parts}
+
+        def step(s):
+            for k, fn in parts:
+                ev[k][s][0].record(self.stream)
+                fn()
+                ev[k][s][1].record(self.stream)
+
+        for s in range(warmup):
+            step(s)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(warmup, n):
+            step(s)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        times = {k: [ev[k][s][0].elapsed_time(ev[k][s][1]) for s in range(warmup, n)] for k, _ in parts}
+        return times, wall
+
+    def results(self, times):
+        b = self.batch
+        out = {}
+        cw = ms_stats(times["cw"])
+        gbps = cache_write_bytes(b) / (cw["ms"] * 1e-3) / 1e9
+        out["cache_write"] = dict(cw, bytes_per_call=cache_write_bytes(b), GB_per_s=gbps,
+                                  frac_hbm_peak=gbps / HBM_PEAK_GBPS)
+        if self.has_pre:
+            st = ms_stats(times["pre"])
+            flops = prefill_flops(b)
+            tf = flops / (st["ms"] * 1e-3) / 1e12
+            out["prefill"] = dict(st, gflop_per_call=flops / 1e9, TFLOP_per_s=tf,
+                                  frac_mfma_peak=tf / MFMA_BF16_PEAK_TFLOPS, rows=self.tp,
+                                  seqs=int(len(b.prefill_context_lens)))
+        if self.has_dec:
+            st = ms_stats(times["dec"])
+            nbytes = decode_bytes(b)
+            gbps = nbytes / (st["ms"] * 1e-3) / 1e9
+            out["decode"] = dict(st, gb_per_call=nbytes / 1e9, GB_per_s=gbps, frac_hbm_peak=gbps / HBM_PEAK_GBPS,
+                                 seqs=int(len(b.decode_seq_lens)), **decode_side_bytes(b))
+        return out
+
+    def free(self):
+        for name in list(vars(self)):
+            if name not in ("pa", "W", "dev", "L", "setup_s"):
+                delattr(self, name)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def config_leg(pa, k: int, dev, steps: int, warmup: int):
+    """Workload k built, timed and freed: its own step (cache write, prefill and / or decode)."""
+    W = wl.workload(k)
+    log(f"config {k}: {W.description}")
+    r = StepRunner(pa, W, dev)
+    times, _ = r.run(steps, warmup)
+    res = r.results(times)
+    res["workload"] = f"{W.name}: {W.description}"
+    res["setup_s"] = round(r.setup_s, 1)
+    r.free()
+    del r
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-configs", action="store_true", help="skip the legs of the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-moves", action="store_true", help="skip the copy_blocks / swap_blocks timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache timing")
@@ -329,113 +527,70 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     W = wl.workload(args.workload)
     log(f"workload {args.workload}: {W.description}")
-    t0 = time.perf_counter()
-    batch = W.batch(dev)
-    L = batch.layer
-    slopes = torch.tensor(L.alibi_slopes, device=dev) if L.alibi_slopes is not None else None
-    layer = pa.Layer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks, L.torch_dtype, L.scale,
-                     slopes, L.sliding_window)
-    cache = torch.full((2, L.num_blocks, L.block_size * L.row_elems), float("nan"), dtype=L.torch_dtype, device=dev)
-    if batch.ctx_key.shape[0]:
-        pa.cache_write(batch.ctx_key, batch.ctx_value, cache, torch.as_tensor(batch.ctx_slots, device=dev), layer)
-    batch.ctx_key = batch.ctx_value = None                       # context is in the cache now
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    log(f"setup {time.perf_counter() - t0:.1f} s; pool {cache.numel() * cache.element_size() / 1e9:.2f} GB")
-
-    i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
-    slots = torch.as_tensor(batch.slot_mapping, device=dev)
-    tp = batch.num_prefill_tokens
-    has_pre = len(batch.prefill_context_lens) > 0
-    has_dec = len(batch.decode_seq_lens) > 0
-    if has_pre:
-        p_bt, p_ctx, p_cu = i32(batch.prefill_block_tables), i32(batch.prefill_context_lens), i32(batch.prefill_cu)
-        p_maxq, p_maxc = int(batch.prefill_query_lens.max()), int(batch.prefill_context_lens.max())
-        q_pre, k_pre, v_pre = batch.query[:tp], batch.key[:tp], batch.value[:tp]
-        out_pre = torch.empty_like(q_pre)
-    if has_dec:
-        d_bt, d_sl = i32(batch.decode_block_tables), i32(batch.decode_seq_lens)
-        d_max = int(batch.decode_seq_lens.max())
-        q_dec = batch.query[tp:]
-        out_dec = torch.empty_like(q_dec)
-        ws_bytes = pa.decode_workspace_size(layer, len(batch.decode_seq_lens), d_max)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-
-    stream = torch.cuda.current_stream(dev)
-    n_ev = 2 * (args.steps + args.warmup)
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("cw", "pre", "dec")}
-
-    def step(s):
-        ev["cw"][2 * s].record(stream)
-        pa.cache_write(batch.key, batch.value, cache, slots, layer)
-        ev["cw"][2 * s + 1].record(stream)
-        if has_pre:
-            ev["pre"][2 * s].record(stream)
-            pa.prefill_varlen(q_pre, k_pre, v_pre, cache, p_bt, p_ctx, p_cu, layer, p_maxq, p_maxc, out=out_pre)
-            ev["pre"][2 * s + 1].record(stream)
-        if has_dec:
-            ev["dec"][2 * s].record(stream)
-            pa.decode(q_dec, cache, d_bt, d_sl, layer, d_max, out=out_dec, workspace=ws)
-            ev["dec"][2 * s + 1].record(stream)
-
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.warmup, args.warmup + args.steps):
-        step(s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    R = StepRunner(pa, W, dev)
+    L, batch, layer, cache = R.L, R.batch, R.layer, R.cache
+    log(f"setup {R.setup_s:.1f} s; pool {cache.numel() * cache.element_size() / 1e9:.2f} GB")
+    times, wall = R.run(args.steps, args.warmup)
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+    secondary = R.results(times)
 
-    def avg_ms(key):
-        ts = [ev[key][2 * s].elapsed_time(ev[key][2 * s + 1]) for s in range(args.warmup, args.warmup + args.steps)]
-        return float(np.mean(ts)), float(np.min(ts))
-
-    cw_ms, _ = avg_ms("cw")
-    cw_gbps = cache_write_bytes(batch) / (cw_ms * 1e-3) / 1e9
-    secondary = {"cache_write": {"ms": cw_ms, "GB_per_s": cw_gbps, "frac_hbm_peak": cw_gbps / HBM_PEAK_GBPS}}
-    secondary["cache_write_cold"] = cold_cache_write_leg(pa, batch, cache, slots, layer, dev)
+    secondary["cache_write_cold"] = cold_cache_write_leg(pa, batch, cache, R.slots, layer, dev)
     if not args.no_block_moves:
         secondary.update(block_moves(pa, L, dev))
     if not args.no_fp8 and L.dtype != wl.F32:
         secondary["fp8_cache"] = fp8_cache_leg(
             pa, L, layer, cache, dev,
-            (q_dec, d_bt, d_sl, d_max, decode_bytes(batch)) if has_dec else None,
-            (q_pre, k_pre, v_pre, p_bt, p_ctx, p_cu, p_maxq, p_maxc, prefill_flops(batch)) if has_pre else None)
+            (R.q_dec, R.d_bt, R.d_sl, R.d_max, decode_bytes(batch)) if R.has_dec else None,
+            (R.q_pre, R.k_pre, R.v_pre, R.p_bt, R.p_ctx, R.p_cu, R.p_maxq, R.p_maxc, prefill_flops(batch))
+            if R.has_pre else None)
     if not args.no_long_prefill and L.dtype != wl.F32:
         secondary["prefill_long_prompts"] = long_prefill_leg(pa, dev)
-    value = None
-    unit = "GB/s"
-    roofline = None
-    if has_pre:
-        pre_ms, pre_min = avg_ms("pre")
-        flops = prefill_flops(batch)
-        tflops = flops / (pre_ms * 1e-3) / 1e12
-        secondary["prefill"] = {"ms": pre_ms, "ms_min": pre_min, "gflop_per_call": flops / 1e9, "TFLOP_per_s": tflops,
-                                "frac_mfma_peak": tflops / MFMA_BF16_PEAK_TFLOPS}
-    if has_dec:
-        dec_ms, dec_min = avg_ms("dec")
-        nbytes = decode_bytes(batch)
-        gbps = nbytes / (dec_ms * 1e-3) / 1e9
-        value = gbps
-        secondary["decode"] = {"ms": dec_ms, "ms_min": dec_min, "gb_per_call": nbytes / 1e9, "GB_per_s": gbps,
-                               "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
-        roofline = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
-                    "kernel": "decode_split_kernel (+ decode_plan_kernel and decode_merge_kernel: one pa_decode call)",
-                    "algorithmic_bytes_per_launch": nbytes}
+
+    value, unit = None, "GB/s"
+    if R.has_dec:
+        d = secondary["decode"]
+        value = d["GB_per_s"]
+        roofline = {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": value / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
+                    "kernel": "pa_decode (decode_plan_kernel + decode_split_kernel + decode_merge_kernel)",
+                    "algorithmic_bytes_per_launch": decode_bytes(batch), "ms_median": d["ms"]}
     else:
-        value = secondary["prefill"]["TFLOP_per_s"]
-        unit = "TFLOP/s"
+        value, unit = secondary["prefill"]["TFLOP_per_s"], "TFLOP/s"
         roofline = {"bound": "mfma", "achieved": value, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": value / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_mfma_kernel",
-                    "algorithmic_flops_per_launch": prefill_flops(batch)}
+                    "algorithmic_flops_per_launch": prefill_flops(batch), "ms_median": secondary["prefill"]["ms"]}
+    if R.has_pre and R.has_dec:
+        p = secondary["prefill"]
+        secondary["prefill_roofline"] = {"bound": "mfma", "achieved": p["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": p["frac_mfma_peak"],
+                                         "kernel": "prefill_mfma_kernel",
+                                         "algorithmic_flops_per_launch": prefill_flops(batch)}
 
     cpu = None
-    if not args.no_cpu_baseline and has_dec:
+    if not args.no_cpu_baseline and (R.has_dec or R.has_pre):
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(batch, cache, args.cpu_budget)
+        pool = wl.host_bits(cache)                                  # exact bytes the GPU used
+        if R.has_dec:
+            cpu = cpu_baseline(batch, pool, args.cpu_budget * (0.5 if R.has_pre else 1.0))
+        if R.has_pre:
+            pre = cpu_prefill_baseline(batch, pool, args.cpu_budget * (0.5 if R.has_dec else 1.0))
+            if cpu is None:
+                cpu = dict(pre, kind="oracle", cpu_model=cpu_model())
+            else:
+                cpu["prefill"] = pre
+        del pool
+
+    cfg_info = {"workload": f"{W.name} (config {W.index}): {W.description}", "seed": W.seed,
+                "num_tokens": batch.num_tokens, "prefill_rows": R.tp if R.has_pre else 0,
+                "decode_seqs": int(len(batch.decode_seq_lens)), "parallelism": "single GPU"}
+    R.free()
+    del R, batch, cache
+    if not args.no_configs:
+        configs = {}
+        for k in (1, 2, 3, 4, 5):
+            if k != args.workload:
+                configs[str(k)] = config_leg(pa, k, dev, args.steps, args.warmup)
+        secondary["configs"] = configs
 
     line = {
         "metric": METRIC,
@@ -450,10 +605,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": L.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{W.name} (config {W.index}): {W.description}", "seed": W.seed,
-                   "num_tokens": batch.num_tokens, "prefill_rows": tp,
-                   "decode_seqs": int(len(batch.decode_seq_lens)),
-                   "parallelism": "single GPU"},
+        "config": cfg_info,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
