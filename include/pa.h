@@ -5,7 +5,8 @@
  * pointer.  The library (libpa.so) never allocates device memory, never synchronizes the
  * device and never reads device buffers on the host; all work is enqueued on the HIP stream
  * the caller passes (NULL = the legacy default stream).  Calls are reentrant: the only
- * global state is a per-device attribute cache and a thread-local error message.
+ * global state is a per-device attribute cache, a thread-local error message and the fixed
+ * scratch array that pa_decode_noalloc uses in place of a workspace.
  *
  * The problem statement follows the reference pages:
  *   - query  [num_tokens, num_heads * head_size]
@@ -174,6 +175,25 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
                     const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
                     const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * Decode without any allocation, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid it).  The
+ * same computation and kernels as pa_decode; the workspace is a fixed device array of
+ * 32 MiB (33554432 bytes) inside the library, one per GPU, held until the process ends.
+ *   Arguments as in pa_decode, without workspace / workspace_bytes.
+ *   A batch whose pa_decode_workspace_size() exceeds 32 MiB returns PA_ERR_WORKSPACE and
+ *   launches nothing (use pa_decode with a caller workspace for it).
+ *   The array of the calling thread's current device is used; the stream must belong to that
+ *   device.  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ *   streams, other host threads) race and give unspecified results.  Nothing in the array needs
+ *   to start at zero; each call writes every byte it later reads.
+ * No hipMalloc, hipFree or other allocating call is made; the array's device address is looked up
+ * once per device (hipGetSymbolAddress) on the first call there.
+ */
+pa_status pa_decode_noalloc(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                            const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, void *stream);
 
 /*
  * Multi-token decode: the uniform batches of 1 + speculative tokens that the pages let a backend

@@ -31,7 +31,8 @@ PA_DTYPE_F16 = 2
 PA_KV_CACHE_AUTO = 0
 PA_KV_CACHE_FP8_E4M3 = 1
 
-EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_decode_multi", "pa_decode_multi_workspace_size",
+EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_multi",
+            "pa_decode_multi_workspace_size",
             "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string", "pa_last_error_message",
             "pa_version")
 
@@ -74,6 +75,8 @@ def _load_library(path: str = LIB_PATH):
     lib.pa_decode_workspace_size.restype = SZ
     lib.pa_decode.argtypes = [LP, P, P, I64, P, P, I32, P, I32, I32, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [LP, P, P, I64, P, P, I32, P, I32, I32, P]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_multi_workspace_size.argtypes = [LP, I32, I32, I32]
     lib.pa_decode_multi_workspace_size.restype = SZ
     lib.pa_decode_multi.argtypes = [LP, P, P, I64, P, P, I32, P, I32, I32, I32, P, SZ, P]
@@ -284,6 +287,27 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tens
         _check(_lib.pa_decode_multi(ctypes.byref(c), out.data_ptr(), query.data_ptr(), qs, _cache(kv_cache, layer),
                                     bt, block_tables.shape[1], sl, B, int(query_len), int(max_seq_len), ws_ptr,
                                     ws_bytes, _stream(query.device)))
+    return out
+
+
+def decode_noalloc(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                   layer: Layer, max_seq_len: int, out: torch.Tensor) -> torch.Tensor:
+    """Decode through pa_decode_noalloc: the library's fixed device scratch array replaces the
+    workspace, and ``out`` must be passed (nothing is allocated)."""
+    width = layer.num_heads * layer.head_size
+    qs = _rows(query, "query", width, layer.dtype)
+    B = seq_lens.numel()
+    if query.shape[0] != B:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, f"query has {query.shape[0]} rows, expected {B}")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, "block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    bt = _index(block_tables, "block_tables", torch.int32)
+    sl = _index(seq_lens, "seq_lens", torch.int32, (B,))
+    if tuple(out.shape) != (B, width) or not out.is_contiguous() or out.dtype != layer.dtype:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, "out must be a contiguous [num_seqs, H*D] tensor of the layer dtype")
+    c = layer._c()
+    _check(_lib.pa_decode_noalloc(ctypes.byref(c), out.data_ptr(), query.data_ptr(), qs, _cache(kv_cache, layer), bt,
+                                  block_tables.shape[1], sl, B, int(max_seq_len), _stream(query.device)))
     return out
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/pa.h"
 #include "pa_kernels.h"
 
@@ -86,6 +88,36 @@ pa_status decode_impl(const char *fn, const pa_layer *layer, void *out, const vo
                       const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
                       const int32_t *seq_lens, int32_t num_seqs, int32_t query_len, int32_t max_seq_len,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+// ---- pa_decode_noalloc: the decode workspace lives in a fixed device array instead of caller
+// memory.  Every GPU the library runs on holds its own copy of `scratch` (at its own address) until
+// the process ends.  In host code the name is only a stand-in for the symbol, never a device
+// address: the address is looked up once per device with hipGetSymbolAddress, with that device
+// current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+pa_status scratch_address(const char *fn, void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
 
 }  // namespace
 
@@ -221,6 +253,29 @@ pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t
                     int32_t num_seqs, int32_t max_seq_len, void *workspace, size_t workspace_bytes, void *stream) {
     return decode_impl("pa_decode", layer, out, query, q_row_stride, kv_cache, block_tables, max_blocks_per_seq,
                        seq_lens, num_seqs, 1, max_seq_len, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
+                            const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, void *stream) {
+    const char *fn = "pa_decode_noalloc";
+    pa_status st = check_layer(layer, fn);
+    if (st != PA_OK) return st;
+    void *ws = nullptr;
+    if (num_seqs > 0 && max_seq_len >= 0) {
+        const size_t need = pa_decode_workspace_size(layer, num_seqs, max_seq_len);
+        if (need > kScratchBytes)
+            return fail(PA_ERR_WORKSPACE,
+                        "%s: %d sequences need %zu bytes of decode scratch, more than the %zu-byte device array; "
+                        "use pa_decode with a caller workspace",
+                        fn, num_seqs, need, kScratchBytes);
+        if (need > 0) {
+            st = scratch_address(fn, &ws);
+            if (st != PA_OK) return st;
+        }
+    }
+    return decode_impl(fn, layer, out, query, q_row_stride, kv_cache, block_tables, max_blocks_per_seq, seq_lens,
+                       num_seqs, 1, max_seq_len, ws, ws ? kScratchBytes : 0, stream);
 }
 
 pa_status pa_decode_multi(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,

@@ -22,7 +22,7 @@ def pa():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["pa_cache_write", "pa_decode", "pa_decode_workspace_size",
+    assert declared_functions() == sorted(["pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_decode_noalloc",
                                            "pa_decode_multi", "pa_decode_multi_workspace_size",
                                            "pa_prefill_varlen", "pa_copy_blocks", "pa_swap_blocks",
                                            "pa_status_string", "pa_last_error_message", "pa_version"])
@@ -79,7 +79,20 @@ def test_zero_sizes_are_noops(pa):
     assert lib.pa_decode(ctypes.byref(c), None, None, 1024, None, None, 1, None, 0, 0, None, 0, None) == 0
     assert lib.pa_prefill_varlen(ctypes.byref(c), None, None, 1024, None, None, 256, None, None, 0, None, None, 0, 0,
                                  0, 0, None) == 0
+    assert lib.pa_decode_noalloc(ctypes.byref(c), None, None, 1024, None, None, 1, None, 0, 0, None) == 0
     assert lib.pa_last_error_message() == b""
+
+
+def test_decode_noalloc_rejects_batches_beyond_its_scratch(pa):
+    """pa_decode_noalloc checks the batch's workspace size against its fixed 32 MiB array on the
+    host and returns PA_ERR_WORKSPACE, launching nothing, when it does not fit."""
+    lib = pa.library()
+    c = _layer(pa, num_heads=32, num_kv_heads=8)
+    need = lib.pa_decode_workspace_size(ctypes.byref(c), 1 << 16, 4096)
+    assert need > 32 << 20
+    st = lib.pa_decode_noalloc(ctypes.byref(c), 256, 256, 4096, 256, 256, 256, 256, 1 << 16, 4096, None)
+    assert st == pa.PA_ERR_WORKSPACE
+    assert b"32" in lib.pa_last_error_message() and b"pa_decode_noalloc" in lib.pa_last_error_message()
 
 
 def test_bad_pointers_and_alignment(pa):
