@@ -69,6 +69,9 @@ pa_status check_layer(const pa_layer *L, const char *fn) {
     if (L->num_blocks > (int64_t(1) << 31))
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_blocks %lld exceeds int32 block ids", fn,
                     (long long)L->num_blocks);
+    if (int64_t(L->block_size) * L->num_kv_heads * L->head_size * 4 >= (int64_t(1) << 31))
+        return fail(PA_ERR_UNSUPPORTED, "%s: one cache block (block_size * num_kv_heads * head_size elements) must "
+                    "stay below 2^31 bytes", fn);
     if (!(L->scale == L->scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: scale is NaN", fn);
     if (!(L->logits_soft_cap == L->logits_soft_cap) || L->logits_soft_cap > 3.0e38f)
         return fail(PA_ERR_INVALID_ARGUMENT, "%s: logits_soft_cap must be finite", fn);

@@ -27,6 +27,8 @@
 // fp32 kernel: a plain wavefront-per-(row, head) VALU loop (no MFMA for fp32 here).
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -128,6 +130,18 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t lane_off, uint3
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, lane_off, soff, 0, 0);
 }
 
+// The same copy into the LDS byte address lds_addr.
+__device__ __forceinline__ void dma16_at(const char *base, uint32_t lane_off, uint32_t soff, uint32_t lds_addr) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)lds_addr, 16, lane_off, soff, 0, 0);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return uint32_t(uintptr_t((const lds_void *)p));
+}
+
 // The same copy from a per-lane address.
 __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
     __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)lds_dst, 16, 0, 0);
@@ -145,22 +159,21 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 // Each wavefront copies 16 keys (rows 16 w .. 16 w + 15) of each tile, which lie in one cache
 // block (two for 8-token blocks), so one descriptor per block and tile serves all its copies.
 //
-// Scores.  A wavefront's 32 rows meet a tile in two 32-key halves.  Per half the scores are
-// kept in raw units s (q.k, plus for ALiBi the in-half key offset times slope / |scale|, added
-// by one rank-1 MFMA per score block); the base-2 logit is s * |scale| log2(e) + c_row with a
-// per-row constant c_row (the ALiBi term of the half's first key, else 0).  A half is
+// Scores.  A wavefront's 32 rows meet a tile in two 32-key halves.  Q is multiplied by
+// scale log2(e) and rounded to the element type once, when it is loaded, so the score MFMAs
+// produce base-2 logits; their accumulators start at c_row - m, where c_row is the row's ALiBi
+// term for the half's first key (0 without ALiBi) and m the finite stand-in of the row's running
+// max, and ALiBi's in-half key offset times slope log2(e) is added by one rank-1 MFMA per score
+// block.  A score then leaves the MFMAs as the exponent of its weight.  A half is
 //   * empty for the wavefront when every (row, key) pair is masked -- skipped entirely;
 //   * full when none is -- no per-score work besides the max and the exponent;
 //   * partial otherwise -- masked scores are set to -inf.
-// A negative scale is folded into a sign flip of Q (exact in both 16-bit formats), a zero scale
-// into Q = 0.
 //
-// With a logits soft-cap c (SOFTCAP) the raw scores become c log2(e) tanh(s |scale| / c) right
-// after the score MFMAs, the ALiBi key term is added to them in fp32 (it must stay outside the
-// cap, so the rank-1 MFMA is not used), and the exponent takes them with a unit multiplier.  fp16
-// layers with ALiBi take the fp32 key term too (s |scale| log2(e) + term), since the rank-1
-// factor slope / |scale| need not fit fp16's range.  Sink logits (p.sinks) join the row sums in
-// the epilogue.
+// With a logits soft-cap c (SOFTCAP) the raw dot product must reach tanh, so Q keeps its values
+// (a negative scale folded into a sign flip of Q, exact in both 16-bit formats; a zero scale into
+// Q = 0); the raw scores become c log2(e) tanh(s |scale| / c) right after the score MFMAs, the
+// ALiBi key term is added to them in fp32 (it must stay outside the cap), and the exponent
+// subtracts the running max.  Sink logits (p.sinks) join the row sums in the epilogue.
 
 template <typename T>
 struct Operand8 { typedef bf16x8_v type; };   // 8 elements of an MFMA operand
@@ -222,20 +235,31 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     const int p0 = si.c + t0;                                  // its position
 
     const float qk_scale = p.scale * kLog2e;
-    const float qk_eff = qk_scale > 0.f ? qk_scale : (qk_scale < 0.f ? -qk_scale : 1.f);
+    // Without a soft-cap (PRE) Q is multiplied by scale log2(e) once, here, and rounded to the
+    // element type, so the score MFMAs produce base-2 logits directly; their accumulators start at
+    // the row's ALiBi term minus the running max, so a score leaves the MFMA ready for the
+    // exponent.  With a soft-cap the raw dot product must reach tanh, so Q keeps its values (a
+    // negative scale as a sign flip, exact; a zero scale as Q = 0).
+    constexpr bool PRE = !SOFTCAP;
     const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // sign flips of both halves
     const uint32_t qand = qk_scale == 0.f ? 0u : 0xffffffffu;
-    // The ALiBi key term rides on the score MFMAs (rank-1 update in 16-bit hi/lo parts) for bf16
-    // without a soft-cap; with a soft-cap it must stay outside the cap, and in fp16 the factor
-    // slope / |scale| could overflow, so there it is added in fp32 after the scores are formed.
-    constexpr bool KBIAS_MFMA = ALIBI && !SOFTCAP && !kIsF16<T>;
-    constexpr bool KBIAS_F32 = ALIBI && !KBIAS_MFMA;
-    // multiplier of the (transformed) scores in the exponent: |scale| log2(e), or 1 once they
-    // have been turned into base-2 logits
-    constexpr bool LOGITS = SOFTCAP || KBIAS_F32;
-    const float s_mul = LOGITS ? 1.f : qk_eff;
+    // The ALiBi key term rides on the score MFMAs as a rank-1 update (the factor slope log2(e) in
+    // 16-bit hi/lo parts) when Q is pre-scaled; with a soft-cap it must stay outside the cap, so
+    // there it is added in fp32 after the scores are formed.
+    constexpr bool KBIAS_MFMA = ALIBI && PRE;
+    constexpr bool KBIAS_F32 = ALIBI && !PRE;
+    // multiplier of the soft-capped scores in the exponent (they are base-2 logits already)
+    const float s_mul = 1.f;
     const float cap_in = SOFTCAP ? fabsf(p.scale) / p.softcap : 0.f;
     const float cap2 = SOFTCAP ? p.softcap * kLog2e : 0.f;
+    auto elt_lo = [](uint32_t w) -> float {
+        if constexpr (kIsF16<T>) return f16_to_f32(f16_t(uint16_t(w & 0xffffu)));
+        else return bf16_lo(w);
+    };
+    auto elt_hi = [](uint32_t w) -> float {
+        if constexpr (kIsF16<T>) return f16_to_f32(f16_t(uint16_t(w >> 16)));
+        else return bf16_hi(w);
+    };
 
     // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qbk + l16), d = 32 dc + 8 lg .. +7.
     V8 qf[2][DC];
@@ -247,10 +271,17 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
             uint4 w = *reinterpret_cast<const uint4 *>(qrow + 32 * dc);
-            w.x = (w.x ^ qxor) & qand;
-            w.y = (w.y ^ qxor) & qand;
-            w.z = (w.z ^ qxor) & qand;
-            w.w = (w.w ^ qxor) & qand;
+            if constexpr (PRE) {
+                uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ww[k] = pack_x2<T>(elt_lo(ww[k]) * qk_scale, elt_hi(ww[k]) * qk_scale);
+                w = make_uint4(ww[0], ww[1], ww[2], ww[3]);
+            } else {
+                w.x = (w.x ^ qxor) & qand;
+                w.y = (w.y ^ qxor) & qand;
+                w.z = (w.z ^ qxor) & qand;
+                w.w = (w.w ^ qxor) & qand;
+            }
             qf[qbk][dc] = __builtin_bit_cast(V8, w);
         }
     }
@@ -261,13 +292,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
     const int kt_lo = key_lo / kBN, kt_hi = key_hi / kBN;
 
-    // ALiBi: slope in base-2 units; the rank-1 MFMA term adds (key - half start) * slope2 / qk_eff
-    // to the raw scores, with the factor split into a high and a low 16-bit part (k slots 0 and 1).
+    // ALiBi: slope in base-2 units; the rank-1 MFMA term adds (key - half start) * slope2 to the
+    // base-2 logits, with slope2 split into a high and a low 16-bit part (k slots 0 and 1).
     float slope2 = 0.f;
     V8 bslope = {}, arel[2] = {};
     if constexpr (ALIBI) slope2 = p.alibi_slopes[h] * kLog2e;
     if constexpr (KBIAS_MFMA) {
-        const float ratio = slope2 / qk_eff;
+        const float ratio = slope2;
         const T hi = to_elt<T>(ratio);
         const T lo = to_elt<T>(ratio - elt_to_f32(hi));
         const uint32_t hl = lane < 16 ? (elt_bits(hi) | (elt_bits(lo) << 16)) : 0u;
@@ -469,8 +500,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             for (int j = 0; j < NJ; ++j) {
                 const int kk = min(w0 + j * RPI + lrow, key_hi);
                 const bool cached = kk < si.c;
-                const int64_t bl = clamp_block(
-                    p.block_tables[int64_t(seq) * p.max_blocks + (min(kk, max(si.c - 1, 0)) >> p.block_shift)]);
+                // the table is read only for cached rows: without a context it may be null
+                int64_t bl = 0;
+                if (cached) bl = clamp_block(p.block_tables[int64_t(seq) * p.max_blocks + (kk >> p.block_shift)]);
                 const int64_t off = cached ? bl * block_bytes + int64_t(kk & bmask) * cache_row_bytes + head_off
                                            : int64_t(si.start + (kk - si.c)) * new_row_bytes + head_off;
                 bf16_t *kd = kdst + (NJ * wave + j) * 512;
@@ -486,6 +518,87 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                     dma16_lane(vn_bytes + off + v_chunk(lrow, pc, j), vd);
                 }
             }
+        }
+    };
+
+    constexpr bool INTERLEAVE = false;
+    // ---- deferred copies.  The copies of the two fast paths (a wavefront's 16 rows all cached, or
+    // all new and at or below key_hi) are planned before the tile that streams them starts --
+    // scalar arithmetic only: a 32-bit block clamp and one 64-bit base per block, the value plane
+    // lying a constant distance from the key plane -- and issued one (K, V) pair after each group
+    // of score MFMAs of that tile's first half, so the matrix unit stays fed while they go out.
+    // Other tiles (mixed rows, an FP8 cache's cached rows) are copied by copy_tile up front.
+    const int nbm1 = int(p.num_blocks - 1);             // block ids fit int32 (checked on the host)
+    const uint32_t crow32 = uint32_t(cache_row_bytes), nrow32 = uint32_t(new_row_bytes);
+    const uint32_t blk32 = uint32_t(block_bytes);
+    const char *kc_head = kc_bytes + head_off;
+    const char *kn_head = kn_bytes + head_off;
+    const int64_t vc_diff = vc_bytes - kc_bytes;
+    const int64_t vn_diff = vn_bytes - kn_bytes;
+    const bool one_block = (1 << p.block_shift) >= 16;
+    struct CopyPlan {
+        const char *b0;      // key bytes of this wavefront's first row (its block for cached rows)
+        const char *b1;      // cached rows in a second block (block size 8): that block's key row 0
+        int mode;            // 0: nothing deferred, 1: cached rows, 2: new rows
+    };
+    auto plan_copy = [&](int kt, int id0_raw, int id1_raw) __attribute__((always_inline)) -> CopyPlan {
+        CopyPlan cp{nullptr, nullptr, 0};
+        const int w0 = kt * kBN + wrow0;
+        if (!C8 && w0 + 15 < si.c) {
+            const int b0 = min(max(id0_raw, 0), nbm1), b1 = min(max(id1_raw, 0), nbm1);
+            cp.b0 = kc_head + int64_t(uint32_t(b0)) * blk32 + uint32_t(w0 & bmask) * crow32;
+            cp.b1 = kc_head + int64_t(uint32_t(b1)) * blk32;
+            cp.mode = 1;
+        } else if (w0 >= si.c && w0 + 15 <= key_hi) {
+            cp.b0 = kn_head + int64_t(si.start + (w0 - si.c)) * nrow32;
+            cp.mode = 2;
+        }
+        return cp;
+    };
+    // Copy instruction pair j (tile rows 16 w + j RPI ..) of a planned tile into the LDS stretches
+    // at byte addresses kb + 1 KB j and vb + 1 KB j; soff is the pair's row offset in bytes.
+    // MODE is the plan's mode (1 or 2).
+    auto issue_pair = [&](const CopyPlan &cp, auto mode_c, int j, uint32_t kb, uint32_t vb, uint32_t soff)
+                          __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_c)::value;
+        int lrow = 0, pc = 0;
+        if constexpr (!HOLD) lane_terms(lrow, pc);
+        if constexpr (MODE == 1) {
+            const bool second = !one_block && j >= NJ / 2;
+            const char *base = second ? cp.b1 : cp.b0;
+            const uint32_t lro = uint32_t(lrow) * crow32;
+            const uint32_t kl = HOLD ? koc[j % NH] : lro + k_chunk(lrow, pc, j);
+            const uint32_t vl = HOLD ? voc[j % NH] : lro + v_chunk(lrow, pc, j);
+            dma16_at(base, kl, soff, kb + 1024u * j);
+            dma16_at(base + vc_diff, vl, soff, vb + 1024u * j);
+        } else {
+            const uint32_t lro = uint32_t(lrow) * nrow32;
+            const uint32_t kl = HOLD ? kon[j % NH] : lro + k_chunk(lrow, pc, j);
+            const uint32_t vl = HOLD ? von[j % NH] : lro + v_chunk(lrow, pc, j);
+            dma16_at(cp.b0, kl, soff, kb + 1024u * j);
+            dma16_at(cp.b0 + vn_diff, vl, soff, vb + 1024u * j);
+        }
+    };
+    // All copies of a planned tile (one branch on the mode per tile).  The tile's LDS bases and the
+    // row step pass through empty asm statements, so the compiler forms each copy's LDS address and
+    // row offset with one scalar add instead of holding every one of them in a register across the
+    // loop.
+    auto issue_all = [&](const CopyPlan &cp, bf16_t *kdst, bf16_t *vdst) __attribute__((always_inline)) {
+        uint32_t kb = lds_address(kdst) + 1024u * NJ * wave, vb = lds_address(vdst) + 1024u * NJ * wave;
+        asm volatile("" : "+s"(kb), "+s"(vb));
+        if (cp.mode == 1) {
+            uint32_t step = RPI * crow32;
+            asm volatile("" : "+s"(step));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t soff = (!one_block && j >= NJ / 2 ? j - NJ / 2 : j) * step;
+                issue_pair(cp, std::integral_constant<int, 1>(), j, kb, vb, soff);
+            }
+        } else if (cp.mode == 2) {
+            uint32_t step = RPI * nrow32;
+            asm volatile("" : "+s"(step));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) issue_pair(cp, std::integral_constant<int, 2>(), j, kb, vb, j * step);
         }
     };
 
@@ -549,33 +662,45 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // One 32-key half (keys k0h .. k0h + 31, key chunk kc of the tile in (ks, vs)); ka holds its
     // K operands on entry.  next_kc >= 0: the next half is chunk next_kc of the same tile, whose
     // K operands are read into ka here.
-    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs, int next_kc) __attribute__((always_inline)) {
+    // cp: a planned copy of the next tile into (kdn, vdn), issued during this half's score MFMAs.
+    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs, int next_kc, bool with_copy, CopyPlan cp,
+                    bf16_t *kdn, bf16_t *vdn) __attribute__((always_inline)) {
         // wavefront rows are positions p0 .. p0 + 31; a key is visible from pos iff
         // pos - W < key <= pos
         const bool empty = k0h > p0 + 31 || (p.window > 0 && k0h + 31 <= p0 - p.window);
         if (empty) {
+            if (with_copy) issue_all(cp, kdn, vdn);
             if (next_kc >= 0) load_k(ks, next_kc);
             return;
         }
         const bool full = k0h + 31 <= p0 && (p.window <= 0 || k0h > p0 + 31 - p.window);
 
         // ---- S^T = K Q^T (+ ALiBi term): s[kk][qbk] holds keys k0h + 16 kk + 4 lg + i of row 16 qbk + l16
+        // crow: the ALiBi term of the half's first key for the row (base 2), a per-row constant
+        float crow[2];
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
         floatx4_v s[2][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int qbk = 0; qbk < 2; ++qbk) {
+            // PRE: the scores come out as base-2 logits minus the finite stand-in of the running max
+            const float c0 = PRE ? crow[qbk] - m_fin[qbk] : 0.f;
 #pragma unroll
-            for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < 2; ++kk) s[kk][qbk] = floatx4_v{c0, c0, c0, c0};
+        }
         // Raised wave priority while the score MFMAs issue: when both wavefronts of a SIMD want the
         // matrix unit, this one goes first and the other turns to its exponentials, so the two
         // drift into alternating phases instead of colliding.
         __builtin_amdgcn_s_setprio(1);
+        static_assert(NJ == DC, "one copy pair per group of score MFMAs");
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
+        for (int dc = 0; dc < DC; ++dc) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int qbk = 0; qbk < 2; ++qbk)
                     s[kk][qbk] = mfma16(ka[dc][kk], qf[qbk][dc], s[kk][qbk]);
+        }
         if constexpr (KBIAS_MFMA) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -593,13 +718,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cap_in), kbias[kk][i]);
-        } else if constexpr (KBIAS_F32) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[kk][qbk][i] = fmaf(s[kk][qbk][i], qk_eff, kbias[kk][i]);
         }
 
         // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
@@ -626,28 +744,40 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             }
         }
 
-        // ---- running max (lazy: raised only when a row's max grows by more than kRescaleSlack)
-        float crow[2], tmax[2];
+        // ---- running max (lazy: raised only when a row's max grows by more than kRescaleSlack).
+        // PRE: tmax is relative to m_fin and m_thr holds the relative threshold (kRescaleSlack, or
+        // -inf until the row has seen a visible key); otherwise both are absolute.
+        float tmax[2];
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) {
-            crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
             // a chain of three-way maxima (exact in any order)
             float mx = fmaxf(fmaxf(s[0][qbk][0], s[0][qbk][1]), s[0][qbk][2]);
             mx = fmaxf(fmaxf(mx, s[0][qbk][3]), s[1][qbk][0]);
             mx = fmaxf(fmaxf(mx, s[1][qbk][1]), s[1][qbk][2]);
             mx = fmaxf(mx, s[1][qbk][3]);
-            tmax[qbk] = fmaf(mx, s_mul, crow[qbk]);
+            tmax[qbk] = PRE ? mx : fmaf(mx, s_mul, crow[qbk]);
         }
         const bool raise = tmax[0] > m_thr[0] || tmax[1] > m_thr[1];
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk) {
                 const float r = max_xor32(max_xor16(tmax[qbk]));
-                const float m_new = fmaxf(m_run[qbk], r);
+                const float m_new = fmaxf(m_run[qbk], PRE ? m_fin[qbk] + r : r);
                 const float alpha = (m_run[qbk] == -INFINITY) ? 0.f : fast_exp2(m_run[qbk] - m_new);
+                const float fin = m_new == -INFINITY ? 0.f : m_new;
+                if constexpr (PRE) {
+                    // this half's scores were formed against the old stand-in: move them to the new one
+                    const float delta = fin - m_fin[qbk];
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[kk][qbk][i] -= delta;
+                    m_thr[qbk] = m_new == -INFINITY ? -INFINITY : kRescaleSlack;
+                } else {
+                    m_thr[qbk] = m_new + kRescaleSlack;
+                }
                 m_run[qbk] = m_new;
-                m_thr[qbk] = m_new + kRescaleSlack;
-                m_fin[qbk] = m_new == -INFINITY ? 0.f : m_new;
+                m_fin[qbk] = fin;
                 lsum[qbk] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
@@ -668,7 +798,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             for (int kk = 0; kk < 2; ++kk) {
                 float pf[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pf[i] = fast_exp2(fmaf(s[kk][qbk][i], s_mul, off));
+                for (int i = 0; i < 4; ++i)
+                    pf[i] = fast_exp2(PRE ? s[kk][qbk][i] : fmaf(s[kk][qbk][i], s_mul, off));
                 pk[kk][0] = pack_x2<T>(pf[0], pf[1]);
                 pk[kk][1] = pack_x2<T>(pf[2], pf[3]);
             }
@@ -686,10 +817,11 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             lsum[qbk] = mfma16(ones, pb[qbk], lsum[qbk]);
     };
     // Tile kt from stage (ks, vs), second half first; the first half's K operands are read here.
-    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
-        load_k(ks, 1);
-        half(kt * kBN + 32, 1, ks, vs, 0);
-        half(kt * kBN, 0, ks, vs, -1);
+    // cp (or null): the next tile's planned copies into (kdn, vdn), issued during the first half.
+    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs, CopyPlan cp, bf16_t *kdn,
+                            bf16_t *vdn) __attribute__((always_inline)) {
+        half(kt * kBN + 32, 1, ks, vs, 0, INTERLEAVE && cp.mode != 0, cp, kdn, vdn);
+        half(kt * kBN, 0, ks, vs, -1, false, cp, kdn, vdn);
     };
 
     // ---- pipeline.  Tiles are taken from the last (nearest the diagonal) to the first: with
@@ -721,21 +853,33 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     asm volatile("" : "+v"(ids));
     __syncthreads();
     for (int kt = kt_hi; kt >= kt_lo; kt -= 2) {
+        CopyPlan cp{nullptr, nullptr, 0};
+        // the first half's K operands are read before the next tile's copies go out: the copies may
+        // stall at issue, and the reads (of the other LDS stage) need not wait behind them
+        load_k(Ks0, 1);
         if (kt > kt_lo) {
-            copy_tile(kt - 1, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks1, Vs1);
+            const int i0 = __builtin_amdgcn_readlane(ids, 0), i1 = __builtin_amdgcn_readlane(ids, 1);
+            cp = plan_copy(kt - 1, i0, i1);
+            if (cp.mode == 0) copy_tile(kt - 1, i0, i1, Ks1, Vs1);
+            else if (!INTERLEAVE) issue_all(cp, Ks1, Vs1);
             if (kt - 2 >= kt_lo) ids = fetch_ids(kt - 2);
         }
-        compute_tile(kt, Ks0, Vs0);
+        compute_tile(kt, Ks0, Vs0, cp, Ks1, Vs1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         fp8_commit(Ks1, Vs1);
         asm volatile("" : "+v"(ids));
         __syncthreads();
         if (kt - 1 < kt_lo) break;
+        CopyPlan cq{nullptr, nullptr, 0};
+        load_k(Ks1, 1);
         if (kt - 1 > kt_lo) {
-            copy_tile(kt - 2, __builtin_amdgcn_readlane(ids, 0), __builtin_amdgcn_readlane(ids, 1), Ks0, Vs0);
+            const int i0 = __builtin_amdgcn_readlane(ids, 0), i1 = __builtin_amdgcn_readlane(ids, 1);
+            cq = plan_copy(kt - 2, i0, i1);
+            if (cq.mode == 0) copy_tile(kt - 2, i0, i1, Ks0, Vs0);
+            else if (!INTERLEAVE) issue_all(cq, Ks0, Vs0);
             if (kt - 3 >= kt_lo) ids = fetch_ids(kt - 3);
         }
-        compute_tile(kt - 1, Ks1, Vs1);
+        compute_tile(kt - 1, Ks1, Vs1, cq, Ks0, Vs0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         fp8_commit(Ks0, Vs0);
         asm volatile("" : "+v"(ids));
