@@ -85,7 +85,11 @@ __device__ __forceinline__ void row_ptrs(const PrefillParams &p, const SeqInfo &
 // are dealt to the 8 XCDs round-robin by index, so the index is built as
 // ((group / 8) * group_size + member) * 8 + group % 8: the members of a group run back to back on
 // one XCD and share its L2, and each XCD takes every 8th group in heavy-first order (late query
-// tiles see the most keys).
+// tiles see the most keys).  Groups are enumerated by query-tile level (latest first), then
+// sequence, then KV head.  In compact mode (up to 64 sequences and 64 query-tile levels, one query
+// tile per group) a level lists only the sequences long enough to have that tile, so no workgroup
+// of the grid stands for a tile past a sequence's end; the grid is sized from num_tokens (at most
+// num_tokens / rows + num_seqs tiles per KV head), and workgroups past the last group exit at once.
 struct PrefillGrid {
     int heads;             // query heads per workgroup (hp = 4, 2 or 1; divides G)
     int rows;              // query rows per workgroup (128 / hp)
@@ -93,7 +97,8 @@ struct PrefillGrid {
     int qtiles_per_group;  // query tiles in a group
     int num_qblocks;       // ceil(num_qtiles / qtiles_per_group)
     int group_size;        // (G / hp) * qtiles_per_group workgroups
-    int num_groups;        // num_qblocks * num_seqs * num_kv_heads
+    int num_groups;        // num_qblocks * num_seqs * num_kv_heads, or its bound in compact mode
+    int compact;           // 1: only groups of existing query tiles are enumerated (qtiles_per_group 1)
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -214,10 +219,39 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     const int k = (qq / grid.group_size) * 8 + xcd;
     if (k >= grid.num_groups) return;
     const int group = p.num_heads / p.num_kv_heads;
-    const int per_qb = p.num_seqs * p.num_kv_heads;
-    const int qb = grid.num_qblocks - 1 - k / per_qb;
-    const int seq = (k % per_qb) / p.num_kv_heads;
-    const int g = k % p.num_kv_heads;
+    int qb, seq, g;
+    if (grid.compact) {
+        // lane i < num_seqs: query tiles of sequence i; level l holds the sequences with more than l
+        const int lane_id = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
+        int nq = 0;
+        if (lane_id < p.num_seqs) {
+            int a = p.cu_subquery[lane_id], e = p.cu_subquery[lane_id + 1];
+            a = max(0, min(a, int(p.num_tokens)));
+            e = max(a, min(e, int(p.num_tokens)));
+            nq = (e - a + grid.rows - 1) / grid.rows;
+        }
+        int rem = k, lvl = grid.num_qtiles - 1;
+        uint64_t m = 0;
+        for (; lvl >= 0; --lvl) {
+            m = __builtin_amdgcn_ballot_w64(nq > lvl);
+            const int cnt = __builtin_popcountll(m) * p.num_kv_heads;
+            if (rem < cnt) break;
+            rem -= cnt;
+        }
+        if (lvl < 0) return;
+        // the (rem / Hkv)-th sequence of the level: the lane whose bit is set with that many set bits below it
+        const int r = rem / p.num_kv_heads;
+        const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(((m >> lane_id) & 1) && below == r);
+        seq = __builtin_ctzll(hit);
+        g = rem % p.num_kv_heads;
+        qb = lvl;
+    } else {
+        const int per_qb = p.num_seqs * p.num_kv_heads;
+        qb = grid.num_qblocks - 1 - k / per_qb;
+        seq = (k % per_qb) / p.num_kv_heads;
+        g = k % p.num_kv_heads;
+    }
     const int hblocks = group / grid.heads;
     const int qt = qb * grid.qtiles_per_group + member / hblocks;
     const SeqInfo si = seq_info(p, seq);
@@ -521,7 +555,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         }
     };
 
-    constexpr bool INTERLEAVE = false;
     // ---- deferred copies.  The copies of the two fast paths (a wavefront's 16 rows all cached, or
     // all new and at or below key_hi) are planned before the tile that streams them starts --
     // scalar arithmetic only: a 32-bit block clamp and one 64-bit base per block, the value plane
@@ -662,14 +695,11 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // One 32-key half (keys k0h .. k0h + 31, key chunk kc of the tile in (ks, vs)); ka holds its
     // K operands on entry.  next_kc >= 0: the next half is chunk next_kc of the same tile, whose
     // K operands are read into ka here.
-    // cp: a planned copy of the next tile into (kdn, vdn), issued during this half's score MFMAs.
-    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs, int next_kc, bool with_copy, CopyPlan cp,
-                    bf16_t *kdn, bf16_t *vdn) __attribute__((always_inline)) {
+    auto half = [&](int k0h, int kc, const bf16_t *ks, const bf16_t *vs, int next_kc) __attribute__((always_inline)) {
         // wavefront rows are positions p0 .. p0 + 31; a key is visible from pos iff
         // pos - W < key <= pos
         const bool empty = k0h > p0 + 31 || (p.window > 0 && k0h + 31 <= p0 - p.window);
         if (empty) {
-            if (with_copy) issue_all(cp, kdn, vdn);
             if (next_kc >= 0) load_k(ks, next_kc);
             return;
         }
@@ -692,7 +722,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         // matrix unit, this one goes first and the other turns to its exponentials, so the two
         // drift into alternating phases instead of colliding.
         __builtin_amdgcn_s_setprio(1);
-        static_assert(NJ == DC, "one copy pair per group of score MFMAs");
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
 #pragma unroll
@@ -817,11 +846,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             lsum[qbk] = mfma16(ones, pb[qbk], lsum[qbk]);
     };
     // Tile kt from stage (ks, vs), second half first; the first half's K operands are read here.
-    // cp (or null): the next tile's planned copies into (kdn, vdn), issued during the first half.
-    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs, CopyPlan cp, bf16_t *kdn,
-                            bf16_t *vdn) __attribute__((always_inline)) {
-        half(kt * kBN + 32, 1, ks, vs, 0, INTERLEAVE && cp.mode != 0, cp, kdn, vdn);
-        half(kt * kBN, 0, ks, vs, -1, false, cp, kdn, vdn);
+    auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
+        half(kt * kBN + 32, 1, ks, vs, 0);
+        half(kt * kBN, 0, ks, vs, -1);
     };
 
     // ---- pipeline.  Tiles are taken from the last (nearest the diagonal) to the first: with
@@ -861,10 +888,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             const int i0 = __builtin_amdgcn_readlane(ids, 0), i1 = __builtin_amdgcn_readlane(ids, 1);
             cp = plan_copy(kt - 1, i0, i1);
             if (cp.mode == 0) copy_tile(kt - 1, i0, i1, Ks1, Vs1);
-            else if (!INTERLEAVE) issue_all(cp, Ks1, Vs1);
+            else issue_all(cp, Ks1, Vs1);
             if (kt - 2 >= kt_lo) ids = fetch_ids(kt - 2);
         }
-        compute_tile(kt, Ks0, Vs0, cp, Ks1, Vs1);
+        compute_tile(kt, Ks0, Vs0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         fp8_commit(Ks1, Vs1);
         asm volatile("" : "+v"(ids));
@@ -876,10 +903,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             const int i0 = __builtin_amdgcn_readlane(ids, 0), i1 = __builtin_amdgcn_readlane(ids, 1);
             cq = plan_copy(kt - 2, i0, i1);
             if (cq.mode == 0) copy_tile(kt - 2, i0, i1, Ks0, Vs0);
-            else if (!INTERLEAVE) issue_all(cq, Ks0, Vs0);
+            else issue_all(cq, Ks0, Vs0);
             if (kt - 3 >= kt_lo) ids = fetch_ids(kt - 3);
         }
-        compute_tile(kt - 1, Ks1, Vs1, cq, Ks0, Vs0);
+        compute_tile(kt - 1, Ks1, Vs1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         fp8_commit(Ks0, Vs0);
         asm volatile("" : "+v"(ids));
@@ -985,11 +1012,17 @@ hipError_t launch_mfma(const PrefillParams &p, int head_size, hipStream_t stream
     grid.rows = kRowsPerBlock / grid.heads;
     grid.num_qtiles = (p.max_subquery_len + grid.rows - 1) / grid.rows;
     const int hblocks = group / grid.heads;
-    grid.qtiles_per_group = hblocks >= 8 ? 1 : min(8 / hblocks, grid.num_qtiles);
+    grid.compact = p.num_seqs <= 64 && grid.num_qtiles <= 64 ? 1 : 0;
+    grid.qtiles_per_group = grid.compact || hblocks >= 8 ? 1 : min(8 / hblocks, grid.num_qtiles);
     if (grid.qtiles_per_group < 1) grid.qtiles_per_group = 1;
     grid.num_qblocks = (grid.num_qtiles + grid.qtiles_per_group - 1) / grid.qtiles_per_group;
     grid.group_size = hblocks * grid.qtiles_per_group;
-    const int64_t groups = int64_t(grid.num_qblocks) * p.num_seqs * p.num_kv_heads;
+    int64_t groups = int64_t(grid.num_qblocks) * p.num_seqs * p.num_kv_heads;
+    if (grid.compact) {
+        // sum over sequences of ceil(n / rows) <= num_tokens / rows + num_seqs
+        const int64_t tiles = p.num_tokens / grid.rows + p.num_seqs;
+        groups = min(groups, tiles * p.num_kv_heads);
+    }
     if (groups == 0) return hipSuccess;
     const int64_t blocks = (groups + 7) / 8 * 8 * grid.group_size;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
