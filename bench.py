@@ -485,6 +485,42 @@ class StepRunner:
         torch.cuda.empty_cache()
 
 
+def multi_token_leg(pa, r, ks=(2, 4, 8), reps: int = 10):
+    """Multi-token decode (pa_decode_multi) over a decode workload's cache: query_len = k rows per
+    sequence at the end of its cached tokens (N(0, 1) queries, seed 7).  GB/s counts each sequence's
+    visible K+V once, as for single-token decode."""
+    b, L, layer = r.batch, r.L, r.layer
+    B = len(b.decode_seq_lens)
+    G = L.num_heads // L.num_kv_heads
+    nbytes = decode_bytes(b)
+    gen = torch.Generator(device=r.dev)
+    gen.manual_seed(7)
+    res = {}
+    for k in ks:
+        q = torch.empty((B * k, L.num_heads * L.head_size), dtype=L.torch_dtype, device=r.dev)
+        q.normal_(0.0, 1.0, generator=gen)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(pa.decode_workspace_size(layer, B, r.d_max, k), 1), dtype=torch.uint8, device=r.dev)
+        run = lambda: pa.decode(q, r.cache, r.d_bt, r.d_sl, layer, r.d_max, out=out, workspace=ws, query_len=k)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(r.stream)
+            run()
+            e1.record(r.stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        st = ms_stats(ts)
+        gbps = nbytes / (st["ms"] * 1e-3) / 1e9
+        res[str(k)] = dict(st, GB_per_s=gbps, frac_hbm_peak=gbps / HBM_PEAK_GBPS,
+                           kernels="MFMA prefill" if k * G > 8 and L.dtype != wl.F32 else "decode")
+        del q, out, ws
+    return res
+
+
 def config_leg(pa, k: int, dev, steps: int, warmup: int):
     """Workload k built, timed and freed: its own step (cache write, prefill and / or decode)."""
     W = wl.workload(k)
@@ -492,6 +528,8 @@ def config_leg(pa, k: int, dev, steps: int, warmup: int):
     r = StepRunner(pa, W, dev)
     times, _ = r.run(steps, warmup)
     res = r.results(times)
+    if k == 3:
+        res["multi_token_decode"] = multi_token_leg(pa, r)
     res["workload"] = f"{W.name}: {W.description}"
     res["setup_s"] = round(r.setup_s, 1)
     r.free()
@@ -534,6 +572,8 @@ def main(argv=None):
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
     secondary = R.results(times)
 
+    if args.workload == 3:
+        secondary["multi_token_decode"] = multi_token_leg(pa, R)
     secondary["cache_write_cold"] = cold_cache_write_leg(pa, batch, cache, R.slots, layer, dev)
     if not args.no_block_moves:
         secondary.update(block_moves(pa, L, dev))

@@ -201,11 +201,11 @@ pa_status pa_decode_noalloc(const pa_layer *layer, void *out, const void *query,
  * _init_reorder_batch_threshold).  Every sequence has query_len query rows, rows
  * i * query_len .. i * query_len + query_len - 1 of query, whose K/V are already in the cache;
  * row t of sequence i sits at position seq_lens[i] - query_len + t and attends causally (with
- * the window, ALiBi, soft-cap and sinks as in decode) to the cached keys up to it.  The query
- * rows of a sequence and the query heads of a KV head share every K/V byte read as long as
- * query_len * (num_heads / num_kv_heads) <= 8; beyond that the K/V bytes are read once per
- * group of 8, and pa_prefill_varlen over the same rows (context seq_lens[i] - query_len, the
- * query_len rows new) is the faster form.
+ * the window, ALiBi, soft-cap and sinks as in decode) to the cached keys up to it.  While
+ * query_len * (num_heads / num_kv_heads) <= 8 (and for fp32 layers) the decode kernels run, the
+ * query rows of a sequence and the query heads of a KV head sharing every K/V byte read; beyond
+ * that, for bf16 and fp16 layers, the rows run on the MFMA prefill kernel (a chunked prefill of
+ * query_len rows whose keys all come from the cache), which also shares each K/V tile among them.
  *   out              device [num_seqs * query_len, num_heads * head_size], contiguous, written
  *   query            device [num_seqs * query_len, ...], rows q_row_stride elements apart
  *   seq_lens         device int32 [num_seqs], counting every query row; 0 marks a padded

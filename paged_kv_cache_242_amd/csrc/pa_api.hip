@@ -328,6 +328,48 @@ pa_status decode_impl(const char *fn, const pa_layer *layer, void *out, const vo
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(PA_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
     }
+    // Multi-token decode whose query rows times the query heads of a KV head exceed one head group:
+    // the decode kernels would read every K/V byte once per group, so the rows go to the MFMA
+    // prefill kernel instead, as a chunked prefill whose keys all come from the cache.
+    if (query_len > 1 && layer->dtype != PA_DTYPE_F32 && plan.head_groups > 1) {
+        if (int64_t(num_seqs) * query_len > 0x7fffffff)
+            return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_seqs * query_len exceeds int32", fn);
+        pa::PrefillParams q{};
+        q.out = out;
+        q.query = query;
+        q.q_stride = q_row_stride;
+        q.key = nullptr;
+        q.value = nullptr;
+        q.kv_stride = int64_t(layer->num_kv_heads) * layer->head_size;
+        q.k_cache = kv_cache;
+        q.v_cache = static_cast<const char *>(kv_cache) + layer->num_blocks * layer->block_size *
+                                                              int64_t(layer->num_kv_heads) * layer->head_size *
+                                                              cache_elt_bytes(layer);
+        q.block_tables = block_tables;
+        q.max_blocks = max_blocks_per_seq;
+        q.context_lens = nullptr;
+        q.cu_subquery = nullptr;
+        q.num_seqs = num_seqs;
+        q.num_tokens = int64_t(num_seqs) * query_len;
+        q.num_heads = layer->num_heads;
+        q.num_kv_heads = layer->num_kv_heads;
+        q.block_shift = log2_exact(layer->block_size);
+        q.num_blocks = layer->num_blocks;
+        q.scale = layer->scale;
+        q.alibi_slopes = layer->alibi_slopes;
+        q.window = layer->sliding_window;
+        q.softcap = layer->logits_soft_cap > 0.f ? layer->logits_soft_cap : 0.f;
+        q.sinks = layer->sinks;
+        q.max_subquery_len = query_len;
+        q.max_context_len = max_seq_len;
+        q.k_scale = layer->k_scale;
+        q.v_scale = layer->v_scale;
+        q.uniform_qlen = query_len;
+        q.seq_lens = seq_lens;
+        hipError_t e = pa::launch_prefill(q, kernel_dtype(layer), layer->head_size, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    }
     pa::DecodeParams p;
     p.out = out;
     p.query = query;
@@ -428,6 +470,8 @@ pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query,
     p.max_context_len = max_context_len;
     p.k_scale = layer->k_scale;
     p.v_scale = layer->v_scale;
+    p.uniform_qlen = 0;
+    p.seq_lens = nullptr;
     hipError_t e = pa::launch_prefill(p, kernel_dtype(layer), layer->head_size, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();

@@ -108,6 +108,10 @@ struct PrefillParams {
     int32_t max_subquery_len;
     int32_t max_context_len;
     float k_scale, v_scale;   // FP8 cache scales (element types 3 and 4)
+    // Uniform multi-token mode (> 0, 16-bit kernels only): uniform_qlen query rows per sequence,
+    // all keys in the cache, lengths from seq_lens (cu_subquery and context_lens unused).
+    int32_t uniform_qlen;
+    const int32_t *seq_lens;
 };
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipStream_t stream);
 

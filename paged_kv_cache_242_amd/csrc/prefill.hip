@@ -45,11 +45,24 @@ constexpr float kRescaleSlack = 8.0f;
 struct SeqInfo {
     int start;      // first query/key row of the sequence
     int n;          // subquery rows
-    int c;          // cached context tokens
+    int c;          // keys read from the cache (those below c); keys from c on are the call's new rows
+    int q0;         // position of subquery row 0 (c, except in the uniform multi-token mode)
+    bool empty;     // uniform mode: a padded (or too short) sequence, whose rows are written as zeros
 };
 
 __device__ __forceinline__ SeqInfo seq_info(const PrefillParams &p, int seq) {
     SeqInfo s;
+    if (p.uniform_qlen > 0) {
+        // multi-token decode: query_len rows per sequence at seq * query_len, at positions
+        // L - query_len .. L - 1, every key (0 .. L - 1) already in the cache
+        const int L = max(0, min(p.seq_lens[seq], min(p.max_blocks << p.block_shift, p.max_context_len)));
+        s.start = seq * p.uniform_qlen;
+        s.n = p.uniform_qlen;
+        s.c = L;
+        s.q0 = L - p.uniform_qlen;
+        s.empty = L < p.uniform_qlen;
+        return s;
+    }
     int a = p.cu_subquery[seq];
     int b = p.cu_subquery[seq + 1];
     a = max(0, min(a, int(p.num_tokens)));
@@ -59,6 +72,8 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams &p, int seq) {
     int c = p.context_lens ? p.context_lens[seq] : 0;
     c = max(0, min(c, p.block_tables ? (p.max_blocks << p.block_shift) : 0));
     s.c = c;
+    s.q0 = c;
+    s.empty = false;
     return s;
 }
 
@@ -225,10 +240,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         const int lane_id = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
         int nq = 0;
         if (lane_id < p.num_seqs) {
-            int a = p.cu_subquery[lane_id], e = p.cu_subquery[lane_id + 1];
-            a = max(0, min(a, int(p.num_tokens)));
-            e = max(a, min(e, int(p.num_tokens)));
-            nq = (e - a + grid.rows - 1) / grid.rows;
+            if (p.uniform_qlen > 0) {
+                nq = (p.uniform_qlen + grid.rows - 1) / grid.rows;
+            } else {
+                int a = p.cu_subquery[lane_id], e = p.cu_subquery[lane_id + 1];
+                a = max(0, min(a, int(p.num_tokens)));
+                e = max(a, min(e, int(p.num_tokens)));
+                nq = (e - a + grid.rows - 1) / grid.rows;
+            }
         }
         int rem = k, lvl = grid.num_qtiles - 1;
         uint64_t m = 0;
@@ -266,7 +285,21 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // so for hp = 4 all four see the same diagonal and reach every tile with equal work
     const int h = g * group + (member % hblocks) * grid.heads + wave % grid.heads;
     const int t0 = qt * grid.rows + (wave / grid.heads) * 32;   // first subquery row of this wavefront
-    const int p0 = si.c + t0;                                  // its position
+    const int p0 = si.q0 + t0;                                 // its position
+    if (si.empty) {
+        // uniform mode, a padded sequence: zero rows (uniform over the workgroup, before any barrier)
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+            const int trow = t0 + 16 * qbk + l16;
+            if (trow < si.n) {
+                bf16_t *orow = reinterpret_cast<bf16_t *>(p.out) + int64_t(si.start + trow) * p.num_heads * D +
+                               int64_t(h) * D + 4 * lg;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) *reinterpret_cast<uint2 *>(orow + 16 * db) = make_uint2(0u, 0u);
+            }
+        }
+        return;
+    }
 
     const float qk_scale = p.scale * kLog2e;
     // Without a soft-cap (PRE) Q is multiplied by scale log2(e) once, here, and rounded to the
@@ -321,8 +354,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     }
 
     const int row_hi = min(qt * grid.rows + grid.rows, si.n) - 1;
-    const int pos_lo = si.c + qt * grid.rows;
-    const int key_hi = si.c + row_hi;
+    const int pos_lo = si.q0 + qt * grid.rows;
+    const int key_hi = si.q0 + row_hi;
     const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
     const int kt_lo = key_lo / kBN, kt_hi = key_hi / kBN;
 
@@ -1063,6 +1096,7 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipS
     if (dtype == 2) return launch_mfma<f16_t>(p, head_size, stream);
     if (dtype == 3) return launch_mfma<bf16_c8_t>(p, head_size, stream);
     if (dtype == 4) return launch_mfma<f16_c8_t>(p, head_size, stream);
+    if (p.uniform_qlen > 0) return hipErrorInvalidValue;      // the uniform mode has 16-bit kernels only
     const int64_t blocks = p.num_tokens * p.num_heads;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

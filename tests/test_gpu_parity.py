@@ -347,14 +347,19 @@ def test_multi_token_decode_as_chunked_prefill(k, layer):
 
 # ------------------------------------------------------------------------------ full-size workloads
 
+# (query_len, layer, number of extra sequences).  Calls whose query rows times query heads per KV
+# head exceed 8 (16-bit layers) run on the MFMA prefill kernel with every key from the cache; the
+# others, and fp32 layers, on the decode kernels.
 MULTI_CASES = [
-    (2, _layer(32, 8, 128, 16)),
-    (4, _layer(32, 8, 128, 16)),                               # 16 virtual heads per KV head: two groups
-    (3, _layer(32, 32, 128, 16, alibi=True, window=300)),      # 3 rows of one head: padded group of 4
-    (2, _layer(64, 8, 128, 32, fp8=True)),
-    (4, _layer(16, 2, 64, 8, wl.F16, sinks=True, softcap=3.0, scale=0.3)),
-    (2, _layer(8, 8, 64, 16, wl.F32, alibi=True, window=40)),
-    (8, _layer(8, 1, 128, 16, alibi=True)),                    # 64 virtual heads of one KV head
+    (2, _layer(32, 8, 128, 16), 0),                               # 8 virtual heads: decode kernels
+    (4, _layer(32, 8, 128, 16), 0),                               # 16: prefill kernel
+    (3, _layer(32, 32, 128, 16, alibi=True, window=300), 0),      # 3 rows of one head: decode, padded group of 4
+    (2, _layer(64, 8, 128, 32, fp8=True), 0),                     # 16, fp8 cache: prefill kernel
+    (4, _layer(16, 2, 64, 8, wl.F16, sinks=True, softcap=3.0, scale=0.3), 0),   # 32: prefill kernel
+    (2, _layer(8, 8, 64, 16, wl.F32, alibi=True, window=40), 0),  # fp32: decode kernels
+    (8, _layer(8, 1, 128, 16, alibi=True), 0),                    # 64: prefill kernel
+    (4, _layer(16, 4, 256, 16, alibi=True, window=300), 0),       # head size 256: prefill kernel
+    (3, _layer(32, 8, 128, 16, window=1000), 64),                 # 80 sequences (no compact grid): prefill kernel
 ]
 
 
@@ -362,9 +367,9 @@ MULTI_CASES = [
 def test_decode_multi(ci):
     """Multi-token decode (pa_decode_multi): k query rows per sequence, every K/V already in the
     cache, against the oracle's multi-token decode; a padded sequence (length 0) gives zero rows."""
-    k, layer = MULTI_CASES[ci]
+    k, layer, extra = MULTI_CASES[ci]
     rng = np.random.default_rng(80 + ci)
-    lens = [k, k + 1, 31, 129, 1000, 0, 2049, 4100] + rng.integers(k, 3000, size=8).tolist()
+    lens = [k, k + 1, 31, 129, 1000, 0, 2049, 4100] + rng.integers(k, 3000, size=8 + extra).tolist()
     live = [L for L in lens if L]
     batch = wl.make_batch(layer, seed=81 + ci, prefill=[(L - k, k) for L in live], device=gh.device())
     _say(f"decode_multi k={k} layer {ci}: {batch.layer}")
