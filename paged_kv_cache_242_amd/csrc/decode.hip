@@ -45,6 +45,12 @@ namespace {
 
 constexpr int kTile = 32;          // keys per wavefront tile
 constexpr int kMaxGroup = 8;       // query heads per work unit
+// Up to this many sequences the split kernel's wavefronts plan their own share (a scan of the
+// sequences' tile counts each); beyond it a planning kernel does it once.
+#ifndef PA_DECODE_INWAVE_MAX
+#define PA_DECODE_INWAVE_MAX 2048
+#endif
+constexpr int kInWavePlanMax = PA_DECODE_INWAVE_MAX;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -124,6 +130,7 @@ struct DecodeShape {
     int tile;               // keys per tile of the split kernel instance
     int max_len;            // bound on every sequence length
     int kvh;                // KV heads per work unit
+    int inwave;             // 1: every split wavefront finds its own first tile (no planning kernel)
 };
 
 template <typename T>
@@ -353,6 +360,61 @@ __device__ __forceinline__ void load_ids(const DecodeParams &p, const DecodeShap
     }
 }
 
+// Up to a few thousand sequences a split wavefront plans its own share: it scans the tile counts of
+// all sequences, 64 at a time -- their total, then the sequence holding its first tile and that
+// sequence's prefix -- instead of a planning kernel running first.  Wavefront 0 stores the total for
+// the merge kernel (which also reads the prefixes the split wavefronts store as they enter
+// sequences; every sequence with tiles is entered by some wavefront).  Counts are 32-bit (the host
+// enables this only while num_seqs * tiles per sequence stays below 2^30); the results are
+// wave-uniform and returned through readfirstlane, so they live in scalar registers.
+struct InWavePlan {
+    int64_t total;      // tiles of all work units
+    int seq;            // sequence holding the wavefront's first tile
+    int64_t pre;        // tiles of the work units of the sequences before it
+};
+__device__ __forceinline__ InWavePlan plan_in_wave(const DecodeParams &p, const DecodeShape &shape, int wave,
+                                                   int lane) {
+    const int B = p.num_seqs;
+    const int ups = shape.units_per_seq;
+    auto tiles_of = [&](int q) -> int {
+        int L_, lo_;
+        return q < B ? seq_tiles(p, shape, q, L_, lo_) : 0;
+    };
+    InWavePlan ip{0, 0, 0};
+    int tot = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        int x = tiles_of(c0 + lane);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d, 64);
+        tot += __builtin_amdgcn_readfirstlane(x);
+    }
+    ip.total = int64_t(tot) * ups;
+    if (wave == 0 && lane == 0) p.ws_prefix[B] = ip.total;
+    const int64_t tb = int64_t(wave) * ip.total / shape.num_waves;
+    if (tb >= int64_t(wave + 1) * ip.total / shape.num_waves) return ip;     // no tiles
+    const int tbu = int(tb / ups);           // its sequence is the first whose inclusive count exceeds tbu
+    int base = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int own = tiles_of(c0 + lane);
+        int incl = own;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += y;
+        }
+        const int chunk = __builtin_amdgcn_readlane(incl, 63);
+        if (base + chunk > tbu) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > tbu);
+            const int l = int(__builtin_ctzll(hit));
+            ip.seq = c0 + l;
+            ip.pre = int64_t(base + __builtin_amdgcn_readlane(incl - own, l)) * ups;
+            break;
+        }
+        base += chunk;
+    }
+    return ip;
+}
+
 // Even split: wavefront i takes tiles floor(i T / N) .. floor((i + 1) T / N) - 1 of the
 // concatenated tiles of all work units (sequence-major, then KV head, then head group), i.e. a
 // run of segments each inside one work unit.  A segment that is a whole unit writes the output;
@@ -409,12 +471,21 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     const float cap2 = p.softcap * kLog2e;
     const bool has_alibi = p.alibi_slopes != nullptr;
 
-    const int64_t Ttot = p.ws_prefix[p.num_seqs];
+    int64_t Ttot, pre = 0;
+    int seq = 0;
+    if (shape.inwave) {
+        const InWavePlan ip = plan_in_wave(p, shape, wave, lane);
+        Ttot = ip.total;
+        seq = ip.seq;
+        pre = ip.pre;
+    } else {
+        Ttot = p.ws_prefix[p.num_seqs];
+        seq = p.ws_wseq[wave];
+        pre = p.ws_prefix[seq];
+    }
     const int64_t t_begin = int64_t(wave) * Ttot / shape.num_waves;
     const int64_t t_end = int64_t(wave + 1) * Ttot / shape.num_waves;
     if (t_begin >= t_end) return;
-    int seq = p.ws_wseq[wave];
-    int64_t pre = p.ws_prefix[seq];
 
     int64_t t = t_begin;
     while (t < t_end) {
@@ -425,6 +496,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             ++seq;
             continue;
         }
+        if (shape.inwave && lane == 0) p.ws_prefix[seq] = pre;
         const int64_t local = t - pre;
         const int u_in = int(local / ts);
         const int tile0 = int(local - int64_t(u_in) * ts);
@@ -852,9 +924,12 @@ hipError_t launch_typed(const DecodeParams &p, const DecodeShape &s, hipStream_t
     constexpr int TILE = tile_keys<T, D, GP, KVH>();
     const int64_t units = int64_t(p.num_seqs) * s.units_per_seq;
     if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!s.inwave) {
+        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const bool one_block = (1 << p.block_shift) >= TILE;
     e = one_block ? launch_split<T, D, GP, true, KVH>(p, s, stream) : launch_split<T, D, GP, false, KVH>(p, s, stream);
     if (e != hipSuccess) return e;
@@ -976,6 +1051,9 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
     s.tile = plan.tile;
     s.max_len = p.max_seq_len;
     s.kvh = plan.kv_per_unit;
+    s.inwave = p.num_seqs <= kInWavePlanMax &&
+                       int64_t(p.num_seqs) * ((int64_t(p.max_seq_len) + s.tile - 1) / s.tile + 1) < (int64_t(1) << 30)
+                   ? 1 : 0;
     return dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
         return launch_group<typename decltype(t)::type, decltype(d)::value>(p, s, plan.padded_group, stream);
     });

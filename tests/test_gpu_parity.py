@@ -571,16 +571,17 @@ def test_decode_split_cut_invariance(layer):
         gh.assert_close(outs[k], outs[0], batch.layer, f"placement {k} against placement 0")
 
 
-def test_decode_many_sequences():
-    """More than 1024 sequences: the planning kernel scans per-thread chunks of sequences and
-    searches inside a chunk for each wavefront's first sequence.  1500 short sequences (lengths 0 to
-    300, some padded) against the oracle."""
+@pytest.mark.parametrize("n", [1500, 2600])
+def test_decode_many_sequences(n):
+    """Many short sequences (lengths 0 to 300, some padded) against the oracle.  Up to 2048
+    sequences each split wavefront scans all of them (64 per step) to find its first sequence; 2600
+    take the planning kernel, whose threads scan chunks of sequences and search inside a chunk."""
     layer = _layer(32, 8, 128, 16)
     rng = np.random.default_rng(99)
-    lens = rng.integers(0, 300, size=1500)
+    lens = rng.integers(0, 300, size=n)
     lens[::97] = 0
     batch = wl.make_batch(layer, seed=99, decode=lens.tolist(), device=gh.device())
-    _check_full(batch, "1500 sequences")
+    _check_full(batch, f"{n} sequences")
 
 
 # ------------------------------------------------------------------------------ NaN propagation
