@@ -181,10 +181,10 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 //
 // Scores.  A wavefront's 32 rows meet a tile in two 32-key halves.  Q is multiplied by
 // scale log2(e) and rounded to the element type once, when it is loaded, so the score MFMAs
-// produce base-2 logits; their accumulators start at c_row - m, where c_row is the row's ALiBi
-// term for the half's first key (0 without ALiBi) and m the finite stand-in of the row's running
-// max, and ALiBi's in-half key offset times slope log2(e) is added by one rank-1 MFMA per score
-// block.  A score then leaves the MFMAs as the exponent of its weight.  A half is
+// produce base-2 logits; their accumulators start at c_row - m + b_key, where c_row is the row's
+// ALiBi term for the half's first key (0 without ALiBi), m the finite stand-in of the row's running
+// max and b_key the key's ALiBi offset from the half's first key times slope log2(e) (a per-lane
+// constant).  A score then leaves the MFMAs as the exponent of its weight.  A half is
 //   * empty for the wavefront when every (row, key) pair is masked -- skipped entirely;
 //   * full when none is -- no per-score work besides the max and the exponent;
 //   * partial otherwise -- masked scores are set to -inf.
@@ -313,7 +313,11 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // The ALiBi key term rides on the score MFMAs as a rank-1 update (the factor slope log2(e) in
     // 16-bit hi/lo parts) when Q is pre-scaled; with a soft-cap it must stay outside the cap, so
     // there it is added in fp32 after the scores are formed.
-    constexpr bool KBIAS_MFMA = ALIBI && PRE;
+#ifndef PA_PREFILL_ALIBI_MFMA
+#define PA_PREFILL_ALIBI_MFMA 0
+#endif
+    constexpr bool KBIAS_MFMA = ALIBI && PRE && PA_PREFILL_ALIBI_MFMA;
+    constexpr bool KBIAS_INIT = ALIBI && PRE && !PA_PREFILL_ALIBI_MFMA;   // key term in the accumulators' start
     constexpr bool KBIAS_F32 = ALIBI && !PRE;
     // multiplier of the soft-capped scores in the exponent (they are base-2 logits already)
     const float s_mul = 1.f;
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 
     // ALiBi key term of slot (kk, i) relative to the half's first key, for the fp32 path
     float kbias[2][4] = {};
-    if constexpr (KBIAS_F32) {
+    if constexpr (KBIAS_F32 || KBIAS_INIT) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -749,7 +753,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             // PRE: the scores come out as base-2 logits minus the finite stand-in of the running max
             const float c0 = PRE ? crow[qbk] - m_fin[qbk] : 0.f;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) s[kk][qbk] = floatx4_v{c0, c0, c0, c0};
+            for (int kk = 0; kk < 2; ++kk) {
+                if constexpr (KBIAS_INIT)
+                    s[kk][qbk] = floatx4_v{c0 + kbias[kk][0], c0 + kbias[kk][1], c0 + kbias[kk][2], c0 + kbias[kk][3]};
+                else
+                    s[kk][qbk] = floatx4_v{c0, c0, c0, c0};
+            }
         }
         // Raised wave priority while the score MFMAs issue: when both wavefronts of a SIMD want the
         // matrix unit, this one goes first and the other turns to its exponentials, so the two
