@@ -310,14 +310,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     constexpr bool PRE = !SOFTCAP;
     const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // sign flips of both halves
     const uint32_t qand = qk_scale == 0.f ? 0u : 0xffffffffu;
-    // The ALiBi key term rides on the score MFMAs as a rank-1 update (the factor slope log2(e) in
-    // 16-bit hi/lo parts) when Q is pre-scaled; with a soft-cap it must stay outside the cap, so
-    // there it is added in fp32 after the scores are formed.
-#ifndef PA_PREFILL_ALIBI_MFMA
-#define PA_PREFILL_ALIBI_MFMA 0
-#endif
-    constexpr bool KBIAS_MFMA = ALIBI && PRE && PA_PREFILL_ALIBI_MFMA;
-    constexpr bool KBIAS_INIT = ALIBI && PRE && !PA_PREFILL_ALIBI_MFMA;   // key term in the accumulators' start
+    // The ALiBi key term (the key's offset from the half's first key times slope log2(e)) joins the
+    // score accumulators' starting values when Q is pre-scaled; with a soft-cap it must stay outside
+    // the cap, so there it is added in fp32 after the cap.
+    constexpr bool KBIAS_INIT = ALIBI && PRE;
     constexpr bool KBIAS_F32 = ALIBI && !PRE;
     // multiplier of the soft-capped scores in the exponent (they are base-2 logits already)
     const float s_mul = 1.f;
@@ -363,26 +359,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
     const int kt_lo = key_lo / kBN, kt_hi = key_hi / kBN;
 
-    // ALiBi: slope in base-2 units; the rank-1 MFMA term adds (key - half start) * slope2 to the
-    // base-2 logits, with slope2 split into a high and a low 16-bit part (k slots 0 and 1).
+    // ALiBi: slope in base-2 units; kbias[kk][i] is the key term of accumulator slot (kk, i), the key
+    // k0h + 16 kk + 4 lg + i, relative to the half's first key k0h.
     float slope2 = 0.f;
-    V8 bslope = {}, arel[2] = {};
     if constexpr (ALIBI) slope2 = p.alibi_slopes[h] * kLog2e;
-    if constexpr (KBIAS_MFMA) {
-        const float ratio = slope2;
-        const T hi = to_elt<T>(ratio);
-        const T lo = to_elt<T>(ratio - elt_to_f32(hi));
-        const uint32_t hl = lane < 16 ? (elt_bits(hi) | (elt_bits(lo) << 16)) : 0u;
-        bslope = __builtin_bit_cast(V8, make_uint4(hl, 0u, 0u, 0u));
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const uint32_t r = elt_bits(to_elt<T>(float(16 * kk + l16)));
-            const uint32_t rr = lane < 16 ? (r | (r << 16)) : 0u;
-            arel[kk] = __builtin_bit_cast(V8, make_uint4(rr, 0u, 0u, 0u));
-        }
-    }
-
-    // ALiBi key term of slot (kk, i) relative to the half's first key, for the fp32 path
     float kbias[2][4] = {};
     if constexpr (KBIAS_F32 || KBIAS_INIT) {
 #pragma unroll
@@ -771,13 +751,6 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
                 for (int qbk = 0; qbk < 2; ++qbk)
                     s[kk][qbk] = mfma16(ka[dc][kk], qf[qbk][dc], s[kk][qbk]);
-        }
-        if constexpr (KBIAS_MFMA) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk)
-                    s[kk][qbk] = mfma16(arel[kk], bslope, s[kk][qbk]);
         }
         __builtin_amdgcn_s_setprio(0);
         load_v(vs, kc);
