@@ -235,20 +235,15 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     if (k >= grid.num_groups) return;
     const int group = p.num_heads / p.num_kv_heads;
     int qb, seq, g;
+    SeqInfo si;
     if (grid.compact) {
-        // lane i < num_seqs: query tiles of sequence i; level l holds the sequences with more than l
+        // lane i < num_seqs holds sequence i's bounds (loaded once: the workgroup's sequence is then
+        // read out of its lane, with no second round trip) and query tiles; level l holds the
+        // sequences with more than l query tiles
         const int lane_id = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
-        int nq = 0;
-        if (lane_id < p.num_seqs) {
-            if (p.uniform_qlen > 0) {
-                nq = (p.uniform_qlen + grid.rows - 1) / grid.rows;
-            } else {
-                int a = p.cu_subquery[lane_id], e = p.cu_subquery[lane_id + 1];
-                a = max(0, min(a, int(p.num_tokens)));
-                e = max(a, min(e, int(p.num_tokens)));
-                nq = (e - a + grid.rows - 1) / grid.rows;
-            }
-        }
+        SeqInfo ls{0, 0, 0, 0, false};
+        if (lane_id < p.num_seqs) ls = seq_info(p, lane_id);
+        const int nq = (ls.n + grid.rows - 1) / grid.rows;
         int rem = k, lvl = grid.num_qtiles - 1;
         uint64_t m = 0;
         for (; lvl >= 0; --lvl) {
@@ -265,15 +260,20 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         seq = __builtin_ctzll(hit);
         g = rem % p.num_kv_heads;
         qb = lvl;
+        si.start = __builtin_amdgcn_readlane(ls.start, seq);
+        si.n = __builtin_amdgcn_readlane(ls.n, seq);
+        si.c = __builtin_amdgcn_readlane(ls.c, seq);
+        si.q0 = __builtin_amdgcn_readlane(ls.q0, seq);
+        si.empty = __builtin_amdgcn_readlane(int(ls.empty), seq) != 0;
     } else {
         const int per_qb = p.num_seqs * p.num_kv_heads;
         qb = grid.num_qblocks - 1 - k / per_qb;
         seq = (k % per_qb) / p.num_kv_heads;
         g = k % p.num_kv_heads;
+        si = seq_info(p, seq);
     }
     const int hblocks = group / grid.heads;
     const int qt = qb * grid.qtiles_per_group + member / hblocks;
-    const SeqInfo si = seq_info(p, seq);
     if (qt >= grid.num_qtiles || qt * grid.rows >= si.n) return;
 
     const int tid = threadIdx.x;
