@@ -515,8 +515,13 @@ def multi_token_leg(pa, r, ks=(2, 4, 8), reps: int = 10):
             ts.append(e0.elapsed_time(e1))
         st = ms_stats(ts)
         gbps = nbytes / (st["ms"] * 1e-3) / 1e9
-        res[str(k)] = dict(st, GB_per_s=gbps, frac_hbm_peak=gbps / HBM_PEAK_GBPS,
-                           kernels="MFMA prefill" if k * G > 8 and L.dtype != wl.F32 else "decode")
+        if L.dtype == wl.F32 or k * G <= 8:
+            kern = "VALU decode"
+        elif k * G <= 16 and L.head_size == 128 and L.block_size >= 16:
+            kern = "MFMA decode"
+        else:
+            kern = "MFMA prefill"
+        res[str(k)] = dict(st, GB_per_s=gbps, frac_hbm_peak=gbps / HBM_PEAK_GBPS, kernels=kern)
         del q, out, ws
     return res
 

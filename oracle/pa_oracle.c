@@ -113,8 +113,9 @@ static double e4m3_to_double(uint8_t c)
 }
 
 /* The E4M3 code nearest to x: ties go to the code with an even fraction, magnitudes above 448
- * saturate to 448, NaN gives the NaN code.  Found by scanning the 127 finite non-negative codes. */
-static uint8_t float_to_e4m3(float x)
+ * saturate to 448, NaN gives the NaN code.  Found by scanning the 127 finite non-negative codes,
+ * whose values the caller passes in (value[c] = e4m3_to_double(c)). */
+static uint8_t float_to_e4m3(float x, const double *value)
 {
     if (x != x) return signbit(x) ? 0xFF : 0x7F;
     const uint8_t sign = signbit(x) ? 0x80 : 0x00;
@@ -123,7 +124,7 @@ static uint8_t float_to_e4m3(float x)
     int best = 0;
     double best_err = INFINITY;
     for (int c = 0; c < 127; ++c) {
-        const double err = fabs(a - e4m3_to_double((uint8_t)c));
+        const double err = fabs(a - value[c]);
         if (err < best_err || (err == best_err && (c & 1) == 0)) {
             best = c;
             best_err = err;
@@ -248,6 +249,8 @@ int orc_cache_write(const orc_layer *L, const void *key, const void *value, int6
     const int64_t row = (int64_t)L->num_kv_heads * L->head_size;
     char *kc = (char *)kv_cache;
     char *vc = kc + plane * cb;
+    double e4m3_value[127];
+    for (int c = 0; c < 127; ++c) e4m3_value[c] = e4m3_to_double((uint8_t)c);
     for (int64_t t = 0; t < num_tokens; ++t) {
         int64_t s = slot_mapping[t];
         if (s < 0) continue;
@@ -262,8 +265,8 @@ int orc_cache_write(const orc_layer *L, const void *key, const void *value, int6
                     /* quantize: the fp32 quotient, then the nearest code */
                     const float kq = (float)elt_to_double(key, src, L->dtype) / L->k_scale;
                     const float vq = (float)elt_to_double(value, src, L->dtype) / L->v_scale;
-                    ((uint8_t *)kc)[dst] = float_to_e4m3(kq);
-                    ((uint8_t *)vc)[dst] = float_to_e4m3(vq);
+                    ((uint8_t *)kc)[dst] = float_to_e4m3(kq, e4m3_value);
+                    ((uint8_t *)vc)[dst] = float_to_e4m3(vq, e4m3_value);
                 } else {
                     memcpy(kc + dst * eb, (const char *)key + src * eb, eb);
                     memcpy(vc + dst * eb, (const char *)value + src * eb, eb);

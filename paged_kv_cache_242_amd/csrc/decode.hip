@@ -778,6 +778,399 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
     }
 }
 
+// ---- MFMA variant for wide head groups ------------------------------------------------------
+// With many virtual heads per KV head the dot products of the VALU kernel above cost more issue
+// time than the bytes take to arrive: an FP8 cache with a group of 8 query heads (the bytes halve,
+// the products do not), or the 9 to 16 query rows x heads of a multi-token decode, which the VALU
+// kernel could only split over two units that each read K/V.  This kernel forms the products on
+// the matrix unit instead, with the same work split, partial slots and merge:
+//   * a work unit is one (sequence, KV head) with its nh <= 16 virtual heads as the 16 columns
+//     of v_mfma_f32_16x16x32_{bf16,f16};
+//   * a 32-key tile is two 16-key blocks; lane (k = lane % 16, g = lane / 16) loads 16 bytes at
+//     byte 64 j + 16 g of key k's head row for j = 0 .. NL - 1, which for 16-bit rows is exactly
+//     the A operand of S^T = K Q^T (d = 32 j + 8 g .. + 7 for MFMA j).  For an FP8 row a load
+//     holds 16 codes (d = 64 j + 16 g .. + 15) that widen to the operands of MFMAs 2 j and
+//     2 j + 1; the query chunks are gathered in the same d order, so each MFMA still pairs
+//     equal d;
+//   * S^T leaves lane (head k, g) the scores of keys 16 kk + 4 g + i; the weights, rounded to the
+//     element type, are the B operand of O^T = V^T P^T as in the prefill kernel;
+//   * V passes through per-wavefront LDS tiles (row-major, 32-byte units xor-swizzled by key) and
+//     is read back transposed with ds_read_b64_tr_b16.  16-bit rows go there by load-to-LDS
+//     copies into two stages: before any LDS read the compiler waits for every copy in flight,
+//     so the next tile's loads are issued after this tile's reads and a deeper ring would gain
+//     nothing.  FP8 codes are loaded into a ring of registers, widened and written;
+//   * row sums come from an all-ones MFMA on the same rounded weights; the running max is raised
+//     lazily as in the VALU kernel.
+// 16-key blocks must lie inside one cache block (block size >= 16).  With up to 8 virtual heads
+// of 16-bit rows the VALU kernel is as fast or faster (its products still hide behind the bytes),
+// so it keeps them.
+constexpr int kMfmaTile = 32;
+constexpr int kMfmaMaxHeads = 16;
+// Smallest group (query heads x query rows per KV head) that takes the MFMA kernel: 16-bit rows
+// past the VALU kernel's 8 heads per unit; FP8 rows from 5 (at 4 the two kernels are level).
+#ifndef PA_DECODE_MFMA_MIN_GROUP
+#define PA_DECODE_MFMA_MIN_GROUP 9
+#endif
+#ifndef PA_DECODE_MFMA_MIN_GROUP8
+#define PA_DECODE_MFMA_MIN_GROUP8 5
+#endif
+
+#ifndef PA_DECODE_MFMA_DEPTH
+#define PA_DECODE_MFMA_DEPTH 2
+#endif
+#ifndef PA_DECODE_MFMA_OCC
+#define PA_DECODE_MFMA_OCC 2
+#endif
+#ifndef PA_DECODE_MFMA_DEPTH8
+#define PA_DECODE_MFMA_DEPTH8 3
+#endif
+#ifndef PA_DECODE_MFMA_OCC8
+#define PA_DECODE_MFMA_OCC8 2
+#endif
+template <typename T>
+constexpr int mfma_depth() { return kFp8Cache<T> ? PA_DECODE_MFMA_DEPTH8 : PA_DECODE_MFMA_DEPTH; }
+template <typename T>
+constexpr int mfma_occ() { return kFp8Cache<T> ? PA_DECODE_MFMA_OCC8 : PA_DECODE_MFMA_OCC; }
+
+// V tile swizzle: the 32-byte unit u of key r sits at unit u ^ (r & 7), so the 8 keys a
+// transposing read touches at one d fall in distinct 32-byte units.
+__device__ __forceinline__ int mfma_vswz(int r) { return r & 7; }
+
+template <typename T, int D, int DEPTH, int OCC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
+    typedef typename Operand8<T>::type V8;
+    constexpr int TILE = kMfmaTile;
+    constexpr int CB = kFp8Cache<T> ? 1 : 2;      // cache bytes per element
+    constexpr int DC = D / 32;                      // score MFMAs per 16-key block
+    constexpr int DB = D / 16;                      // d-blocks of O^T
+    constexpr int NL = D * CB / 64;                 // 16-byte loads per lane per 16-key block and row kind
+    static_assert(D == 128, "the MFMA decode kernel is built for head size 128");
+    constexpr bool VDMA = CB == 2;                  // V rows copied straight into LDS
+    constexpr int VST = VDMA ? DEPTH : 1;           // V stages in LDS
+    constexpr int NVR = VDMA ? 1 : NL;              // V register loads per 16-key block (unused with VDMA)
+    __shared__ __align__(16) bf16_t vt[VST][TILE * D];
+
+    const int wave = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int group = p.num_heads / p.num_kv_heads;
+    const int nh = shape.heads_per_group;
+    const int ups = shape.units_per_seq;
+    const int bmask = (1 << p.block_shift) - 1;
+    const uint32_t row_bytes = uint32_t(p.num_kv_heads) * D * CB;
+    const int64_t block_bytes = int64_t(row_bytes) << p.block_shift;
+    const char *kcache = reinterpret_cast<const char *>(p.k_cache);
+    const char *vcache = reinterpret_cast<const char *>(p.v_cache);
+    const bool has_cap = p.softcap > 0.f;
+    const float qk_scale = has_cap ? p.scale / p.softcap : p.scale * kLog2e;
+    const float cap2 = p.softcap * kLog2e;
+    const bool has_alibi = p.alibi_slopes != nullptr;
+    const uint32_t one2 = uint32_t(__builtin_bit_cast(uint16_t, to_elt<T>(1.f))) * 0x10001u;
+    const V8 ones = __builtin_bit_cast(V8, make_uint4(one2, one2, one2, one2));
+    // element offset of the 8 query elements that lane group lg supplies to score MFMA n
+    auto q_d = [&](int n) -> int { return CB == 1 ? 64 * (n >> 1) + 16 * lg + 8 * (n & 1) : 32 * n + 8 * lg; };
+    // V^T operand reads (elements): lane l16 = 4 a + c of group lg reads key 4 lg + a (and 16 more)
+    // at d = 16 db + 4 c
+    int v_off[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        v_off[db] = (4 * lg + (l16 >> 2)) * D + ((db ^ mfma_vswz(4 * lg + (l16 >> 2))) << 4) + 4 * (l16 & 3);
+    // V copies: copy q (0..3) of a 16-key block fills its rows 4 q .. 4 q + 3, lane l the 16-byte
+    // place l16 of row 4 q + lg; it fetches the source chunk that the swizzle puts there.  The
+    // swizzle of row 4 q + lg depends on q only through q & 1.
+    uint32_t v_chunk[2] = {0u, 0u};
+    if constexpr (VDMA) {
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            v_chunk[par] = uint32_t((((l16 >> 1) ^ mfma_vswz(4 * par + lg)) << 1) | (l16 & 1)) * 16u;
+    }
+
+    int64_t Ttot, pre = 0;
+    int seq = 0;
+    if (shape.inwave) {
+        const InWavePlan ip = plan_in_wave(p, shape, wave, lane);
+        Ttot = ip.total;
+        seq = ip.seq;
+        pre = ip.pre;
+    } else {
+        Ttot = p.ws_prefix[p.num_seqs];
+        seq = p.ws_wseq[wave];
+        pre = p.ws_prefix[seq];
+    }
+    const int64_t t_begin = int64_t(wave) * Ttot / shape.num_waves;
+    const int64_t t_end = int64_t(wave + 1) * Ttot / shape.num_waves;
+    if (t_begin >= t_end) return;
+
+    int64_t t = t_begin;
+    while (t < t_end) {
+        int L, lo;
+        const int ts = seq_tiles(p, shape, seq, L, lo);
+        if (t >= pre + int64_t(ts) * ups) {
+            pre += int64_t(ts) * ups;
+            ++seq;
+            continue;
+        }
+        if (shape.inwave && lane == 0) p.ws_prefix[seq] = pre;
+        const int64_t local = t - pre;
+        const int u_in = int(local / ts);               // the KV head (one head group per KV head)
+        const int tile0 = int(local - int64_t(u_in) * ts);
+        const int tile1 = int(min(int64_t(ts), int64_t(tile0) + (t_end - t)));
+        const int g = u_in;
+        // this lane's column: virtual head h = query row h / G, query head g G + h % G
+        const int h = l16;
+        const bool live = h < nh;
+        const int64_t my_row = int64_t(seq) * p.qlen + (live ? h / group : 0);
+        const int my_head = g * group + (live ? h % group : 0);
+
+        // Q^T operands (zero for padding columns)
+        V8 qf[DC];
+        {
+            const T *qrow = reinterpret_cast<const T *>(p.query) + my_row * p.q_stride + int64_t(my_head) * D;
+#pragma unroll
+            for (int n = 0; n < DC; ++n) {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (live) v = *reinterpret_cast<const uint4 *>(qrow + q_d(n));
+                qf[n] = __builtin_bit_cast(V8, v);
+            }
+        }
+        const float slope2 = (has_alibi && live) ? p.alibi_slopes[my_head] * kLog2e : 0.f;
+        const int pos = L - p.qlen + (live ? h / group : 0);
+        const int lo_h = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+        const int pos_min = L - p.qlen;
+        const int lo_max = p.window > 0 ? max(0, L - p.window) : 0;
+        const int kfirst = (lo / TILE + tile0) * TILE;
+        const int kend = min(L, (lo / TILE + tile1) * TILE);
+        const uint32_t head_off = uint32_t(g) * D * CB;
+        const uint32_t lane_off = uint32_t(l16) * row_bytes + head_off + 16u * uint32_t(lg);
+        const uint32_t v_lane0 = uint32_t(lg) * row_bytes + head_off + v_chunk[0];
+        const uint32_t v_lane1 = uint32_t(lg) * row_bytes + head_off + v_chunk[1];
+
+        float m_run = -INFINITY;
+        floatx4_v o[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+        floatx4_v lsum = floatx4_v{0.f, 0.f, 0.f, 0.f};
+
+        // One tile in two phases.  A: scores from the K registers kr, the V tile into LDS (FP8: from
+        // the V registers vr; 16-bit rows were copied into stage vs), and the V^T operands read
+        // back.  B: mask, softmax and the P.V and row-sum MFMAs.  The compiler waits for every
+        // outstanding load-to-LDS copy before an LDS read, so with copies the next tile's loads
+        // are issued between the two phases, after this tile's reads.
+        floatx4_v s[2];
+        V8 vop[DB];
+        auto tile_a = [&](int tb, const uint4 (&kr)[2][NL], const uint4 (&vr)[2][NVR], bf16_t *vs) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                s[kk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int n = 0; n < DC; ++n) {
+                    V8 ka;
+                    if constexpr (CB == 1) {
+                        const uint4 c = kr[kk][n >> 1];
+                        ka = __builtin_bit_cast(V8, widen_e4m3<T>((n & 1) ? make_uint2(c.z, c.w) : make_uint2(c.x, c.y)));
+                    } else {
+                        ka = __builtin_bit_cast(V8, kr[kk][n]);
+                    }
+                    s[kk] = mfma16(ka, qf[n], s[kk]);
+                }
+            }
+            const bool tail = tb + TILE > L;
+            if constexpr (!VDMA) {
+                // FP8: widened V rows into the LDS tile (rows past the sequence's end zeroed: their
+                // zero weights must not meet unwritten cache bytes)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int key = 16 * kk + l16;
+                    const bool past = tail && tb + key >= L;
+                    bf16_t *row = vs + key * D;
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) {
+                        const uint4 c = vr[kk][j];
+                        uint4 lo8 = widen_e4m3<T>(make_uint2(c.x, c.y));
+                        uint4 hi8 = widen_e4m3<T>(make_uint2(c.z, c.w));
+                        if (past) lo8 = hi8 = make_uint4(0u, 0u, 0u, 0u);
+                        const int u = 4 * j + lg;                 // 32-byte unit of d = 64 j + 16 lg
+                        uint4 *dst = reinterpret_cast<uint4 *>(row + ((u ^ mfma_vswz(key)) << 4));
+                        dst[0] = lo8;
+                        dst[1] = hi8;
+                    }
+                }
+            }
+            wave_lds_sync();
+            // copied V rows past the sequence's end hold unwritten cache bytes: their weights are
+            // zero, but 0 * NaN would poison O, so the tail tile's operands of those keys are zeroed
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16_t *vb = vs + v_off[db];
+                v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)vb);
+                v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + 16 * D));
+                if (VDMA && tail) {
+                    // lane holds keys 4 lg + i (a) and 16 + 4 lg + i (b) of the tile
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        a[i] = tb + 4 * lg + i < L ? a[i] : short(0);
+                        b[i] = tb + 16 + 4 * lg + i < L ? b[i] : short(0);
+                    }
+                }
+                const v4i16 both[2] = {a, b};
+                vop[db] = __builtin_bit_cast(V8, both);
+            }
+            wave_lds_sync();
+        };
+        auto tile_b = [&](int tb) {
+            // scores in base-2 units, bias and mask: key tb + 16 kk + 4 lg + i
+            const bool edge = tb < lo_max || tb + TILE - 1 > pos_min;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = s[kk][i] * qk_scale;
+                    if (has_cap) x = cap2 * tanh_fast(x);
+                    const int key = tb + 16 * kk + 4 * lg + i;
+                    if (has_alibi) x += slope2 * float(key - pos);
+                    if (edge) x = (key >= lo_h && key <= pos) ? x : -INFINITY;
+                    s[kk][i] = x;
+                }
+            float tmax = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+            tmax = fmaxf(fmaxf(tmax, s[0][3]), s[1][0]);
+            tmax = fmaxf(fmaxf(tmax, s[1][1]), s[1][2]);
+            tmax = max_xor32(max_xor16(fmaxf(tmax, s[1][3])));
+            if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
+                const float m_new = fmaxf(m_run, tmax);
+                const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+                m_run = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[db] *= alpha;
+            }
+            uint32_t pk[2][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float pf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pf[i] = (s[kk][i] == -INFINITY) ? 0.f : fast_exp2(s[kk][i] - m_run);
+                pk[kk][0] = pack_x2<T>(pf[0], pf[1]);
+                pk[kk][1] = pack_x2<T>(pf[2], pf[3]);
+            }
+            const V8 pb = __builtin_bit_cast(V8, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = mfma16(vop[db], pb, o[db]);
+            lsum = mfma16(ones, pb, lsum);
+        };
+
+        for (int ch = kfirst / shape.chunk; ch * shape.chunk < kend; ++ch) {
+            int ids0, ids1;
+            load_ids(p, shape, seq, ch, lane, ids0, ids1);
+            const int cend = min(kend, (ch + 1) * shape.chunk);
+            const int pblock0 = (ch * shape.chunk) >> p.block_shift;
+            // base of 16-key block kk of the tile at tb (one cache block holds all 16 keys)
+            auto block_base = [&](int tb, int kk) -> int64_t {
+                const int row0 = tb + 16 * kk;
+                const int bidx = (row0 >> p.block_shift) - pblock0;
+                const int blk = __builtin_amdgcn_readlane(bidx < 64 ? ids0 : ids1, bidx & 63);
+                return int64_t(blk) * block_bytes + int64_t(row0 & bmask) * row_bytes;
+            };
+            auto load_k = [&](int tb, uint4 (&x)[2][NL]) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const char *base = kcache + block_base(tb, kk) + lane_off;
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) x[kk][j] = *reinterpret_cast<const uint4 *>(base + 64 * j);
+                }
+            };
+            // V of the tile at tb: copies into stage vs (16-bit) or loads into registers (FP8)
+            auto load_v = [&](int tb, uint4 (&x)[2][NVR], bf16_t *vs) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if constexpr (VDMA) {
+                        const char *base = vcache + block_base(tb, kk);
+                        const uint32_t lds0 = lds_address(vs + 16 * kk * D);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            dma16_at(base, (q & 1) ? v_lane1 : v_lane0, uint32_t(4 * q) * row_bytes,
+                                     lds0 + uint32_t(4 * q * D * 2));
+                    } else {
+                        const char *base = vcache + block_base(tb, kk) + lane_off;
+#pragma unroll
+                        for (int j = 0; j < NL; ++j) x[kk][j] = *reinterpret_cast<const uint4 *>(base + 64 * j);
+                    }
+                }
+            };
+            const int tfirst = max(kfirst, ch * shape.chunk);
+            const int tlast = ((cend - 1) / TILE) * TILE;
+            uint4 kr[DEPTH][2][NL], vr[DEPTH][2][NVR];
+#pragma unroll
+            for (int d = 0; d < DEPTH - 1; ++d) {
+                const int tt = min(tfirst + d * TILE, tlast);
+                load_k(tt, kr[d]);
+                load_v(tt, vr[d], vt[VDMA ? d : 0]);
+            }
+            int tb = tfirst;
+            bool done = false;
+            while (!done) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    if (!done) {
+                        const int nd = (d + DEPTH - 1) % DEPTH;
+                        const int ahead = min(tb + (DEPTH - 1) * TILE, tlast);
+                        if constexpr (VDMA) {
+                            tile_a(tb, kr[d], vr[d], vt[d]);
+                            load_k(ahead, kr[nd]);
+                            load_v(ahead, vr[nd], vt[nd]);
+                        } else {
+                            load_k(ahead, kr[nd]);
+                            load_v(ahead, vr[nd], vt[0]);
+                            tile_a(tb, kr[d], vr[d], vt[0]);
+                        }
+                        tile_b(tb);
+                        done = tb >= tlast;
+                        tb += TILE;
+                    }
+                }
+            }
+            if constexpr (VDMA) {
+                // no copy may still be writing a stage when the next chunk or unit reuses it
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                wave_lds_sync();
+            }
+        }
+
+        const float l_sum = lsum[0];
+        if (tile0 == 0 && tile1 == ts) {
+            if (live) {
+                float lh = l_sum;
+                if (p.sinks) lh += fast_exp2(p.sinks[my_head] * kLog2e - m_run);
+                const float inv = p.out_scale / lh;
+                T *out_row = reinterpret_cast<T *>(p.out) + (my_row * p.num_heads + my_head) * D + 4 * lg;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const uint2 w = make_uint2(pack_x2<T>(o[db][0] * inv, o[db][1] * inv),
+                                               pack_x2<T>(o[db][2] * inv, o[db][3] * inv));
+                    *reinterpret_cast<uint2 *>(out_row + 16 * db) = w;
+                }
+            }
+        } else if (live) {
+            const int64_t slot = (int64_t(wave) + int64_t(seq) * ups + u_in) * nh + h;
+            float *dst = p.ws_acc + slot * D + 4 * lg;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<float4 *>(dst + 16 * db) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+            if (lg == 0) {
+                p.ws_ml[slot * 2] = m_run;
+                p.ws_ml[slot * 2 + 1] = l_sum;
+            }
+        }
+
+        t += tile1 - tile0;
+        if (tile1 == ts && u_in == ups - 1) {
+            pre += int64_t(ts) * ups;
+            ++seq;
+        }
+    }
+}
+
 // Merge, one wavefront per (work unit, head of its group): zero rows of empty sequences, and for
 // units split over several wavefronts out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i over
 // their partials.  Lane j takes partial i0 + j (+ 64 k) for the (max, sum) step, so the step
@@ -939,6 +1332,41 @@ hipError_t launch_typed(const DecodeParams &p, const DecodeShape &s, hipStream_t
     return hipGetLastError();
 }
 
+// Resident wavefronts of the MFMA instance for element type T (cached per device, as split_waves).
+template <typename T>
+int mfma_waves() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const void *fn = reinterpret_cast<const void *>(&decode_mfma_kernel<T, 128, mfma_depth<T>(), mfma_occ<T>()>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 8;
+    cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+    return cus * per_cu;
+}
+
+template <typename T>
+hipError_t launch_mfma(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
+    const int64_t units = int64_t(p.num_seqs) * s.units_per_seq;
+    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (!s.inwave) {
+        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p, s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, mfma_depth<T>(), mfma_occ<T>()>), dim3(unsigned(s.num_waves)),
+                       dim3(64), 0, stream, p, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t merges = units * s.heads_per_group;
+    if (merges > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3(unsigned(merges)), dim3(64), 0, stream, p, s);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int GP>
 hipError_t launch_kvh(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
     if constexpr (kvh_max<T, GP>() > 1) {
@@ -1017,11 +1445,29 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     // Block-id chunk: 128 blocks (two id registers per lane), at most 4096 keys.
     plan.chunk = (128 << block_shift) < 4096 ? (128 << block_shift) : 4096;
     int kvh = 1, tile = 32, waves = 2048;
-    dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
-        instance_info<typename decltype(t)::type, decltype(d)::value>(plan.padded_group, num_kv_heads, block_shift, kvh,
-                                                                      tile, waves);
-        return 0;
-    });
+    // Wide groups of 16-bit (or FP8-cache) rows at head size 128 take the MFMA kernel: one work
+    // unit per (sequence, KV head) with all its virtual heads as MFMA columns.
+    const int mfma_min = (dtype == 3 || dtype == 4) ? PA_DECODE_MFMA_MIN_GROUP8 : PA_DECODE_MFMA_MIN_GROUP;
+    plan.mfma = dtype >= 1 && dtype <= 4 && head_size == 128 && block_shift >= 4 && group >= mfma_min &&
+                group <= kMfmaMaxHeads;
+    if (plan.mfma) {
+        plan.head_groups = 1;
+        plan.heads_per_group = group;
+        plan.padded_group = kMfmaMaxHeads;
+        tile = kMfmaTile;
+        switch (dtype) {
+            case 1: waves = mfma_waves<bf16_t>(); break;
+            case 2: waves = mfma_waves<f16_t>(); break;
+            case 3: waves = mfma_waves<bf16_c8_t>(); break;
+            default: waves = mfma_waves<f16_c8_t>(); break;
+        }
+    } else {
+        dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
+            instance_info<typename decltype(t)::type, decltype(d)::value>(plan.padded_group, num_kv_heads, block_shift,
+                                                                          kvh, tile, waves);
+            return 0;
+        });
+    }
     plan.kv_per_unit = kvh;
     plan.units_per_seq = num_kv_heads / kvh * plan.head_groups;
     plan.tile = tile;
@@ -1054,6 +1500,14 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
     s.inwave = p.num_seqs <= kInWavePlanMax &&
                        int64_t(p.num_seqs) * ((int64_t(p.max_seq_len) + s.tile - 1) / s.tile + 1) < (int64_t(1) << 30)
                    ? 1 : 0;
+    if (plan.mfma) {
+        switch (dtype) {
+            case 1: return launch_mfma<bf16_t>(p, s, stream);
+            case 2: return launch_mfma<f16_t>(p, s, stream);
+            case 3: return launch_mfma<bf16_c8_t>(p, s, stream);
+            default: return launch_mfma<f16_c8_t>(p, s, stream);
+        }
+    }
     return dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
         return launch_group<typename decltype(t)::type, decltype(d)::value>(p, s, plan.padded_group, stream);
     });

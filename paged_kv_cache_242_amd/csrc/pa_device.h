@@ -194,4 +194,63 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// max(x, x of lane ^ 16) and max(x, x of lane ^ 32) with the gfx950 row-swap moves (VALU, no
+// LDS traffic): swapping x with itself leaves each lane one of its own value and its partner's.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// 8 elements of a 16x16x32 MFMA operand, by element type (an FP8-cache type computes in its
+// 16-bit type).
+template <typename T>
+struct Operand8 { typedef bf16x8_v type; };
+template <>
+struct Operand8<f16_t> { typedef halfx8_v type; };
+template <>
+struct Operand8<f16_c8_t> { typedef halfx8_v type; };
+
+__device__ __forceinline__ floatx4_v mfma16(bf16x8_v a, bf16x8_v b, floatx4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4_v mfma16(halfx8_v a, halfx8_v b, floatx4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte-per-lane global -> LDS copy: lane l reads base + soff + lane_off (bytes) and fills
+// 16-byte unit l of the 1 KB stretch at lds_dst.  base and soff must be wave-uniform; base goes
+// into a raw buffer descriptor (scalar registers), soff into the scalar offset and the lane
+// offset into the vector offset.
+__device__ __forceinline__ void dma16(const char *base, uint32_t lane_off, uint32_t soff, bf16_t *lds_dst) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, lane_off, soff, 0, 0);
+}
+
+// The same copy into the LDS byte address lds_addr.
+__device__ __forceinline__ void dma16_at(const char *base, uint32_t lane_off, uint32_t soff, uint32_t lds_addr) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)lds_addr, 16, lane_off, soff, 0, 0);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return uint32_t(uintptr_t((const lds_void *)p));
+}
+
+// The same copy from a per-lane address.
+__device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
+    __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)lds_dst, 16, 0, 0);
+}
+
 }  // namespace pa

@@ -36,13 +36,14 @@ hipError_t launch_copy_blocks(const CopyBlocksParams &p, int32_t num_layers, hip
 // Decode policy shared by pa_decode and pa_decode_workspace_size.
 struct DecodePlan {
     int32_t head_groups;      // query heads of one KV head are processed in this many groups
-    int32_t heads_per_group;  // real heads per group (<= 8)
-    int32_t padded_group;     // heads_per_group rounded up to 1, 2, 4 or 8
+    int32_t heads_per_group;  // real heads per group (<= 8; <= 16 for the MFMA kernel)
+    int32_t padded_group;     // heads_per_group rounded up to 1, 2, 4 or 8 (16 for the MFMA kernel)
     int32_t kv_per_unit;      // KV heads per work unit (1 or 2)
     int32_t units_per_seq;    // num_kv_heads / kv_per_unit * head_groups work units per sequence
     int32_t chunk;            // keys per block-id chunk
     int32_t tile;             // keys per tile of the kernel instance
     int32_t num_waves;        // wavefronts of the even split (resident at once on the device)
+    int32_t mfma;             // 1: the MFMA kernel (one unit per sequence and KV head, <= 16 virtual heads)
     size_t ws_prefix_off, ws_wseq_off, ws_acc_off, ws_ml_off;   // workspace layout (bytes)
     size_t workspace_bytes;
 };

@@ -116,55 +116,12 @@ struct PrefillGrid {
     int compact;           // 1: only groups of existing query tiles are enumerated (qtiles_per_group 1)
 };
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
 // V tile swizzle of row r: spreads the 8 rows read together by 32 lanes of the transposing load
 // (4 rows at 8 bytes per lane in each 16-lane group) over distinct 32-byte units of a 256-byte
 // bank window.
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
     return D >= 128 ? (r & 7) : ((r >> 1) & 3);
-}
-
-// max(x, x of lane ^ 16) and max(x, x of lane ^ 32) with the gfx950 row-swap moves (VALU, no
-// LDS traffic): swapping x with itself leaves each lane one of its own value and its partner's.
-__device__ __forceinline__ float max_xor16(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// One 16-byte-per-lane global -> LDS copy: lane l reads base + soff + lane_off (bytes) and fills
-// 16-byte unit l of the 1 KB stretch at lds_dst.  base and soff must be wave-uniform; base goes
-// into a raw buffer descriptor (scalar registers), soff into the scalar offset and the lane
-// offset into the vector offset.
-__device__ __forceinline__ void dma16(const char *base, uint32_t lane_off, uint32_t soff, bf16_t *lds_dst) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_dst, 16, lane_off, soff, 0, 0);
-}
-
-// The same copy into the LDS byte address lds_addr.
-__device__ __forceinline__ void dma16_at(const char *base, uint32_t lane_off, uint32_t soff, uint32_t lds_addr) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)lds_addr, 16, lane_off, soff, 0, 0);
-}
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-    return uint32_t(uintptr_t((const lds_void *)p));
-}
-
-// The same copy from a per-lane address.
-__device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
-    __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)lds_dst, 16, 0, 0);
 }
 
 // Tile staging.  K and V tiles (64 keys x D) are copied global -> LDS by the load-to-LDS path
@@ -194,20 +151,6 @@ __device__ __forceinline__ void dma16_lane(const char *src, bf16_t *lds_dst) {
 // Q = 0); the raw scores become c log2(e) tanh(s |scale| / c) right after the score MFMAs, the
 // ALiBi key term is added to them in fp32 (it must stay outside the cap), and the exponent
 // subtracts the running max.  Sink logits (p.sinks) join the row sums in the epilogue.
-
-template <typename T>
-struct Operand8 { typedef bf16x8_v type; };   // 8 elements of an MFMA operand
-template <>
-struct Operand8<f16_t> { typedef halfx8_v type; };
-template <>
-struct Operand8<f16_c8_t> { typedef halfx8_v type; };
-
-__device__ __forceinline__ floatx4_v mfma16(bf16x8_v a, bf16x8_v b, floatx4_v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4_v mfma16(halfx8_v a, halfx8_v b, floatx4_v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 
 // Head size 256 doubles the O accumulators and the operands per wavefront and the LDS stages
 // (128 KB): one workgroup per CU then, with the register file of a single wavefront per SIMD.

@@ -203,6 +203,9 @@ DECODE_LAYERS = [
     _layer(32, 32, 128, 16, wl.F16, fp8=True, alibi=True, window=100),
     _layer(16, 2, 64, 8, fp8=True, softcap=3.0, scale=0.3),
     _layer(12, 2, 128, 64, wl.F16, fp8=True),
+    # fp8 cache with 5 or more query heads per KV head at head size 128: the MFMA decode kernel
+    _layer(64, 8, 128, 16, wl.F16, fp8=True, alibi=True, window=300),
+    _layer(40, 8, 128, 32, fp8=True, softcap=5.0, scale=0.3, sinks=True),
     # head size 256
     _layer(16, 8, 256, 16),
     _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
@@ -347,19 +350,24 @@ def test_multi_token_decode_as_chunked_prefill(k, layer):
 
 # ------------------------------------------------------------------------------ full-size workloads
 
-# (query_len, layer, number of extra sequences).  Calls whose query rows times query heads per KV
-# head exceed 8 (16-bit layers) run on the MFMA prefill kernel with every key from the cache; the
-# others, and fp32 layers, on the decode kernels.
+# (query_len, layer, number of extra sequences).  Query rows times query heads per KV head ("virtual
+# heads") decide the kernel: up to 8 the VALU decode kernel (from 5 the MFMA decode kernel for an
+# fp8 cache), 9 to 16 at head size 128 the MFMA decode kernel, more (16-bit layers) the MFMA
+# prefill kernel with every key from the cache; fp32 layers always the VALU decode kernel.
 MULTI_CASES = [
-    (2, _layer(32, 8, 128, 16), 0),                               # 8 virtual heads: decode kernels
-    (4, _layer(32, 8, 128, 16), 0),                               # 16: prefill kernel
-    (3, _layer(32, 32, 128, 16, alibi=True, window=300), 0),      # 3 rows of one head: decode, padded group of 4
-    (2, _layer(64, 8, 128, 32, fp8=True), 0),                     # 16, fp8 cache: prefill kernel
+    (2, _layer(32, 8, 128, 16), 0),                               # 8 virtual heads: VALU decode
+    (4, _layer(32, 8, 128, 16), 0),                               # 16: MFMA decode
+    (3, _layer(32, 32, 128, 16, alibi=True, window=300), 0),      # 3 rows of one head: VALU decode, padded group of 4
+    (2, _layer(64, 8, 128, 32, fp8=True), 0),                     # 16, fp8 cache: MFMA decode
+    (4, _layer(32, 8, 128, 16, wl.F16, alibi=True, sinks=True, softcap=4.0, scale=0.25), 0),   # 16: MFMA decode
+    (3, _layer(24, 8, 128, 16, alibi=True, window=50), 0),        # 9 (padded to 16 columns): MFMA decode
+    (2, _layer(32, 8, 128, 16, fp8=True, alibi=True, window=500), 0),   # 8, fp8 cache: MFMA decode
     (4, _layer(16, 2, 64, 8, wl.F16, sinks=True, softcap=3.0, scale=0.3), 0),   # 32: prefill kernel
     (2, _layer(8, 8, 64, 16, wl.F32, alibi=True, window=40), 0),  # fp32: decode kernels
     (8, _layer(8, 1, 128, 16, alibi=True), 0),                    # 64: prefill kernel
     (4, _layer(16, 4, 256, 16, alibi=True, window=300), 0),       # head size 256: prefill kernel
-    (3, _layer(32, 8, 128, 16, window=1000), 64),                 # 80 sequences (no compact grid): prefill kernel
+    (3, _layer(32, 8, 128, 16, window=1000), 64),                 # 12, 80 sequences: MFMA decode
+    (6, _layer(32, 8, 128, 16, window=1000), 64),                 # 24, 80 sequences (no compact grid): prefill kernel
 ]
 
 
@@ -538,7 +546,8 @@ def test_workload5_full():
 
 # ------------------------------------------------------------------------------ split-KV cut points
 
-@pytest.mark.parametrize("layer", [_layer(32, 8, 128, 16), _layer(64, 8, 128, 32, alibi=True, window=3000)])
+@pytest.mark.parametrize("layer", [_layer(32, 8, 128, 16), _layer(64, 8, 128, 32, alibi=True, window=3000),
+                                   _layer(64, 8, 128, 32, fp8=True)])
 def test_decode_split_cut_invariance(layer):
     """The even split cuts the concatenated key tiles of all sequences at fixed fractions, so the
     sequences placed before a sequence decide where its cuts fall.  One batch of 23 + 12 sequences;
@@ -571,14 +580,16 @@ def test_decode_split_cut_invariance(layer):
         gh.assert_close(outs[k], outs[0], batch.layer, f"placement {k} against placement 0")
 
 
-@pytest.mark.parametrize("n", [1500, 2600])
-def test_decode_many_sequences(n):
+@pytest.mark.parametrize("n,fp8", [(1500, False), (2600, False), (2600, True)])
+def test_decode_many_sequences(n, fp8):
     """Many short sequences (lengths 0 to 300, some padded) against the oracle.  Up to 2048
     sequences each split wavefront scans all of them (64 per step) to find its first sequence; 2600
-    take the planning kernel, whose threads scan chunks of sequences and search inside a chunk."""
-    layer = _layer(32, 8, 128, 16)
+    take the planning kernel, whose threads scan chunks of sequences and search inside a chunk.  The
+    fp8 case (8 query heads per KV head) runs the MFMA decode kernel; its lengths stay below 40,
+    since the oracle's quantizing cache write searches the code table element by element."""
+    layer = _layer(64, 8, 128, 16, fp8=True) if fp8 else _layer(32, 8, 128, 16)
     rng = np.random.default_rng(99)
-    lens = rng.integers(0, 300, size=n)
+    lens = rng.integers(0, 40 if fp8 else 300, size=n)
     lens[::97] = 0
     batch = wl.make_batch(layer, seed=99, decode=lens.tolist(), device=gh.device())
     _check_full(batch, f"{n} sequences")
