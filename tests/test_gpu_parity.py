@@ -223,14 +223,17 @@ def test_decode_grid(li):
     _check_full(batch, f"decode layer {li}")
 
 
-def test_decode_strided_query_and_determinism():
-    layer = _layer(32, 8, 128, 16)
+@pytest.mark.parametrize("layer", [_layer(32, 8, 128, 16), _layer(64, 8, 128, 16, fp8=True)])
+def test_decode_strided_query_and_determinism(layer):
+    """A query view with a row stride of three rows (the VALU kernel, and the MFMA kernel through
+    an fp8 cache with 8 query heads per KV head) equals the contiguous query's output bit for bit."""
     batch = wl.make_batch(layer, seed=50, decode=[700, 3000, 1, 64], device=gh.device())
     pl = gh.player(batch.layer)
     cache = gh.gpu_pool(batch, pl)
-    wide = torch.zeros(4, 3 * 32 * 128, dtype=torch.bfloat16, device=gh.device())
-    wide[:, 128:128 + 4096] = batch.query
-    q = wide[:, 128:128 + 4096]
+    width = layer.num_heads * layer.head_size
+    wide = torch.zeros(4, 3 * width, dtype=torch.bfloat16, device=gh.device())
+    wide[:, 128:128 + width] = batch.query
+    q = wide[:, 128:128 + width]
     bt, sl = gh.i32(batch.decode_block_tables), gh.i32(batch.decode_seq_lens)
     a = gh.pa().decode(q, cache, bt, sl, pl, 3000)
     b = gh.pa().decode(batch.query, cache, bt, sl, pl, 3000)
@@ -401,8 +404,9 @@ def test_decode_multi(ci):
 
 def test_graph_capture_replays():
     """The library neither allocates, nor synchronizes, nor clears memory with memset, so a whole
-    step -- cache write, prefill, decode, multi-token decode -- can be captured in a HIP graph:
-    three replays, with eager work in between, each reproduce the eager outputs bit for bit."""
+    step -- cache write, prefill, decode, multi-token decode (2 rows: VALU decode kernel; 4 rows,
+    16 virtual heads: MFMA decode kernel) -- can be captured in a HIP graph: three replays, with
+    eager work in between, each reproduce the eager outputs bit for bit."""
     layer = _layer(16, 4, 128, 16, alibi=True, window=200, sinks=True)
     batch = wl.make_batch(layer, seed=95, prefill=[(100, 150), (0, 90)], decode=[1, 250, 700, 0],
                           device=gh.device())
@@ -421,30 +425,36 @@ def test_graph_capture_replays():
     m_sl = gh.i32(batch.prefill_context_lens + batch.prefill_query_lens)
     q_multi = torch.stack([batch.query[int(batch.prefill_cu[i + 1]) - 2:int(batch.prefill_cu[i + 1])]
                            for i in range(2)]).reshape(4, -1).contiguous()
+    q_multi4 = torch.stack([batch.query[int(batch.prefill_cu[i + 1]) - 4:int(batch.prefill_cu[i + 1])]
+                            for i in range(2)]).reshape(8, -1).contiguous()
     out_pre, out_dec, out_multi = torch.empty_like(p_args[0]), torch.empty_like(q_dec), torch.empty_like(q_multi)
+    out_multi4 = torch.empty_like(q_multi4)
     ws_d = torch.empty(pa.decode_workspace_size(pl, 4, 700), dtype=torch.uint8, device=gh.device())
     ws_m = torch.empty(pa.decode_workspace_size(pl, 2, 400, 2), dtype=torch.uint8, device=gh.device())
+    ws_m4 = torch.empty(pa.decode_workspace_size(pl, 2, 400, 4), dtype=torch.uint8, device=gh.device())
 
     def step():
         pa.cache_write(batch.key, batch.value, cache, slots, pl)
         pa.prefill_varlen(*p_args, out=out_pre)
         pa.decode(q_dec, cache, d_bt, d_sl, pl, 700, out=out_dec, workspace=ws_d)
         pa.decode(q_multi, cache, m_bt, m_sl, pl, 400, out=out_multi, workspace=ws_m, query_len=2)
+        pa.decode(q_multi4, cache, m_bt, m_sl, pl, 400, out=out_multi4, workspace=ws_m4, query_len=4)
 
+    outs = (out_pre, out_dec, out_multi, out_multi4)
     step()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (out_pre, out_dec, out_multi)]
+    ref = [t.clone() for t in outs]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in (out_pre, out_dec, out_multi):
+        for t in outs:
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for name, got, want in zip(("prefill", "decode", "multi-token decode"), (out_pre, out_dec, out_multi), ref):
+        for name, got, want in zip(("prefill", "decode", "multi-token decode", "4-row decode"), outs, ref):
             assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {rep}: {name} differs"
 
 

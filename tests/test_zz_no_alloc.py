@@ -1,6 +1,7 @@
 """pa_decode_noalloc (decode with the library's fixed device scratch array instead of a caller
 workspace) against pa_decode on the same inputs: two calls in a row, the second on a smaller
-batch, each bit-identical to pa_decode (the same kernels and split) and within the bf16
+batch, each bit-identical to pa_decode (the same kernels and split: the VALU decode kernel, and
+the MFMA decode kernel for an fp8 cache with 8 query heads per KV head) and within the bf16
 tolerance of the fp64 oracle."""
 import math
 
@@ -24,6 +25,10 @@ def _layer(H, Hkv, D, bs, **kw):
     ((_layer(64, 8, 128, 32, alibi_slopes=wl.alibi_slopes_geometric(64), sliding_window=700), 303,
       [5000, 12000, 1, 640] * 4),
      (_layer(8, 8, 64, 16), 304, [3, 129])),
+    # an fp8 cache with 8 query heads per KV head: the MFMA decode kernel
+    ((_layer(64, 8, 128, 16, kv_cache_dtype="fp8_e4m3", k_scale=wl.fp32(0.02), v_scale=wl.fp32(0.015)), 305,
+      [3000, 1, 700, 0, 2049]),
+     (_layer(32, 8, 128, 16), 306, [40, 600])),
 ])
 def test_decode_noalloc_matches_decode(first, second):
     pa = gh.pa()
