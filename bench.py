@@ -517,7 +517,7 @@ def multi_token_leg(pa, r, ks=(2, 4, 8), reps: int = 10):
         gbps = nbytes / (st["ms"] * 1e-3) / 1e9
         if L.dtype == wl.F32 or k * G <= 8:
             kern = "VALU decode"
-        elif k * G <= 16 and L.head_size == 128 and L.block_size >= 16:
+        elif k * G <= 32 and L.head_size == 128 and L.block_size >= 16:
             kern = "MFMA decode"
         else:
             kern = "MFMA prefill"

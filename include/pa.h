@@ -170,8 +170,8 @@ size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t
  * the device holds at once (each wavefront finds its share from seq_lens on the device; above
  * 2048 sequences a small planning kernel does it first); a pair cut between wavefronts leaves
  * (max, sum, weighted-V) partials that a second kernel merges with the log-sum-exp rule.  The
- * dot products run on the VALU, or on the matrix unit for head size 128 with an FP8 cache and
- * 5 or more query heads per KV head.
+ * dot products run on the VALU, or on the matrix unit at head size 128 (block size >= 16) with
+ * an FP8 cache and 5 to 32 query heads per KV head, or 9 to 32 query heads per KV head.
  */
 pa_status pa_decode(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
                     const void *kv_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -206,7 +206,7 @@ pa_status pa_decode_noalloc(const pa_layer *layer, void *out, const void *query,
  * the window, ALiBi, soft-cap and sinks as in decode) to the cached keys up to it.  The query
  * rows of a sequence and the query heads of a KV head ("virtual heads", query_len *
  * num_heads / num_kv_heads of them) share every K/V byte read: up to 8 of them (and for fp32
- * layers) on the decode kernels; 9 to 16 at head size 128 (block size >= 16) on the MFMA decode
+ * layers) on the decode kernels; 9 to 32 at head size 128 (block size >= 16) on the MFMA decode
  * kernel; beyond that, for bf16 and fp16 layers, on the MFMA prefill kernel (a chunked prefill of
  * query_len rows whose keys all come from the cache), which also shares each K/V tile among them.
  *   out              device [num_seqs * query_len, num_heads * head_size], contiguous, written

@@ -781,11 +781,12 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
 // ---- MFMA variant for wide head groups ------------------------------------------------------
 // With many virtual heads per KV head the dot products of the VALU kernel above cost more issue
 // time than the bytes take to arrive: an FP8 cache with a group of 8 query heads (the bytes halve,
-// the products do not), or the 9 to 16 query rows x heads of a multi-token decode, which the VALU
-// kernel could only split over two units that each read K/V.  This kernel forms the products on
+// the products do not), or 9 to 32 query rows x heads (wide groups, multi-token decode), which the
+// VALU kernel could only split over units of 8 that each read K/V.  This kernel forms the products on
 // the matrix unit instead, with the same work split, partial slots and merge:
-//   * a work unit is one (sequence, KV head) with its nh <= 16 virtual heads as the 16 columns
-//     of v_mfma_f32_16x16x32_{bf16,f16};
+//   * a work unit is one (sequence, KV head) with its nh <= 32 virtual heads as the columns of
+//     v_mfma_f32_16x16x32_{bf16,f16}, in NB = 1 or 2 blocks of 16 that share every K and V
+//     operand;
 //   * a 32-key tile is two 16-key blocks; lane (k = lane % 16, g = lane / 16) loads 16 bytes at
 //     byte 64 j + 16 g of key k's head row for j = 0 .. NL - 1, which for 16-bit rows is exactly
 //     the A operand of S^T = K Q^T (d = 32 j + 8 g .. + 7 for MFMA j).  For an FP8 row a load
@@ -805,7 +806,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
 // of 16-bit rows the VALU kernel is as fast or faster (its products still hide behind the bytes),
 // so it keeps them.
 constexpr int kMfmaTile = 32;
-constexpr int kMfmaMaxHeads = 16;
+constexpr int kMfmaMaxHeads = 32;          // two blocks of 16 MFMA columns
 // Smallest group (query heads x query rows per KV head) that takes the MFMA kernel: 16-bit rows
 // past the VALU kernel's 8 heads per unit; FP8 rows from 5 (at 4 the two kernels are level).
 #ifndef PA_DECODE_MFMA_MIN_GROUP
@@ -827,16 +828,23 @@ constexpr int kMfmaMaxHeads = 16;
 #ifndef PA_DECODE_MFMA_OCC8
 #define PA_DECODE_MFMA_OCC8 2
 #endif
+// With two column blocks (17 to 32 virtual heads) the second set of Q operands and accumulators
+// leaves room for one wavefront per SIMD.
+#ifndef PA_DECODE_MFMA_OCC_NB2
+#define PA_DECODE_MFMA_OCC_NB2 1
+#endif
 template <typename T>
 constexpr int mfma_depth() { return kFp8Cache<T> ? PA_DECODE_MFMA_DEPTH8 : PA_DECODE_MFMA_DEPTH; }
-template <typename T>
-constexpr int mfma_occ() { return kFp8Cache<T> ? PA_DECODE_MFMA_OCC8 : PA_DECODE_MFMA_OCC; }
+template <typename T, int NB>
+constexpr int mfma_occ() {
+    return NB > 1 ? PA_DECODE_MFMA_OCC_NB2 : (kFp8Cache<T> ? PA_DECODE_MFMA_OCC8 : PA_DECODE_MFMA_OCC);
+}
 
 // V tile swizzle: the 32-byte unit u of key r sits at unit u ^ (r & 7), so the 8 keys a
 // transposing read touches at one d fall in distinct 32-byte units.
 __device__ __forceinline__ int mfma_vswz(int r) { return r & 7; }
 
-template <typename T, int D, int DEPTH, int OCC>
+template <typename T, int D, int NB, int DEPTH, int OCC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
     typedef typename Operand8<T>::type V8;
@@ -918,26 +926,30 @@ void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
         const int tile0 = int(local - int64_t(u_in) * ts);
         const int tile1 = int(min(int64_t(ts), int64_t(tile0) + (t_end - t)));
         const int g = u_in;
-        // this lane's column: virtual head h = query row h / G, query head g G + h % G
-        const int h = l16;
-        const bool live = h < nh;
-        const int64_t my_row = int64_t(seq) * p.qlen + (live ? h / group : 0);
-        const int my_head = g * group + (live ? h % group : 0);
-
-        // Q^T operands (zero for padding columns)
-        V8 qf[DC];
-        {
-            const T *qrow = reinterpret_cast<const T *>(p.query) + my_row * p.q_stride + int64_t(my_head) * D;
+        // this lane's columns: virtual head h = 16 b + l16 of column block b = query row h / G,
+        // query head g G + h % G
+        bool live[NB];
+        int64_t my_row[NB];
+        int my_head[NB], pos[NB], lo_h[NB];
+        float slope2[NB];
+        V8 qf[NB][DC];          // Q^T operands (zero for padding columns)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int h = 16 * b + l16;
+            live[b] = h < nh;
+            my_row[b] = int64_t(seq) * p.qlen + (live[b] ? h / group : 0);
+            my_head[b] = g * group + (live[b] ? h % group : 0);
+            const T *qrow = reinterpret_cast<const T *>(p.query) + my_row[b] * p.q_stride + int64_t(my_head[b]) * D;
 #pragma unroll
             for (int n = 0; n < DC; ++n) {
                 uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (live) v = *reinterpret_cast<const uint4 *>(qrow + q_d(n));
-                qf[n] = __builtin_bit_cast(V8, v);
+                if (live[b]) v = *reinterpret_cast<const uint4 *>(qrow + q_d(n));
+                qf[b][n] = __builtin_bit_cast(V8, v);
             }
+            slope2[b] = (has_alibi && live[b]) ? p.alibi_slopes[my_head[b]] * kLog2e : 0.f;
+            pos[b] = L - p.qlen + (live[b] ? h / group : 0);
+            lo_h[b] = p.window > 0 ? max(0, pos[b] - p.window + 1) : 0;
         }
-        const float slope2 = (has_alibi && live) ? p.alibi_slopes[my_head] * kLog2e : 0.f;
-        const int pos = L - p.qlen + (live ? h / group : 0);
-        const int lo_h = p.window > 0 ? max(0, pos - p.window + 1) : 0;
         const int pos_min = L - p.qlen;
         const int lo_max = p.window > 0 ? max(0, L - p.window) : 0;
         const int kfirst = (lo / TILE + tile0) * TILE;
@@ -947,23 +959,28 @@ void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
         const uint32_t v_lane0 = uint32_t(lg) * row_bytes + head_off + v_chunk[0];
         const uint32_t v_lane1 = uint32_t(lg) * row_bytes + head_off + v_chunk[1];
 
-        float m_run = -INFINITY;
-        floatx4_v o[DB];
+        float m_run[NB];
+        floatx4_v o[NB][DB], lsum[NB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
-        floatx4_v lsum = floatx4_v{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NB; ++b) {
+            m_run[b] = -INFINITY;
+            lsum[b] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[b][db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+        }
 
         // One tile in two phases.  A: scores from the K registers kr, the V tile into LDS (FP8: from
         // the V registers vr; 16-bit rows were copied into stage vs), and the V^T operands read
         // back.  B: mask, softmax and the P.V and row-sum MFMAs.  The compiler waits for every
         // outstanding load-to-LDS copy before an LDS read, so with copies the next tile's loads
         // are issued between the two phases, after this tile's reads.
-        floatx4_v s[2];
+        floatx4_v s[NB][2];
         V8 vop[DB];
         auto tile_a = [&](int tb, const uint4 (&kr)[2][NL], const uint4 (&vr)[2][NVR], bf16_t *vs) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                s[kk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int b = 0; b < NB; ++b) s[b][kk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int n = 0; n < DC; ++n) {
                     V8 ka;
@@ -973,7 +990,8 @@ void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
                     } else {
                         ka = __builtin_bit_cast(V8, kr[kk][n]);
                     }
-                    s[kk] = mfma16(ka, qf[n], s[kk]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) s[b][kk] = mfma16(ka, qf[b][n], s[b][kk]);
                 }
             }
             const bool tail = tb + TILE > L;
@@ -1022,42 +1040,55 @@ void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
         auto tile_b = [&](int tb) {
             // scores in base-2 units, bias and mask: key tb + 16 kk + 4 lg + i
             const bool edge = tb < lo_max || tb + TILE - 1 > pos_min;
+            bool raise = false;
+            float tmax[NB];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int b = 0; b < NB; ++b) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = s[kk][i] * qk_scale;
-                    if (has_cap) x = cap2 * tanh_fast(x);
-                    const int key = tb + 16 * kk + 4 * lg + i;
-                    if (has_alibi) x += slope2 * float(key - pos);
-                    if (edge) x = (key >= lo_h && key <= pos) ? x : -INFINITY;
-                    s[kk][i] = x;
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = s[b][kk][i] * qk_scale;
+                        if (has_cap) x = cap2 * tanh_fast(x);
+                        const int key = tb + 16 * kk + 4 * lg + i;
+                        if (has_alibi) x += slope2[b] * float(key - pos[b]);
+                        if (edge) x = (key >= lo_h[b] && key <= pos[b]) ? x : -INFINITY;
+                        s[b][kk][i] = x;
+                    }
+                float mx = fmaxf(fmaxf(s[b][0][0], s[b][0][1]), s[b][0][2]);
+                mx = fmaxf(fmaxf(mx, s[b][0][3]), s[b][1][0]);
+                mx = fmaxf(fmaxf(mx, s[b][1][1]), s[b][1][2]);
+                tmax[b] = max_xor32(max_xor16(fmaxf(mx, s[b][1][3])));
+                raise |= tmax[b] > m_run[b] + kRescaleSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float m_new = fmaxf(m_run[b], tmax[b]);
+                    const float alpha = (m_run[b] == -INFINITY) ? 0.f : fast_exp2(m_run[b] - m_new);
+                    m_run[b] = m_new;
+                    lsum[b] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[b][db] *= alpha;
                 }
-            float tmax = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-            tmax = fmaxf(fmaxf(tmax, s[0][3]), s[1][0]);
-            tmax = fmaxf(fmaxf(tmax, s[1][1]), s[1][2]);
-            tmax = max_xor32(max_xor16(fmaxf(tmax, s[1][3])));
-            if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
-                const float m_new = fmaxf(m_run, tmax);
-                const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-                m_run = m_new;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) o[db] *= alpha;
             }
-            uint32_t pk[2][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                float pf[4];
+            for (int b = 0; b < NB; ++b) {
+                uint32_t pk[2][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pf[i] = (s[kk][i] == -INFINITY) ? 0.f : fast_exp2(s[kk][i] - m_run);
-                pk[kk][0] = pack_x2<T>(pf[0], pf[1]);
-                pk[kk][1] = pack_x2<T>(pf[2], pf[3]);
+                for (int kk = 0; kk < 2; ++kk) {
+                    float pf[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pf[i] = (s[b][kk][i] == -INFINITY) ? 0.f : fast_exp2(s[b][kk][i] - m_run[b]);
+                    pk[kk][0] = pack_x2<T>(pf[0], pf[1]);
+                    pk[kk][1] = pack_x2<T>(pf[2], pf[3]);
+                }
+                const V8 pb = __builtin_bit_cast(V8, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[b][db] = mfma16(vop[db], pb, o[b][db]);
+                lsum[b] = mfma16(ones, pb, lsum[b]);
             }
-            const V8 pb = __builtin_bit_cast(V8, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
-#pragma unroll
-            for (int db = 0; db < DB; ++db) o[db] = mfma16(vop[db], pb, o[db]);
-            lsum = mfma16(ones, pb, lsum);
         };
 
         for (int ch = kfirst / shape.chunk; ch * shape.chunk < kend; ++ch) {
@@ -1137,29 +1168,32 @@ void decode_mfma_kernel(DecodeParams p, DecodeShape shape) {
             }
         }
 
-        const float l_sum = lsum[0];
-        if (tile0 == 0 && tile1 == ts) {
-            if (live) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (!live[b]) continue;
+            const float l_sum = lsum[b][0];
+            if (tile0 == 0 && tile1 == ts) {
                 float lh = l_sum;
-                if (p.sinks) lh += fast_exp2(p.sinks[my_head] * kLog2e - m_run);
+                if (p.sinks) lh += fast_exp2(p.sinks[my_head[b]] * kLog2e - m_run[b]);
                 const float inv = p.out_scale / lh;
-                T *out_row = reinterpret_cast<T *>(p.out) + (my_row * p.num_heads + my_head) * D + 4 * lg;
+                T *out_row = reinterpret_cast<T *>(p.out) + (my_row[b] * p.num_heads + my_head[b]) * D + 4 * lg;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const uint2 w = make_uint2(pack_x2<T>(o[db][0] * inv, o[db][1] * inv),
-                                               pack_x2<T>(o[db][2] * inv, o[db][3] * inv));
+                    const uint2 w = make_uint2(pack_x2<T>(o[b][db][0] * inv, o[b][db][1] * inv),
+                                               pack_x2<T>(o[b][db][2] * inv, o[b][db][3] * inv));
                     *reinterpret_cast<uint2 *>(out_row + 16 * db) = w;
                 }
-            }
-        } else if (live) {
-            const int64_t slot = (int64_t(wave) + int64_t(seq) * ups + u_in) * nh + h;
-            float *dst = p.ws_acc + slot * D + 4 * lg;
+            } else {
+                const int64_t slot = (int64_t(wave) + int64_t(seq) * ups + u_in) * nh + 16 * b + l16;
+                float *dst = p.ws_acc + slot * D + 4 * lg;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                *reinterpret_cast<float4 *>(dst + 16 * db) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-            if (lg == 0) {
-                p.ws_ml[slot * 2] = m_run;
-                p.ws_ml[slot * 2 + 1] = l_sum;
+                for (int db = 0; db < DB; ++db)
+                    *reinterpret_cast<float4 *>(dst + 16 * db) =
+                        make_float4(o[b][db][0], o[b][db][1], o[b][db][2], o[b][db][3]);
+                if (lg == 0) {
+                    p.ws_ml[slot * 2] = m_run[b];
+                    p.ws_ml[slot * 2 + 1] = l_sum;
+                }
             }
         }
 
@@ -1332,8 +1366,9 @@ hipError_t launch_typed(const DecodeParams &p, const DecodeShape &s, hipStream_t
     return hipGetLastError();
 }
 
-// Resident wavefronts of the MFMA instance for element type T (cached per device, as split_waves).
-template <typename T>
+// Resident wavefronts of the MFMA instance for element type T and NB column blocks (cached per
+// device, as split_waves).
+template <typename T, int NB>
 int mfma_waves() {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -1342,13 +1377,14 @@ int mfma_waves() {
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    const void *fn = reinterpret_cast<const void *>(&decode_mfma_kernel<T, 128, mfma_depth<T>(), mfma_occ<T>()>);
+    const void *fn =
+        reinterpret_cast<const void *>(&decode_mfma_kernel<T, 128, NB, mfma_depth<T>(), mfma_occ<T, NB>()>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess || per_cu <= 0) per_cu = 8;
     cache[dev].store(cus * per_cu, std::memory_order_relaxed);
     return cus * per_cu;
 }
 
-template <typename T>
+template <typename T, int NB>
 hipError_t launch_mfma(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
     const int64_t units = int64_t(p.num_seqs) * s.units_per_seq;
     if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -1357,8 +1393,8 @@ hipError_t launch_mfma(const DecodeParams &p, const DecodeShape &s, hipStream_t 
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, mfma_depth<T>(), mfma_occ<T>()>), dim3(unsigned(s.num_waves)),
-                       dim3(64), 0, stream, p, s);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, NB, mfma_depth<T>(), mfma_occ<T, NB>()>),
+                       dim3(unsigned(s.num_waves)), dim3(64), 0, stream, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t merges = units * s.heads_per_group;
@@ -1453,13 +1489,14 @@ DecodePlan plan_decode(int32_t num_heads, int32_t num_kv_heads, int32_t head_siz
     if (plan.mfma) {
         plan.head_groups = 1;
         plan.heads_per_group = group;
-        plan.padded_group = kMfmaMaxHeads;
+        plan.padded_group = group > 16 ? 32 : 16;
         tile = kMfmaTile;
+        const bool two = group > 16;
         switch (dtype) {
-            case 1: waves = mfma_waves<bf16_t>(); break;
-            case 2: waves = mfma_waves<f16_t>(); break;
-            case 3: waves = mfma_waves<bf16_c8_t>(); break;
-            default: waves = mfma_waves<f16_c8_t>(); break;
+            case 1: waves = two ? mfma_waves<bf16_t, 2>() : mfma_waves<bf16_t, 1>(); break;
+            case 2: waves = two ? mfma_waves<f16_t, 2>() : mfma_waves<f16_t, 1>(); break;
+            case 3: waves = two ? mfma_waves<bf16_c8_t, 2>() : mfma_waves<bf16_c8_t, 1>(); break;
+            default: waves = two ? mfma_waves<f16_c8_t, 2>() : mfma_waves<f16_c8_t, 1>(); break;
         }
     } else {
         dispatch_type_size(dtype, head_size, [&](auto t, auto d) {
@@ -1501,11 +1538,12 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, int dtyp
                        int64_t(p.num_seqs) * ((int64_t(p.max_seq_len) + s.tile - 1) / s.tile + 1) < (int64_t(1) << 30)
                    ? 1 : 0;
     if (plan.mfma) {
+        const bool two = s.heads_per_group > 16;
         switch (dtype) {
-            case 1: return launch_mfma<bf16_t>(p, s, stream);
-            case 2: return launch_mfma<f16_t>(p, s, stream);
-            case 3: return launch_mfma<bf16_c8_t>(p, s, stream);
-            default: return launch_mfma<f16_c8_t>(p, s, stream);
+            case 1: return two ? launch_mfma<bf16_t, 2>(p, s, stream) : launch_mfma<bf16_t, 1>(p, s, stream);
+            case 2: return two ? launch_mfma<f16_t, 2>(p, s, stream) : launch_mfma<f16_t, 1>(p, s, stream);
+            case 3: return two ? launch_mfma<bf16_c8_t, 2>(p, s, stream) : launch_mfma<bf16_c8_t, 1>(p, s, stream);
+            default: return two ? launch_mfma<f16_c8_t, 2>(p, s, stream) : launch_mfma<f16_c8_t, 1>(p, s, stream);
         }
     }
     return dispatch_type_size(dtype, head_size, [&](auto t, auto d) {

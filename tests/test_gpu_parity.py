@@ -206,6 +206,10 @@ DECODE_LAYERS = [
     # fp8 cache with 5 or more query heads per KV head at head size 128: the MFMA decode kernel
     _layer(64, 8, 128, 16, wl.F16, fp8=True, alibi=True, window=300),
     _layer(40, 8, 128, 32, fp8=True, softcap=5.0, scale=0.3, sinks=True),
+    # 17 to 32 query heads per KV head (two blocks of MFMA columns in the MFMA decode kernel)
+    _layer(32, 1, 128, 16, alibi=True),
+    _layer(24, 1, 128, 32, wl.F16, sinks=True, softcap=4.0, scale=0.25),
+    _layer(32, 1, 128, 16, fp8=True, window=500),
     # head size 256
     _layer(16, 8, 256, 16),
     _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
@@ -355,7 +359,7 @@ def test_multi_token_decode_as_chunked_prefill(k, layer):
 
 # (query_len, layer, number of extra sequences).  Query rows times query heads per KV head ("virtual
 # heads") decide the kernel: up to 8 the VALU decode kernel (from 5 the MFMA decode kernel for an
-# fp8 cache), 9 to 16 at head size 128 the MFMA decode kernel, more (16-bit layers) the MFMA
+# fp8 cache), 9 to 32 at head size 128 the MFMA decode kernel, more (16-bit layers) the MFMA
 # prefill kernel with every key from the cache; fp32 layers always the VALU decode kernel.
 MULTI_CASES = [
     (2, _layer(32, 8, 128, 16), 0),                               # 8 virtual heads: VALU decode
@@ -368,9 +372,11 @@ MULTI_CASES = [
     (4, _layer(16, 2, 64, 8, wl.F16, sinks=True, softcap=3.0, scale=0.3), 0),   # 32: prefill kernel
     (2, _layer(8, 8, 64, 16, wl.F32, alibi=True, window=40), 0),  # fp32: decode kernels
     (8, _layer(8, 1, 128, 16, alibi=True), 0),                    # 64: prefill kernel
+    (8, _layer(32, 8, 128, 16, alibi=True, window=700), 0),       # 32: MFMA decode, two column blocks
+    (5, _layer(32, 8, 128, 32, fp8=True, sinks=True), 0),         # 20, fp8 cache: MFMA decode, two column blocks
     (4, _layer(16, 4, 256, 16, alibi=True, window=300), 0),       # head size 256: prefill kernel
     (3, _layer(32, 8, 128, 16, window=1000), 64),                 # 12, 80 sequences: MFMA decode
-    (6, _layer(32, 8, 128, 16, window=1000), 64),                 # 24, 80 sequences (no compact grid): prefill kernel
+    (12, _layer(32, 8, 128, 16, window=1000), 64),                # 48, 80 sequences (no compact grid): prefill kernel
 ]
 
 
