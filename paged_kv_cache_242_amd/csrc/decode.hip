@@ -505,6 +505,9 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
         const int hgrp = u_in - gu * shape.head_groups;
         const int g = gu * KVH + hk;                       // this lane's KV head
         const int v0 = hgrp * nh;                          // first virtual head of the unit
+        // virtual heads of the unit that exist: the last group of a split is short when the
+        // virtual heads per KV head (group * qlen) are not a multiple of heads_per_group
+        const int nreal = min(nh, group * p.qlen - v0);
         // query row (sequence row seq * qlen + t) and query head of virtual head v0 + h
         auto vrow = [&](int h) -> int64_t { return int64_t(seq) * p.qlen + (v0 + h) / group; };
         auto vhead = [&](int h) -> int { return g * group + (v0 + h) % group; };
@@ -517,15 +520,15 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             for (int s = 0; s < GP; ++s) {
                 const int hs = s ^ my_head;
                 uint4 v = make_uint4(0, 0, 0, 0);
-                if (hs < nh)
+                if (hs < nreal)
                     v = *reinterpret_cast<const uint4 *>(qbase + vrow(hs) * p.q_stride + int64_t(vhead(hs)) * D);
                 q[s][0] = v.x; q[s][1] = v.y; q[s][2] = v.z; q[s][3] = v.w;
             }
         }
-        const float slope2 = (has_alibi && my_head < nh) ? p.alibi_slopes[vhead(my_head)] * kLog2e : 0.f;
+        const float slope2 = (has_alibi && my_head < nreal) ? p.alibi_slopes[vhead(my_head)] * kLog2e : 0.f;
         // positions: this lane's score head (row t) sits at L - qlen + t; the unit's rows span
         // pos_min .. L - 1, and the window start of the last row is lo_max
-        const int pos = L - p.qlen + (my_head < nh ? (v0 + my_head) / group : 0);
+        const int pos = L - p.qlen + (my_head < nreal ? (v0 + my_head) / group : 0);
         const int pos_min = L - p.qlen;
         const int lo_lane = p.window > 0 ? max(0, pos - p.window + 1) : 0;
         const int lo_max = p.window > 0 ? max(0, L - p.window) : 0;
@@ -741,7 +744,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             for (int h = 0; h < GP; ++h) {
                 float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
                 const float mh = __shfl(m_all, r * C + lane_of_head<C, GP>(h), 64);
-                if (tr == 0 && h < nh) {
+                if (tr == 0 && h < nreal) {
                     T *out_row = reinterpret_cast<T *>(p.out) + (vrow(h) * p.num_heads + vhead(h)) * D;
                     // a sink logit joins the denominator only
                     if (p.sinks) lh += fast_exp2(p.sinks[vhead(h)] * kLog2e - mh);
@@ -756,7 +759,7 @@ void decode_split_kernel(DecodeParams p, DecodeShape shape) {
             for (int h = 0; h < GP; ++h) {
                 const float lh = __shfl(l_sum, r * C + lane_of_head<C, GP>(h), 64);
                 const float mh = __shfl(m_all, r * C + lane_of_head<C, GP>(h), 64);
-                if (tr == 0 && h < nh) {
+                if (tr == 0 && h < nreal) {
                     const int64_t slot = slot0 + h;
                     float4 *dst = reinterpret_cast<float4 *>(p.ws_acc + slot * D + c * EPL);
 #pragma unroll
@@ -1225,6 +1228,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     const int g = gu * shape.kvh + hh / nh;
     const int group = p.num_heads / p.num_kv_heads;
     const int v = hgrp * nh + hh % nh;                     // virtual head: query row v / G, head v % G
+    if (v >= group * p.qlen) return;                       // past the last virtual head (a short last group)
     const int head = g * group + v % group;
     T *out_row = reinterpret_cast<T *>(p.out) + ((int64_t(seq) * p.qlen + v / group) * p.num_heads + head) * D;
     int L, lo;

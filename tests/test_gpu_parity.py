@@ -210,6 +210,11 @@ DECODE_LAYERS = [
     _layer(32, 1, 128, 16, alibi=True),
     _layer(24, 1, 128, 32, wl.F16, sinks=True, softcap=4.0, scale=0.25),
     _layer(32, 1, 128, 16, fp8=True, window=500),
+    # query heads per KV head that do not split evenly into groups of at most 8 (the VALU kernel's
+    # last group is short): 9 at head size 64, 11 with block size 8, 9 in fp32
+    _layer(18, 2, 64, 16),
+    _layer(11, 1, 128, 8, alibi=True),
+    _layer(9, 1, 64, 16, wl.F32),
     # head size 256
     _layer(16, 8, 256, 16),
     _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
@@ -371,6 +376,7 @@ MULTI_CASES = [
     (2, _layer(32, 8, 128, 16, fp8=True, alibi=True, window=500), 0),   # 8, fp8 cache: MFMA decode
     (4, _layer(16, 2, 64, 8, wl.F16, sinks=True, softcap=3.0, scale=0.3), 0),   # 32: prefill kernel
     (2, _layer(8, 8, 64, 16, wl.F32, alibi=True, window=40), 0),  # fp32: decode kernels
+    (3, _layer(6, 2, 64, 16, wl.F32), 0),                         # 9 in fp32: VALU decode, groups of 5 and 4
     (8, _layer(8, 1, 128, 16, alibi=True), 0),                    # 64: prefill kernel
     (8, _layer(32, 8, 128, 16, alibi=True, window=700), 0),       # 32: MFMA decode, two column blocks
     (5, _layer(32, 8, 128, 32, fp8=True, sinks=True), 0),         # 20, fp8 cache: MFMA decode, two column blocks
