@@ -215,6 +215,7 @@ DECODE_LAYERS = [
     _layer(18, 2, 64, 16),
     _layer(11, 1, 128, 8, alibi=True),
     _layer(9, 1, 64, 16, wl.F32),
+    _layer(14, 2, 64, 16, alibi=True, window=200),      # 7 heads per KV head: a padded group of 8
     # head size 256
     _layer(16, 8, 256, 16),
     _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
@@ -292,6 +293,9 @@ PREFILL_LAYERS = [
     _layer(4, 4, 128, 32, alibi=True, window=700),
     _layer(16, 2, 128, 64),                             # 8 heads per KV head: two workgroups of 4 heads
     _layer(8, 8, 128, 256, alibi=True, window=300),     # 256-token blocks
+    _layer(24, 4, 128, 16, alibi=True, window=150),     # 6 heads per KV head: workgroups of 2 heads
+    _layer(20, 4, 64, 16),                              # 5 heads per KV head: workgroups of 1 head
+    _layer(48, 4, 128, 32, wl.F16, sinks=True),         # 12 heads per KV head: three workgroups of 4 heads
     # logits soft-cap and sink logits
     _layer(32, 8, 128, 16, scale=0.3, softcap=5.0, sinks=True),
     _layer(32, 32, 128, 16, alibi=True, window=100, softcap=4.0, scale=0.25),
