@@ -35,8 +35,9 @@ def flags() -> list:
             "-I", os.path.join(ROOT, "include")]
 
 
-# Per-source extras.  The prefill kernel never produces NaN from finite inputs and has no NaN
-# tests; without NaN semantics fmax needs no operand canonicalisation (fewer VALU per score).
+# Per-source extras.  Without NaN semantics fmax needs no operand canonicalisation (fewer VALU per
+# score in the prefill kernel).  NaN in the inputs still propagates: a GPU test puts a NaN in one
+# visible cached K or V row and checks that exactly the output rows that see it come out NaN.
 EXTRA_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
 
 
