@@ -271,6 +271,15 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         else return bf16_hi(w);
     };
 
+    // FP8 cache: cached K rows sit in the tile as exact code values (k_scale not applied).  With
+    // cached keys (a context), the pre-scaled Q also carries k_scale, so halves of cached keys need
+    // nothing more; a half holding new rows scales their products by 1 / k_scale (C8_CTX below).
+    // Under a soft-cap the factor goes into the cap's input scale per key instead.
+    constexpr bool C8 = kFp8Cache<T>;
+    const bool c8_ctx = C8 && si.c > 0;
+    const float q_scale = c8_ctx ? qk_scale * p.k_scale : qk_scale;
+    const float inv_ks = C8 ? 1.f / p.k_scale : 1.f;
+
     // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qbk + l16), d = 32 dc + 8 lg .. +7.
     V8 qf[2][DC];
 #pragma unroll
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             if constexpr (PRE) {
                 uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) ww[k] = pack_x2<T>(elt_lo(ww[k]) * qk_scale, elt_hi(ww[k]) * qk_scale);
+                for (int k = 0; k < 4; ++k) ww[k] = pack_x2<T>(elt_lo(ww[k]) * q_scale, elt_hi(ww[k]) * q_scale);
                 w = make_uint4(ww[0], ww[1], ww[2], ww[3]);
             } else {
                 w.x = (w.x ^ qxor) & qand;
@@ -383,7 +392,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // + 15) for K and for V when the tile's copies are issued, and a tile later, when they have
     // long arrived, turns them into code * scale in the element type and writes them into the
     // same swizzled places the copies would have filled.  New-token rows still use the copies.
-    constexpr bool C8 = kFp8Cache<T>;
+    // Rows past key_hi (the last key any row of the workgroup sees) stand in for the row key_hi in
+    // the copies; when that row is cached (always so in the uniform multi-token mode, where every
+    // key is cached) no copy fills them, so their codes are zeros here: masked keys then meet
+    // zero V rows, never unwritten LDS.
     constexpr int NS8 = C8 ? D / 64 : 1;    // slots per lane per operand and tile
     constexpr int SPR8 = D / 16;            // slots per row
     uint4 raw8[2][NS8];
@@ -397,7 +409,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         for (int j = 0; j < NS8; ++j) {
             const int sl = lane + 64 * j, r = sl / SPR8, m = sl % SPR8;
             const int key = w0 + r;
-            if (key < si.c) {
+            if (key > key_hi) {
+                if (key_hi < si.c) {
+                    raw8[0][j] = make_uint4(0u, 0u, 0u, 0u);
+                    raw8[1][j] = make_uint4(0u, 0u, 0u, 0u);
+                    raw8_mask |= 1u << j;
+                }
+            } else if (key < si.c) {
                 const int64_t blk = clamp_block(((key >> p.block_shift) == (w0 >> p.block_shift)) ? id0 : id1);
                 const int64_t off = blk * block8 + int64_t(key & bmask) * row8 + int64_t(g) * D + 16 * m;
                 raw8[0][j] = *reinterpret_cast<const uint4 *>(kc_bytes + off);
@@ -415,7 +433,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                     const int rr = wrow0 + r;
 #pragma unroll
                     for (int o = 0; o < 2; ++o) {
-                        const float sc = o ? p.v_scale : p.k_scale;
+                        // K codes exactly (every E4M3 value is a 16-bit value), V as code * v_scale
+                        // rounded to the element type
+                        const float sc = o ? p.v_scale : 1.f;
                         const uint32_t cw[4] = {raw8[o][j].x, raw8[o][j].y, raw8[o][j].z, raw8[o][j].w};
                         uint32_t w[8];
 #pragma unroll
@@ -454,7 +474,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     auto copy_tile = [&](int kt, int id0_raw, int id1_raw, bf16_t *kdst, bf16_t *vdst) __attribute__((always_inline)) {
         const int w0 = kt * kBN + wrow0;                  // first key of this wavefront (uniform)
         if constexpr (C8) {
-            if (w0 < si.c) fp8_issue(kt, id0_raw, id1_raw);
+            if (w0 < si.c || key_hi < si.c) fp8_issue(kt, id0_raw, id1_raw);
             if (w0 + 15 < si.c) return;                   // all cached: nothing for the copies
         }
         if (!C8 && w0 + 15 < si.c) {
@@ -671,13 +691,16 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
         floatx4_v s[2][2];
+        // an FP8 cache with a context: this half holds new rows, whose products Q's k_scale must
+        // leave (PRE; the starting values are then added after the MFMAs)
+        const bool knew = PRE && c8_ctx && k0h + 31 >= si.c;
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) {
             // PRE: the scores come out as base-2 logits minus the finite stand-in of the running max
-            const float c0 = PRE ? crow[qbk] - m_fin[qbk] : 0.f;
+            const float c0 = PRE && !knew ? crow[qbk] - m_fin[qbk] : 0.f;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                if constexpr (KBIAS_INIT)
+                if (KBIAS_INIT && !knew)
                     s[kk][qbk] = floatx4_v{c0 + kbias[kk][0], c0 + kbias[kk][1], c0 + kbias[kk][2], c0 + kbias[kk][3]};
                 else
                     s[kk][qbk] = floatx4_v{c0, c0, c0, c0};
@@ -697,14 +720,31 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         }
         __builtin_amdgcn_s_setprio(0);
         load_v(vs, kc);
+        if constexpr (C8 && PRE) {
+            if (knew) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = k0h + 16 * kk + 4 * lg + i < si.c ? 1.f : inv_ks;
+#pragma unroll
+                        for (int qbk = 0; qbk < 2; ++qbk)
+                            s[kk][qbk][i] = fmaf(s[kk][qbk][i], f,
+                                                 crow[qbk] - m_fin[qbk] + (KBIAS_INIT ? kbias[kk][i] : 0.f));
+                    }
+            }
+        }
         if constexpr (SOFTCAP) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int qbk = 0; qbk < 2; ++qbk)
+                for (int i = 0; i < 4; ++i) {
+                    // FP8 cache: cached keys' raw products carry the codes, so their cap input takes k_scale
+                    const float cin = C8 && k0h + 16 * kk + 4 * lg + i < si.c ? cap_in * p.k_scale : cap_in;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cap_in), kbias[kk][i]);
+                    for (int qbk = 0; qbk < 2; ++qbk)
+                        s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cin), kbias[kk][i]);
+                }
         }
 
         // ---- mask (partial halves): key k0h + 16 kk + 4 lg + i is visible from row pos iff
