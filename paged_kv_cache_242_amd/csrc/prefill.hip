@@ -245,40 +245,37 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     }
 
     const float qk_scale = p.scale * kLog2e;
-    // Without a soft-cap (PRE) Q is multiplied by scale log2(e) once, here, and rounded to the
-    // element type, so the score MFMAs produce base-2 logits directly; their accumulators start at
-    // the row's ALiBi term minus the running max, so a score leaves the MFMA ready for the
-    // exponent.  With a soft-cap the raw dot product must reach tanh, so Q keeps its values (a
-    // negative scale as a sign flip, exact; a zero scale as Q = 0).
+    // Without a soft-cap (PRE) the score MFMAs take Q as it is and one fp32 FMA per score turns the
+    // result into the base-2 logit relative to the running max: s = m (dot + b_key / m) + (c_row -
+    // m_fin), with m = scale log2(e), b_key the key's ALiBi offset from the half's first key times
+    // slope log2(e) (b_key / m, a per-lane constant, is where the accumulators start), c_row the
+    // row's ALiBi term and m_fin the finite stand-in of the running max (both per row).  An FP8
+    // cache has two multipliers (cached keys carry k_scale); there the accumulators start at zero
+    // and b_key joins the FMA's addend instead, which keeps one set of per-lane constants.
+    // (Pre-scaling Q in the element type instead saves the FMA but rounds scale * q to 8 bits, which
+    // doubled the bf16 error at 2.5 times the default scale.)  With start values a zero scale
+    // zeroes Q and takes m = 1.  With a soft-cap the raw dot product must reach tanh, so Q keeps
+    // its values there too (a negative scale as a sign flip, exact; a zero scale as Q = 0).
     constexpr bool PRE = !SOFTCAP;
-    const uint32_t qxor = qk_scale < 0.f ? 0x80008000u : 0u;       // sign flips of both halves
-    const uint32_t qand = qk_scale == 0.f ? 0u : 0xffffffffu;
+    constexpr bool C8 = kFp8Cache<T>;
+    constexpr bool KB_INIT = PRE && ALIBI && !C8;         // ALiBi start values in the accumulators
+    const uint32_t qxor = !PRE && qk_scale < 0.f ? 0x80008000u : 0u;      // sign flips of both halves
+    const uint32_t qand = (!PRE || KB_INIT) && qk_scale == 0.f ? 0u : 0xffffffffu;
     // The ALiBi key term (the key's offset from the half's first key times slope log2(e)) joins the
-    // score accumulators' starting values when Q is pre-scaled; with a soft-cap it must stay outside
-    // the cap, so there it is added in fp32 after the cap.
-    constexpr bool KBIAS_INIT = ALIBI && PRE;
-    constexpr bool KBIAS_F32 = ALIBI && !PRE;
+    // accumulators' start values or the FMA's addend; with a soft-cap it must stay outside the cap,
+    // so there it is added after the cap.
+    constexpr bool KBIAS = ALIBI;
     // multiplier of the soft-capped scores in the exponent (they are base-2 logits already)
     const float s_mul = 1.f;
     const float cap_in = SOFTCAP ? fabsf(p.scale) / p.softcap : 0.f;
     const float cap2 = SOFTCAP ? p.softcap * kLog2e : 0.f;
-    auto elt_lo = [](uint32_t w) -> float {
-        if constexpr (kIsF16<T>) return f16_to_f32(f16_t(uint16_t(w & 0xffffu)));
-        else return bf16_lo(w);
-    };
-    auto elt_hi = [](uint32_t w) -> float {
-        if constexpr (kIsF16<T>) return f16_to_f32(f16_t(uint16_t(w >> 16)));
-        else return bf16_hi(w);
-    };
 
-    // FP8 cache: cached K rows sit in the tile as exact code values (k_scale not applied).  With
-    // cached keys (a context), the pre-scaled Q also carries k_scale, so halves of cached keys need
-    // nothing more; a half holding new rows scales their products by 1 / k_scale (C8_CTX below).
-    // Under a soft-cap the factor goes into the cap's input scale per key instead.
-    constexpr bool C8 = kFp8Cache<T>;
-    const bool c8_ctx = C8 && si.c > 0;
-    const float q_scale = c8_ctx ? qk_scale * p.k_scale : qk_scale;
-    const float inv_ks = C8 ? 1.f / p.k_scale : 1.f;
+    // FP8 cache: cached K rows sit in the tile as exact code values (k_scale not applied); the
+    // score FMA (or the soft-cap's input scale) of a cached key multiplies by k_scale as well.
+    const float qk_scale_c = C8 ? qk_scale * p.k_scale : qk_scale;     // cached keys
+    // PRE multipliers of new and cached keys (with start values and a zero scale, 1: Q is zero)
+    const float mul_n = KB_INIT && qk_scale == 0.f ? 1.f : qk_scale;
+    const float mul_c = qk_scale_c;
 
     // Q as the B operand of S^T = K Q^T: lane holds row (t0 + 16 qbk + l16), d = 32 dc + 8 lg .. +7.
     V8 qf[2][DC];
@@ -290,12 +287,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
             uint4 w = *reinterpret_cast<const uint4 *>(qrow + 32 * dc);
-            if constexpr (PRE) {
-                uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) ww[k] = pack_x2<T>(elt_lo(ww[k]) * q_scale, elt_hi(ww[k]) * q_scale);
-                w = make_uint4(ww[0], ww[1], ww[2], ww[3]);
-            } else {
+            {
                 w.x = (w.x ^ qxor) & qand;
                 w.y = (w.y ^ qxor) & qand;
                 w.z = (w.z ^ qxor) & qand;
@@ -316,11 +308,21 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     float slope2 = 0.f;
     if constexpr (ALIBI) slope2 = p.alibi_slopes[h] * kLog2e;
     float kbias[2][4] = {};
-    if constexpr (KBIAS_F32 || KBIAS_INIT) {
+    if constexpr (KBIAS) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) kbias[kk][i] = slope2 * float(16 * kk + 4 * lg + i);
+    }
+    // PRE with ALiBi over a 16-bit cache: the score accumulators' starting values b_key / m
+    floatx4_v kb_n[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        kb_n[kk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+        if constexpr (KB_INIT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kb_n[kk][i] = kbias[kk][i] / mul_n;
+        }
     }
 
     // ---- copies
@@ -691,21 +693,10 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
         for (int qbk = 0; qbk < 2; ++qbk) crow[qbk] = ALIBI ? slope2 * float(k0h - (p0 + 16 * qbk + l16)) : 0.f;
         floatx4_v s[2][2];
-        // an FP8 cache with a context: this half holds new rows, whose products Q's k_scale must
-        // leave (PRE; the starting values are then added after the MFMAs)
-        const bool knew = PRE && c8_ctx && k0h + 31 >= si.c;
 #pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-            // PRE: the scores come out as base-2 logits minus the finite stand-in of the running max
-            const float c0 = PRE && !knew ? crow[qbk] - m_fin[qbk] : 0.f;
+        for (int qbk = 0; qbk < 2; ++qbk)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (KBIAS_INIT && !knew)
-                    s[kk][qbk] = floatx4_v{c0 + kbias[kk][0], c0 + kbias[kk][1], c0 + kbias[kk][2], c0 + kbias[kk][3]};
-                else
-                    s[kk][qbk] = floatx4_v{c0, c0, c0, c0};
-            }
-        }
+            for (int kk = 0; kk < 2; ++kk) s[kk][qbk] = kb_n[kk];
         // Raised wave priority while the score MFMAs issue: when both wavefronts of a SIMD want the
         // matrix unit, this one goes first and the other turns to its exponentials, so the two
         // drift into alternating phases instead of colliding.
@@ -720,17 +711,36 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         }
         __builtin_amdgcn_s_setprio(0);
         load_v(vs, kc);
-        if constexpr (C8 && PRE) {
-            if (knew) {
+        if constexpr (PRE) {
+            // s = m (dot + b_key / m) + (c_row - m_fin): the base-2 logit relative to the running
+            // max's finite stand-in (FP8 cache: s = m dot + (c_row - m_fin + b_key), m times
+            // k_scale for a cached key).  The multiplier is uniform over the half unless an FP8 half
+            // holds both cached and new keys.
+            float mul = mul_n;
+            bool mixed = false;
+            if constexpr (C8) {
+                if (k0h + 31 < si.c) mul = mul_c;
+                else mixed = k0h < si.c;
+            }
+            if (!mixed) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int qbk = 0; qbk < 2; ++qbk)
+                            s[kk][qbk][i] = fmaf(s[kk][qbk][i], mul,
+                                                 C8 && ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] : crow[qbk] - m_fin[qbk]);
+            } else {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float f = k0h + 16 * kk + 4 * lg + i < si.c ? 1.f : inv_ks;
+                        const float mk = k0h + 16 * kk + 4 * lg + i < si.c ? mul_c : mul_n;
 #pragma unroll
                         for (int qbk = 0; qbk < 2; ++qbk)
-                            s[kk][qbk][i] = fmaf(s[kk][qbk][i], f,
-                                                 crow[qbk] - m_fin[qbk] + (KBIAS_INIT ? kbias[kk][i] : 0.f));
+                            s[kk][qbk][i] = fmaf(s[kk][qbk][i], mk,
+                                                 ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] : crow[qbk] - m_fin[qbk]);
                     }
             }
         }

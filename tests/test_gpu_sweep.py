@@ -16,11 +16,12 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-CASES = 64
+CASES = 160
 
 
 def _case(seed: int):
     rng = np.random.default_rng([seed, 77])
+    wide = seed >= 64        # later cases: more sequences (past the compact prefill grid's 64) and longer ones
     G = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 16, 20, 24, 32]))
     Hkv = int(rng.choice([1, 2, 4]))
     if G * Hkv > 64:
@@ -41,10 +42,13 @@ def _case(seed: int):
                          kv_cache_dtype="fp8_e4m3" if fp8 else "auto", k_scale=wl.fp32(0.02) if fp8 else 1.0,
                          v_scale=wl.fp32(0.015) if fp8 else 1.0)
     budget = 1500 if fp8 else 4000          # tokens per batch (the oracle's fp8 write is slow)
-    n_pre = int(rng.integers(0, 4))
-    prefill = [(int(rng.integers(0, budget // 4)), int(rng.integers(1, 300))) for _ in range(n_pre)]
-    n_dec = int(rng.integers(1, 7))
-    decode = [int(x) for x in rng.integers(1, budget // 2, size=n_dec)]
+    if wide and not fp8:
+        budget = 12000
+    n_pre = int(rng.integers(0, 4)) if not wide else int(rng.choice([0, 2, 9, 70]))
+    max_sub = 300 if n_pre < 9 else 40
+    prefill = [(int(rng.integers(0, budget // max(4, n_pre))), int(rng.integers(1, max_sub))) for _ in range(n_pre)]
+    n_dec = int(rng.integers(1, 7)) if not wide else int(rng.choice([1, 5, 40]))
+    decode = [int(x) for x in rng.integers(1, max(2, budget // max(2, n_dec // 4)), size=n_dec)]
     decode[int(rng.integers(n_dec))] = 0 if n_dec > 1 else decode[0]
     k = int(rng.integers(2, 7))
     return layer, prefill, decode, k
