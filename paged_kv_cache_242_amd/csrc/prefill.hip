@@ -136,12 +136,12 @@ __device__ __forceinline__ int vswz(int r) {
 // Each wavefront copies 16 keys (rows 16 w .. 16 w + 15) of each tile, which lie in one cache
 // block (two for 8-token blocks), so one descriptor per block and tile serves all its copies.
 //
-// Scores.  A wavefront's 32 rows meet a tile in two 32-key halves.  Q is multiplied by
-// scale log2(e) and rounded to the element type once, when it is loaded, so the score MFMAs
-// produce base-2 logits; their accumulators start at c_row - m + b_key, where c_row is the row's
-// ALiBi term for the half's first key (0 without ALiBi), m the finite stand-in of the row's running
-// max and b_key the key's ALiBi offset from the half's first key times slope log2(e) (a per-lane
-// constant).  A score then leaves the MFMAs as the exponent of its weight.  A half is
+// Scores.  A wavefront's 32 rows meet a tile in two 32-key halves.  The score MFMAs take Q as it
+// is stored, and one fp32 FMA per score turns their result into the exponent of its weight:
+// scale log2(e) times the product plus c_row - m + b_key, where c_row is the row's ALiBi term for
+// the half's first key (0 without ALiBi), m the finite stand-in of the row's running max and b_key
+// the key's ALiBi offset from the half's first key times slope log2(e) (a per-lane constant, which
+// enters through the accumulators' start values or the FMA's addend).  A half is
 //   * empty for the wavefront when every (row, key) pair is masked -- skipped entirely;
 //   * full when none is -- no per-score work besides the max and the exponent;
 //   * partial otherwise -- masked scores are set to -inf.
@@ -263,10 +263,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     const uint32_t qand = (!PRE || KB_INIT) && qk_scale == 0.f ? 0u : 0xffffffffu;
     // The ALiBi key term (the key's offset from the half's first key times slope log2(e)) joins the
     // accumulators' start values or the FMA's addend; with a soft-cap it must stay outside the cap,
-    // so there it is added after the cap.
-    constexpr bool KBIAS = ALIBI;
-    // multiplier of the soft-capped scores in the exponent (they are base-2 logits already)
-    const float s_mul = 1.f;
+    // so there it is added after the cap (the capped scores are base-2 logits already).
     const float cap_in = SOFTCAP ? fabsf(p.scale) / p.softcap : 0.f;
     const float cap2 = SOFTCAP ? p.softcap * kLog2e : 0.f;
 
@@ -308,7 +305,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     float slope2 = 0.f;
     if constexpr (ALIBI) slope2 = p.alibi_slopes[h] * kLog2e;
     float kbias[2][4] = {};
-    if constexpr (KBIAS) {
+    if constexpr (ALIBI) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -792,7 +789,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             mx = fmaxf(fmaxf(mx, s[0][qbk][3]), s[1][qbk][0]);
             mx = fmaxf(fmaxf(mx, s[1][qbk][1]), s[1][qbk][2]);
             mx = fmaxf(mx, s[1][qbk][3]);
-            tmax[qbk] = PRE ? mx : fmaf(mx, s_mul, crow[qbk]);
+            tmax[qbk] = PRE ? mx : mx + crow[qbk];
         }
         const bool raise = tmax[0] > m_thr[0] || tmax[1] > m_thr[1];
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -836,7 +833,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                 float pf[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    pf[i] = fast_exp2(PRE ? s[kk][qbk][i] : fmaf(s[kk][qbk][i], s_mul, off));
+                    pf[i] = fast_exp2(PRE ? s[kk][qbk][i] : s[kk][qbk][i] + off);
                 pk[kk][0] = pack_x2<T>(pf[0], pf[1]);
                 pk[kk][1] = pack_x2<T>(pf[2], pf[3]);
             }
@@ -942,74 +939,218 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     }
 }
 
-// fp32: one wavefront per (query row, head).  Keys in 64-key tiles, lane = key for the scores,
-// lane = output element for P.V.
+// fp32: a workgroup of 4 wavefronts takes up to 128 (query row, head) pairs of one KV head --
+// 32 rows of one query head per wavefront, as in the 16-bit kernel -- and walks their keys in
+// 32-key tiles staged in LDS, so each K/V row read from memory serves every row of the workgroup.
+// Products run on the fp32 matrix unit (v_mfma_f32_16x16x4_f32): S^T = K Q^T with Q held in
+// registers, then O^T += V^T P^T with the weights kept in fp32.  Operand k-slots are permuted
+// consistently on both sides (a sum does not depend on its order): in the score MFMAs, step j of
+// d-block b gives lane group g the element d = 16 b + 4 g + j, so K and Q are read as float4; in
+// the P.V MFMAs, step v of key block kk gives lane group g the key 16 kk + 4 g + v, which is where
+// that lane's score already sits.  Softmax in base 2 with an exact running max.
+constexpr int kF32Keys = 32;        // keys per tile
+constexpr int kF32Pad = 4;          // floats of padding per LDS row (conflict-free operand reads)
+
+struct F32Grid {
+    int heads;          // query heads per workgroup (1, 2 or 4: a divisor of the group)
+    int rows;           // query rows per workgroup (128 / heads)
+    int row_blocks;     // ceil(max_subquery_len / rows)
+    int head_blocks;    // group / heads
+};
+
 template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
-    constexpr int PER = D / 64;
-    __shared__ float qs[D];
-    const int lane = threadIdx.x;
-    const int h = blockIdx.x % p.num_heads;
-    const int64_t t = blockIdx.x / p.num_heads;
-    // sequence of row t: last seq with cu[seq] <= t
-    int lo_s = 0, hi_s = p.num_seqs - 1;
-    while (lo_s < hi_s) {
-        const int mid = (lo_s + hi_s + 1) >> 1;
-        if (p.cu_subquery[mid] <= t) lo_s = mid; else hi_s = mid - 1;
-    }
-    const int seq = lo_s;
+__global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(PrefillParams p, F32Grid grid) {
+    constexpr int DB = D / 16;                              // 16-wide d blocks
+    constexpr int LD = D + kF32Pad;                         // LDS row stride (floats)
+    constexpr int CPR = D / 4;                              // float4 chunks per row
+    constexpr int KPP = kThreads / CPR;                     // key rows per copy pass
+    constexpr int PASSES = kF32Keys / KPP;
+    __shared__ __attribute__((aligned(16))) float ks[kF32Keys * LD];
+    __shared__ __attribute__((aligned(16))) float vs[kF32Keys * LD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    // block -> (row block, sequence, KV head, head block); late row blocks first (they see the most keys)
+    const int64_t per_level = int64_t(p.num_seqs) * p.num_kv_heads * grid.head_blocks;
+    const int rb = grid.row_blocks - 1 - int(blockIdx.x / per_level);
+    int64_t rem = blockIdx.x % per_level;
+    const int seq = int(rem / (int64_t(p.num_kv_heads) * grid.head_blocks));
+    rem %= int64_t(p.num_kv_heads) * grid.head_blocks;
+    const int kvh = int(rem / grid.head_blocks);
+    const int hblk = int(rem % grid.head_blocks);
     const SeqInfo si = seq_info(p, seq);
-    const int trow = int(t) - si.start;
-    if (trow < 0 || trow >= si.n) return;
-    const int g = h / (p.num_heads / p.num_kv_heads);
-    const int pos = si.c + trow;
-    const int klo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
-    const float *qrow = reinterpret_cast<const float *>(p.query) + t * p.q_stride + int64_t(h) * D;
-    for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
-    __syncthreads();
+    const int t0 = rb * grid.rows;
+    if (t0 >= si.n) return;                                 // the whole workgroup: no barrier yet
+    const int t_last = min(t0 + grid.rows, si.n) - 1;
+    const int key_hi = si.q0 + t_last;
+    const int key_lo = p.window > 0 ? max(0, si.q0 + t0 - p.window + 1) : 0;
+    const int kt_lo = key_lo / kF32Keys, kt_hi = key_hi / kF32Keys;
+
+    const int group = p.num_heads / p.num_kv_heads;
+    const int h = kvh * group + hblk * grid.heads + wave % grid.heads;
+    const int w0 = t0 + (wave / grid.heads) * 32;          // first row of this wavefront
+    const bool active = w0 < si.n;
+    const int wpos_lo = si.q0 + w0, wpos_hi = si.q0 + min(w0 + 31, si.n - 1);
+
+    // Q as the B operand: lane (l16, lg) holds row w0 + 16 qbk + l16, d = 16 b + 4 lg .. + 3
+    floatx4_v qf[2][DB];
+#pragma unroll
+    for (int qbk = 0; qbk < 2; ++qbk) {
+        const int trow = min(w0 + 16 * qbk + l16, si.n - 1);
+        const float *qrow = reinterpret_cast<const float *>(p.query) + int64_t(si.start + trow) * p.q_stride +
+                            int64_t(h) * D + 4 * lg;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const float4 v = *reinterpret_cast<const float4 *>(qrow + 16 * b);
+            qf[qbk][b] = floatx4_v{v.x, v.y, v.z, v.w};
+        }
+    }
     const bool has_cap = p.softcap > 0.f;
     const float qk_scale = has_cap ? p.scale / p.softcap : p.scale * kLog2e;
     const float cap2 = p.softcap * kLog2e;
     const float slope2 = p.alibi_slopes ? p.alibi_slopes[h] * kLog2e : 0.f;
-    float m = -INFINITY, l = 0.f, acc[PER];
+
+    // ---- copies: thread tid moves float4 chunk (tid % CPR) of key rows tid / CPR + KPP * pass.
+    // Keys past key_hi re-read row key_hi (masked for every row; a visible row, so finite).
+    float4 kr[PASSES], vr[PASSES];
+    auto fetch = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    for (int kt = klo; kt <= pos; kt += 64) {
-        const int key = kt + lane;
-        const int keyc = min(key, pos);
-        const float *kp, *vp;
-        row_ptrs<float>(p, si, seq, g, D, keyc, kp, vp);
-        float dot = 0.f;
-        for (int d = 0; d < D; d += 4) {
-            const float4 kv = *reinterpret_cast<const float4 *>(kp + d);
-            dot = fmaf(kv.x, qs[d], dot);
-            dot = fmaf(kv.y, qs[d + 1], dot);
-            dot = fmaf(kv.z, qs[d + 2], dot);
-            dot = fmaf(kv.w, qs[d + 3], dot);
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int j = min(kt * kF32Keys + tid / CPR + KPP * ps, key_hi);
+            const float *kp, *vp;
+            row_ptrs<float>(p, si, seq, kvh, D, j, kp, vp);
+            kr[ps] = *reinterpret_cast<const float4 *>(kp + 4 * (tid % CPR));
+            vr[ps] = *reinterpret_cast<const float4 *>(vp + 4 * (tid % CPR));
         }
-        const float x = dot * qk_scale;
-        const float sc = key <= pos ? (has_cap ? cap2 * tanh_fast(x) : x) + slope2 * float(key - pos) : -INFINITY;
-        const float tmax = xor_max_from<1>(sc);
-        const float m_new = fmaxf(m, tmax);
-        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
-        const float pw = (sc == -INFINITY) ? 0.f : fast_exp2(sc - m_new);
-        l = l * alpha + xor_sum_from<1>(pw);
-        m = m_new;
+    };
+    auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] *= alpha;
-        const int nk = min(64, pos - kt + 1);
-        for (int jj = 0; jj < nk; ++jj) {
-            const float pj = __shfl(pw, jj, 64);
-            const float *kq, *vq;
-            row_ptrs<float>(p, si, seq, g, D, kt + jj, kq, vq);
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int r = tid / CPR + KPP * ps;
+            *reinterpret_cast<float4 *>(ks + r * LD + 4 * (tid % CPR)) = kr[ps];
+            *reinterpret_cast<float4 *>(vs + r * LD + 4 * (tid % CPR)) = vr[ps];
+        }
+    };
+
+    floatx4_v o[2][DB];
+    float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < PER; ++k) acc[k] = fmaf(pj, vq[lane + 64 * k], acc[k]);
+    for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[qbk][b] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int kt) __attribute__((always_inline)) {
+        const int k0 = kt * kF32Keys;
+        // tiles no row of this wavefront sees
+        if (!active || k0 > wpos_hi || (p.window > 0 && k0 + kF32Keys - 1 <= wpos_lo - p.window)) return;
+        // ---- S^T = K Q^T: s[kk][qbk] holds keys k0 + 16 kk + 4 lg + v of row 16 qbk + l16
+        floatx4_v s[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk) s[kk][qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float4 kv = *reinterpret_cast<const float4 *>(ks + (16 * kk + l16) * LD + 16 * b + 4 * lg);
+                const float ka[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int qbk = 0; qbk < 2; ++qbk)
+                        s[kk][qbk] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[j], qf[qbk][b][j], s[kk][qbk], 0, 0, 0);
+            }
+        }
+        // ---- scale (or soft-cap), ALiBi, mask; the running max and the weights
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+            const int pos = si.q0 + w0 + 16 * qbk + l16;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int key = k0 + 16 * kk + 4 * lg + v;
+                    float x = s[kk][qbk][v] * qk_scale;
+                    if (has_cap) x = cap2 * tanh_fast(x);
+                    x += slope2 * float(key - pos);
+                    const bool vis = key <= pos && (p.window <= 0 || key > pos - p.window);
+                    x = vis ? x : -INFINITY;
+                    s[kk][qbk][v] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = max_xor32(max_xor16(mx));
+            const float m_new = fmaxf(m_run[qbk], mx);
+            const float alpha = m_run[qbk] == -INFINITY ? 0.f : fast_exp2(m_run[qbk] - m_new);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            float ls = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float w = fast_exp2(s[kk][qbk][v] - m_use);
+                    s[kk][qbk][v] = w;
+                    ls += w;
+                }
+            l_part[qbk] = fmaf(l_part[qbk], alpha, ls);
+            m_run[qbk] = m_new;
+#pragma unroll
+            for (int b = 0; b < DB; ++b) o[qbk][b] *= alpha;
+        }
+        // ---- O^T += V^T P^T: step v of key block kk gives lane group lg the key 16 kk + 4 lg + v
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // (at head size 256 the V reads are held back to one key ahead: registers)
+                if constexpr (D > 128) __builtin_amdgcn_sched_barrier(0);
+                const float *vrow = vs + (16 * kk + 4 * lg + v) * LD + l16;
+#pragma unroll
+                for (int b = 0; b < DB; ++b) {
+                    const float a = vrow[16 * b];
+#pragma unroll
+                    for (int qbk = 0; qbk < 2; ++qbk)
+                        o[qbk][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[kk][qbk][v], o[qbk][b], 0, 0, 0);
+                }
+            }
+    };
+
+    // ---- pipeline: tile kt is computed from LDS while tile kt - 1 is fetched into registers (up
+    // to head size 128; at 256 the registers are taken and the fetch follows the compute)
+    constexpr bool PREFETCH = D <= 128;
+    fetch(kt_hi);
+    commit();
+    __syncthreads();
+    for (int kt = kt_hi; kt >= kt_lo; --kt) {
+        if (PREFETCH && kt > kt_lo) fetch(kt - 1);
+        compute(kt);
+        __syncthreads();
+        if (kt > kt_lo) {
+            if (!PREFETCH) fetch(kt - 1);
+            commit();
+            __syncthreads();
         }
     }
-    if (p.sinks) l += fast_exp2(p.sinks[h] * kLog2e - m);
-    float *orow = reinterpret_cast<float *>(p.out) + t * p.num_heads * D + int64_t(h) * D;
+
+    // ---- epilogue: lane (l16, lg) holds O^T[d = 16 b + 4 lg + v][row 16 qbk + l16]
+    if (!active) return;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) orow[lane + 64 * k] = acc[k] / l;
+    for (int qbk = 0; qbk < 2; ++qbk) {
+        const int trow = w0 + 16 * qbk + l16;
+        float l = xor_sum_from<16>(l_part[qbk]);
+        if (p.sinks) l += fast_exp2(p.sinks[h] * kLog2e - m_run[qbk]);
+        if (trow < si.n) {
+            const float inv = 1.f / l;
+            float *orow = reinterpret_cast<float *>(p.out) + int64_t(si.start + trow) * p.num_heads * D +
+                          int64_t(h) * D + 4 * lg;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+                *reinterpret_cast<float4 *>(orow + 16 * b) =
+                    make_float4(o[qbk][b][0] * inv, o[qbk][b][1] * inv, o[qbk][b][2] * inv, o[qbk][b][3] * inv);
+        }
+    }
 }
 
 template <typename T>
@@ -1072,15 +1213,22 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, hipS
     if (dtype == 3) return launch_mfma<bf16_c8_t>(p, head_size, stream);
     if (dtype == 4) return launch_mfma<f16_c8_t>(p, head_size, stream);
     if (p.uniform_qlen > 0) return hipErrorInvalidValue;      // the uniform mode has 16-bit kernels only
-    const int64_t blocks = p.num_tokens * p.num_heads;
-    if (blocks == 0) return hipSuccess;
+    F32Grid grid;
+    const int group = p.num_heads / p.num_kv_heads;
+    grid.heads = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+    grid.rows = kRowsPerBlock / grid.heads;
+    grid.row_blocks = (p.max_subquery_len + grid.rows - 1) / grid.rows;
+    grid.head_blocks = group / grid.heads;
+    const int64_t blocks = int64_t(grid.row_blocks) * p.num_seqs * p.num_kv_heads * grid.head_blocks;
+    if (blocks == 0 || p.num_tokens == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 nb = dim3(unsigned(blocks)), nt = dim3(kThreads);
     if (head_size == 256)
-        hipLaunchKernelGGL(prefill_f32_kernel<256>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+        hipLaunchKernelGGL(prefill_f32_kernel<256>, nb, nt, 0, stream, p, grid);
     else if (head_size == 128)
-        hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+        hipLaunchKernelGGL(prefill_f32_kernel<128>, nb, nt, 0, stream, p, grid);
     else if (head_size == 64)
-        hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+        hipLaunchKernelGGL(prefill_f32_kernel<64>, nb, nt, 0, stream, p, grid);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
