@@ -319,6 +319,11 @@ PREFILL_LAYERS = [
     _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
     _layer(16, 4, 256, 32, fp8=True, softcap=30.0, scale=0.15, sinks=True),
     _layer(4, 2, 256, 16, wl.F32, alibi=True),
+    # fp32 workgroup shapes: 1, 2 and 4 query heads per workgroup, several head blocks per KV head
+    _layer(12, 4, 64, 16, wl.F32, window=90),           # 3 heads per KV head: workgroups of 1 head, 128 rows
+    _layer(16, 4, 128, 32, wl.F32, sinks=True),         # 4 heads per KV head: 32 rows per workgroup
+    _layer(16, 2, 64, 8, wl.F32, alibi=True, softcap=3.0),  # 8 heads per KV head: two workgroups of 4 heads
+    _layer(12, 2, 256, 16, wl.F32, window=200),         # 6 heads per KV head: three workgroups of 2 heads
 ]
 PREFILL_SEQS = [(0, 1), (0, 5), (0, 128), (0, 129), (1, 64), (15, 127), (16, 130), (17, 300), (200, 33),
                 (1000, 257), (63, 1), (64, 64), (0, 0)]
