@@ -246,8 +246,9 @@ def swap_blocks(src_cache: torch.Tensor, dst_cache: torch.Tensor, block_pairs, l
                                dst_cache.shape[1], pairs.data_ptr(), pairs.shape[0], _stream(dev)))
 
 
-def decode_workspace_size(layer: Layer, num_seqs: int, max_seq_len: int, query_len: int = 1) -> int:
-    c = layer._c()
+def decode_workspace_size(layer: Layer, num_seqs: int, max_seq_len: int, query_len: int = 1,
+                          _clayer: Optional[_CLayer] = None) -> int:
+    c = _clayer if _clayer is not None else layer._c()
     if query_len == 1:
         return int(_lib.pa_decode_workspace_size(ctypes.byref(c), num_seqs, max_seq_len))
     return int(_lib.pa_decode_multi_workspace_size(ctypes.byref(c), num_seqs, query_len, max_seq_len))
@@ -273,11 +274,13 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tens
     elif tuple(out.shape) != (rows, width) or not out.is_contiguous() or out.dtype != layer.dtype:
         raise PaError(PA_ERR_INVALID_ARGUMENT, "out must be a contiguous [rows, H*D] tensor of the layer dtype")
     c = layer._c()
-    need = decode_workspace_size(layer, B, max_seq_len, query_len) if B > 0 else 0
     ws_ptr, ws_bytes = None, 0
-    if need > 0:
-        if workspace is None:
+    if workspace is None:
+        # (a workspace passed in is checked against the need by the library itself)
+        need = decode_workspace_size(layer, B, max_seq_len, query_len, c) if B > 0 else 0
+        if need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if query_len == 1:
         _check(_lib.pa_decode(ctypes.byref(c), out.data_ptr(), query.data_ptr(), qs, _cache(kv_cache, layer), bt,
