@@ -246,7 +246,10 @@ pa_status pa_decode_multi(const pa_layer *layer, void *out, const void *query, i
  *                    (e.g. lengths [4, 6] give [0, 4, 10]); cu_subquery[num_seqs] == num_tokens
  *   max_subquery_len host upper bound of the subquery lengths (sizes the grid)
  *   max_context_len  host upper bound of context_lens (0 when there is no context)
- * All device pointers 16-byte aligned, row strides multiples of 8 elements.
+ * All device pointers 16-byte aligned, row strides multiples of 16 bytes.
+ * Workgroups of 4 wavefronts take up to 128 (query row, head) pairs of one KV head and stage
+ * K/V tiles in LDS; the products run on the matrix unit (bf16 / fp16 MFMAs, fp32 MFMAs for
+ * fp32 layers) with the softmax online in fp32.
  */
 pa_status pa_prefill_varlen(const pa_layer *layer, void *out, const void *query, int64_t q_row_stride,
                             const void *key, const void *value, int64_t kv_row_stride, const void *kv_cache,
