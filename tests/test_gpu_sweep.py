@@ -85,3 +85,33 @@ def test_random_layer_sweep(seed):
     torch.cuda.synchronize()
     ref = oracle.decode_multi(gh.olayer(batch.layer), wl.host_bits(q), pool, batch.decode_block_tables, lens, k)
     gh.assert_close(gh.to_f64(out), ref, batch.layer, f"case {seed} multi-token decode k={k}")
+
+
+# Head size 256 over an fp8 cache with ALiBi: the most register-bound prefill instantiations (one
+# wavefront per SIMD, codes held one tile ahead), with and without soft-caps, windows and fp16.
+HEAD256_CASES = 48
+
+
+@pytest.mark.parametrize("seed", range(HEAD256_CASES))
+def test_head256_fp8_alibi_prefill(seed):
+    rng = np.random.default_rng([seed, 256])
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    Hkv = int(rng.choice([1, 2]))
+    bs = int(rng.choice([8, 16, 32]))
+    cap = float(rng.choice([0.0, 5.0, 30.0]))
+    window = int(rng.integers(1, 500)) if rng.random() < 0.3 else 0
+    scale = (1.0 / 16.0) * float(rng.choice([1.0, 2.5, -1.0]))
+    dtype = wl.BF16 if rng.random() < 0.7 else wl.F16
+    H = G * Hkv
+    layer = wl.LayerSpec(H, Hkv, 256, bs, 0, dtype, wl.fp32(scale), alibi_slopes=wl.alibi_slopes_geometric(H),
+                         sliding_window=window, logits_soft_cap=wl.fp32(cap), kv_cache_dtype="fp8_e4m3",
+                         k_scale=wl.fp32(0.02), v_scale=wl.fp32(0.015))
+    prefill = [(int(rng.integers(0, 400)), int(rng.integers(1, 150))) for _ in range(int(rng.integers(1, 6)))]
+    print(f"head-256 fp8 ALiBi case {seed}: {H}/{Hkv} heads bs={bs} {dtype} cap={cap} window={window} "
+          f"scale={scale:.4f}; prefill {prefill}", flush=True)
+    batch = wl.make_batch(layer, seed=seed, prefill=prefill, decode=[], device=gh.device())
+    cache, pre, _ = gh.gpu_run(batch)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8)), "cache differs"
+    gh.assert_close(gh.to_f64(pre), gh.oracle_prefill(batch, pool), batch.layer, f"head-256 fp8 case {seed}")
