@@ -270,6 +270,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // FP8 cache: cached K rows sit in the tile as exact code values (k_scale not applied); the
     // score FMA (or the soft-cap's input scale) of a cached key multiplies by k_scale as well.
     const float qk_scale_c = C8 ? qk_scale * p.k_scale : qk_scale;     // cached keys
+    // FP8 cache up to head size 128 (EXACT_V): cached V rows sit in the tile as exact code values
+    // too; a cached key's weight carries v_scale instead (log2 v_scale joins its exponent, so the
+    // weight is rounded once, as any weight is) and its row-sum share, kept apart, is divided by
+    // v_scale at the end.  At head size 256 V rows are staged as code * v_scale rounded to the
+    // element type: there this form came out of the compiler wrong with ALiBi and a soft-cap (its
+    // outputs differed from the identical arithmetic of the rounded form even with no cached key).
+    constexpr bool EXACT_V = C8 && D <= 128;
+    const float lvs = EXACT_V ? __log2f(p.v_scale) : 0.f;
     // PRE multipliers of new and cached keys (with start values and a zero scale, 1: Q is zero)
     const float mul_n = KB_INIT && qk_scale == 0.f ? 1.f : qk_scale;
     const float mul_c = qk_scale_c;
@@ -432,17 +440,24 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                     const int rr = wrow0 + r;
 #pragma unroll
                     for (int o = 0; o < 2; ++o) {
-                        // K codes exactly (every E4M3 value is a 16-bit value), V as code * v_scale
-                        // rounded to the element type
-                        const float sc = o ? p.v_scale : 1.f;
-                        const uint32_t cw[4] = {raw8[o][j].x, raw8[o][j].y, raw8[o][j].z, raw8[o][j].w};
+                        // K codes exactly (every E4M3 value is a 16-bit value); V likewise, or
+                        // (head size 256) as code * v_scale rounded to the element type
                         uint32_t w[8];
+                        if constexpr (EXACT_V) {
+                            const uint4 w0 = widen_e4m3<T>(make_uint2(raw8[o][j].x, raw8[o][j].y));
+                            const uint4 w1 = widen_e4m3<T>(make_uint2(raw8[o][j].z, raw8[o][j].w));
+                            w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+                            w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+                        } else {
+                            const float sc = o ? p.v_scale : 1.f;
+                            const uint32_t cw[4] = {raw8[o][j].x, raw8[o][j].y, raw8[o][j].z, raw8[o][j].w};
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw[q]), false);
-                            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw[q]), true);
-                            w[2 * q] = pack_x2<T>(lo[0] * sc, lo[1] * sc);
-                            w[2 * q + 1] = pack_x2<T>(hi[0] * sc, hi[1] * sc);
+                            for (int q = 0; q < 4; ++q) {
+                                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw[q]), false);
+                                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw[q]), true);
+                                w[2 * q] = pack_x2<T>(lo[0] * sc, lo[1] * sc);
+                                w[2 * q + 1] = pack_x2<T>(hi[0] * sc, hi[1] * sc);
+                            }
                         }
                         int off0, off1;
                         if (o == 0) {
@@ -637,10 +652,11 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     floatx4_v o[2][DB];
     // Row sums of the rounded weights, accumulated by the MFMA unit: an all-ones block times P^T
     // gives sum_k P[q][k] in every element of lane (q, .).
-    floatx4_v lsum[2];
+    floatx4_v lsum[2], lsum_c[2];        // lsum_c (EXACT_V): cached keys (weights times v_scale)
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
         lsum[qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+        lsum_c[qbk] = floatx4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qbk][db] = floatx4_v{0.f, 0.f, 0.f, 0.f};
     }
@@ -683,6 +699,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             return;
         }
         const bool full = k0h + 31 <= p0 && (p.window <= 0 || k0h > p0 + 31 - p.window);
+        // FP8 cache (EXACT_V): the half's keys are all cached (c_half), all new (n_half) or both
+        bool c_half = false, n_half = true;
+        if constexpr (EXACT_V) {
+            c_half = k0h + 31 < si.c;
+            n_half = k0h >= si.c;
+        }
 
         // ---- S^T = K Q^T (+ ALiBi term): s[kk][qbk] holds keys k0h + 16 kk + 4 lg + i of row 16 qbk + l16
         // crow: the ALiBi term of the half's first key for the row (base 2), a per-row constant
@@ -711,34 +733,66 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         if constexpr (PRE) {
             // s = m (dot + b_key / m) + (c_row - m_fin): the base-2 logit relative to the running
             // max's finite stand-in (FP8 cache: s = m dot + (c_row - m_fin + b_key), m times
-            // k_scale for a cached key).  The multiplier is uniform over the half unless an FP8 half
-            // holds both cached and new keys.
-            float mul = mul_n;
-            bool mixed = false;
-            if constexpr (C8) {
-                if (k0h + 31 < si.c) mul = mul_c;
-                else mixed = k0h < si.c;
-            }
-            if (!mixed) {
+            // k_scale, and with EXACT_V log2 v_scale added, for a cached key).  The multiplier is
+            // uniform over the half unless an FP8 half holds both cached and new keys.
+            if constexpr (EXACT_V) {
+                const bool mixed = !c_half && !n_half;
+                if (!mixed) {
+                    const float mul = c_half ? mul_c : mul_n;
+                    float a0[2];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
+                    for (int qbk = 0; qbk < 2; ++qbk)
+                        a0[qbk] = c_half ? crow[qbk] - m_fin[qbk] + lvs : crow[qbk] - m_fin[qbk];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                        for (int qbk = 0; qbk < 2; ++qbk)
-                            s[kk][qbk][i] = fmaf(s[kk][qbk][i], mul,
-                                                 C8 && ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] : crow[qbk] - m_fin[qbk]);
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int qbk = 0; qbk < 2; ++qbk)
+                                s[kk][qbk][i] = fmaf(s[kk][qbk][i], mul, ALIBI ? a0[qbk] + kbias[kk][i] : a0[qbk]);
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const bool cached = k0h + 16 * kk + 4 * lg + i < si.c;
+                            const float mk = cached ? mul_c : mul_n;
+                            const float lk = cached ? lvs : 0.f;
+#pragma unroll
+                            for (int qbk = 0; qbk < 2; ++qbk)
+                                s[kk][qbk][i] = fmaf(s[kk][qbk][i], mk,
+                                                     ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] + lk
+                                                           : crow[qbk] - m_fin[qbk] + lk);
+                        }
+                }
             } else {
+                float mul = mul_n;
+                bool mixed = false;
+                if constexpr (C8) {
+                    if (k0h + 31 < si.c) mul = mul_c;
+                    else mixed = k0h < si.c;
+                }
+                if (!mixed) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
+                    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float mk = k0h + 16 * kk + 4 * lg + i < si.c ? mul_c : mul_n;
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int qbk = 0; qbk < 2; ++qbk)
-                            s[kk][qbk][i] = fmaf(s[kk][qbk][i], mk,
-                                                 ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] : crow[qbk] - m_fin[qbk]);
-                    }
+                            for (int qbk = 0; qbk < 2; ++qbk)
+                                s[kk][qbk][i] = fmaf(s[kk][qbk][i], mul,
+                                                     C8 && ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] : crow[qbk] - m_fin[qbk]);
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float mk = k0h + 16 * kk + 4 * lg + i < si.c ? mul_c : mul_n;
+#pragma unroll
+                            for (int qbk = 0; qbk < 2; ++qbk)
+                                s[kk][qbk][i] = fmaf(s[kk][qbk][i], mk,
+                                                     ALIBI ? crow[qbk] - m_fin[qbk] + kbias[kk][i] : crow[qbk] - m_fin[qbk]);
+                        }
+                }
             }
         }
         if constexpr (SOFTCAP) {
@@ -746,11 +800,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // FP8 cache: cached keys' raw products carry the codes, so their cap input takes k_scale
-                    const float cin = C8 && k0h + 16 * kk + 4 * lg + i < si.c ? cap_in * p.k_scale : cap_in;
+                    // FP8 cache: cached keys' raw products carry the codes, so their cap input takes
+                    // k_scale, and their exponent log2 v_scale
+                    const bool cached = C8 && k0h + 16 * kk + 4 * lg + i < si.c;
+                    const float cin = cached ? cap_in * p.k_scale : cap_in;
+                    const float kb = EXACT_V ? kbias[kk][i] + (cached ? lvs : 0.f) : kbias[kk][i];
 #pragma unroll
                     for (int qbk = 0; qbk < 2; ++qbk)
-                        s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cin), kbias[kk][i]);
+                        s[kk][qbk][i] = fmaf(cap2, tanh_fast(s[kk][qbk][i] * cin), kb);
                 }
         }
 
@@ -813,6 +870,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
                 m_run[qbk] = m_new;
                 m_fin[qbk] = fin;
                 lsum[qbk] *= alpha;
+                if constexpr (EXACT_V) lsum_c[qbk] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[qbk][db] *= alpha;
             }
@@ -846,9 +904,30 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
             for (int qbk = 0; qbk < 2; ++qbk)
                 o[qbk][db] = mfma16(vop[db], pb[qbk], o[qbk][db]);
+        if constexpr (EXACT_V) {
+            // cached keys' weights carry v_scale: their sums go to lsum_c.  Operand slot j holds
+            // key k0h + 4 lg + j (j < 4) or k0h + 16 + 4 lg + j - 4.  Both sums are formed for every
+            // half (all-ones or all-zero operands unless the half holds both kinds): a branch around
+            // the row-sum MFMAs makes the compiler spill their accumulators.
+            const int xc = si.c - k0h - 4 * lg;        // slot offsets below xc are cached keys
+            const uint32_t one = one2 & 0xffffu;
+            uint32_t wc[4];
 #pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk)
-            lsum[qbk] = mfma16(ones, pb[qbk], lsum[qbk]);
+            for (int w = 0; w < 4; ++w) {
+                const int off = 16 * (w >> 1) + 2 * (w & 1);
+                wc[w] = (off < xc ? one : 0u) | (off + 1 < xc ? one << 16 : 0u);
+            }
+            const V8 ones_c = __builtin_bit_cast(V8, make_uint4(wc[0], wc[1], wc[2], wc[3]));
+            const V8 ones_n = __builtin_bit_cast(V8, make_uint4(one2 ^ wc[0], one2 ^ wc[1], one2 ^ wc[2], one2 ^ wc[3]));
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk) {
+                lsum_c[qbk] = mfma16(ones_c, pb[qbk], lsum_c[qbk]);
+                lsum[qbk] = mfma16(ones_n, pb[qbk], lsum[qbk]);
+            }
+        } else {
+#pragma unroll
+            for (int qbk = 0; qbk < 2; ++qbk) lsum[qbk] = mfma16(ones, pb[qbk], lsum[qbk]);
+        }
     };
     // Tile kt from stage (ks, vs), second half first; the first half's K operands are read here.
     auto compute_tile = [&](int kt, const bf16_t *ks, const bf16_t *vs) __attribute__((always_inline)) {
@@ -925,7 +1004,8 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
         if (trow < si.n) {
             // a sink logit joins the row sum only (m_run is finite: the diagonal key is visible)
             const float sink = p.sinks ? fast_exp2(p.sinks[h] * kLog2e - m_run[qbk]) : 0.f;
-            const float inv = 1.f / (lsum[qbk][0] + sink);
+            const float l = EXACT_V ? lsum[qbk][0] + lsum_c[qbk][0] / p.v_scale : lsum[qbk][0];
+            const float inv = 1.f / (l + sink);
             bf16_t *orow = reinterpret_cast<bf16_t *>(p.out) + int64_t(si.start + trow) * p.num_heads * D +
                            int64_t(h) * D + 4 * lg;
 #pragma unroll
