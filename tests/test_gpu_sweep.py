@@ -16,7 +16,7 @@ import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-CASES = 160
+CASES = 400
 
 
 def _case(seed: int):
