@@ -397,8 +397,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // path, which copies bytes unchanged.  Each lane instead loads 16 codes of a row (one 16-byte
     // load per slot, slot s = lane + 64 j: tile row 16 w + s / (D / 16), codes 16 (s % (D / 16)) ..
     // + 15) for K and for V when the tile's copies are issued, and a tile later, when they have
-    // long arrived, turns them into code * scale in the element type and writes them into the
-    // same swizzled places the copies would have filled.  New-token rows still use the copies.
+    // long arrived, turns them into 16-bit values (the codes exactly; V at head size 256 as
+    // code * v_scale) and writes them into the same swizzled places the copies would have filled.
+    // New-token rows still use the copies.
     // Rows past key_hi (the last key any row of the workgroup sees) stand in for the row key_hi in
     // the copies; when that row is cached (always so in the uniform multi-token mode, where every
     // key is cached) no copy fills them, so their codes are zeros here: masked keys then meet
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     // FP8 cache: cached keys' raw products carry the codes, so their cap input takes
-                    // k_scale, and their exponent log2 v_scale
+                    // k_scale, and (EXACT_V) their exponent log2 v_scale
                     const bool cached = C8 && k0h + 16 * kk + 4 * lg + i < si.c;
                     const float cin = cached ? cap_in * p.k_scale : cap_in;
                     const float kb = EXACT_V ? kbias[kk][i] + (cached ? lvs : 0.f) : kbias[kk][i];
