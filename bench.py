@@ -26,7 +26,8 @@ Prints ONE JSON line:
                 GB/s to and from pinned host memory (--no-block-moves skips them); and, also outside
                 the timed steps, decode and prefill over an FP8 (E4M3) copy of the cache (--no-fp8);
                 and prefill on long prompts (4 x 8192 new tokens, workload 2's head geometry), where
-                per-workgroup fixed costs are amortized (--no-long-prefill); and the cache write with
+                per-workgroup fixed costs are amortized, with an fp32 prefill batch against the fp32
+                matrix-unit peak (--no-long-prefill skips both); and the cache write with
                 a cold Infinity Cache (512 MB written just before each timed call)
   roofline      the dominant call (decode, HBM-bound): achieved GB/s per launch vs 8 TB/s;
                 traffic = HBM bytes per call measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
@@ -58,6 +59,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SOURCES = ("paged_kv_cache_242_amd/csrc/decode.hip", "paged_kv_cache_242_amd/csrc/pa_device.h")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 
 
 def log(*a):
@@ -284,19 +286,19 @@ def cold_cache_write_leg(pa, batch, cache, slots, layer, dev, reps: int = 10):
     return {"ms": ms, "GB_per_s": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "flush_bytes": 512 << 20}
 
 
-def long_prefill_leg(pa, dev, reps: int = 5):
-    """Outside the timed steps: causal prefill of 4 prompts of 8192 tokens with no cached context
-    (32 query / 8 KV heads, head size 128, block size 16, bf16, seed 12).  Each wavefront then
-    walks ~128 key tiles instead of the ~5-15 of the configured prompts."""
-    lay = wl.LayerSpec(32, 8, 128, 16, 0, wl.BF16, wl.fp32(1.0 / np.sqrt(128)))
-    batch = wl.make_batch(lay, seed=12, prefill=[(0, 8192)] * 4, device=dev)
+def _prefill_leg(pa, dev, lay, prefill, seed, reps: int = 5):
+    """Median time and rate of one prefill call on a seeded batch (outside the timed steps)."""
+    batch = wl.make_batch(lay, seed=seed, prefill=prefill, device=dev)
     L = batch.layer
     layer = pa.Layer(L.num_heads, L.num_kv_heads, L.head_size, L.block_size, L.num_blocks, L.torch_dtype, L.scale,
                      None, 0)
     cache = torch.zeros((2, L.num_blocks, L.block_size * L.row_elems), dtype=L.torch_dtype, device=dev)
+    if batch.ctx_key.shape[0]:
+        pa.cache_write(batch.ctx_key, batch.ctx_value, cache, torch.as_tensor(batch.ctx_slots, device=dev), layer)
     i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
     args = (batch.query, batch.key, batch.value, cache, i32(batch.prefill_block_tables),
-            i32(batch.prefill_context_lens), i32(batch.prefill_cu), layer, int(batch.prefill_query_lens.max()), 0)
+            i32(batch.prefill_context_lens), i32(batch.prefill_cu), layer, int(batch.prefill_query_lens.max()),
+            int(batch.prefill_context_lens.max()))
     out = torch.empty_like(batch.query)
     for _ in range(2):
         pa.prefill_varlen(*args, out=out)
@@ -311,11 +313,32 @@ def long_prefill_leg(pa, dev, reps: int = 5):
         ts.append(e0.elapsed_time(e1))
     flops = prefill_flops(batch)
     ms = float(np.median(ts))
-    tflops = flops / (ms * 1e-3) / 1e12
     del batch, cache, out
     torch.cuda.empty_cache()
+    return ms, flops
+
+
+def long_prefill_leg(pa, dev, reps: int = 5):
+    """Outside the timed steps: causal prefill of 4 prompts of 8192 tokens with no cached context
+    (32 query / 8 KV heads, head size 128, block size 16, bf16, seed 12).  Each wavefront then
+    walks ~128 key tiles instead of the ~5-15 of the configured prompts."""
+    lay = wl.LayerSpec(32, 8, 128, 16, 0, wl.BF16, wl.fp32(1.0 / np.sqrt(128)))
+    ms, flops = _prefill_leg(pa, dev, lay, [(0, 8192)] * 4, 12, reps)
+    tflops = flops / (ms * 1e-3) / 1e12
     return {"shape": "4 x 8192 new tokens, H=32, Hkv=8, D=128, bs=16, causal, no context", "ms": ms,
             "gflop_per_call": flops / 1e9, "TFLOP_per_s": tflops, "frac_mfma_peak": tflops / MFMA_BF16_PEAK_TFLOPS}
+
+
+def f32_prefill_leg(pa, dev, reps: int = 5):
+    """Outside the timed steps: the fp32 prefill kernel on 2 prompts of 1024 tokens and 2 chunks of
+    256 rows on 2000-token contexts (32 query / 8 KV heads, head size 128, block size 16, seed 7),
+    against the fp32 matrix-unit peak."""
+    lay = wl.LayerSpec(32, 8, 128, 16, 0, wl.F32, wl.fp32(1.0 / np.sqrt(128)))
+    ms, flops = _prefill_leg(pa, dev, lay, [(0, 1024)] * 2 + [(2000, 256)] * 2, 7, reps)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"shape": "fp32: 2 x 1024 new tokens + 2 x 256 rows on 2000-token contexts, H=32, Hkv=8, D=128, bs=16",
+            "ms": ms, "gflop_per_call": flops / 1e9, "TFLOP_per_s": tflops,
+            "frac_f32_mfma_peak": tflops / MFMA_F32_PEAK_TFLOPS}
 
 
 def fp8_cache_leg(pa, L, layer, cache, dev, dec_args, pre_args, reps: int = 10):
@@ -591,6 +614,7 @@ def main(argv=None):
             if R.has_pre else None)
     if not args.no_long_prefill and L.dtype != wl.F32:
         secondary["prefill_long_prompts"] = long_prefill_leg(pa, dev)
+        secondary["prefill_fp32"] = f32_prefill_leg(pa, dev)
 
     value, unit = None, "GB/s"
     if R.has_dec:
