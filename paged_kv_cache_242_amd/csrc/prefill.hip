@@ -1046,8 +1046,14 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(
     constexpr int CPR = D / 4;                              // float4 chunks per row
     constexpr int KPP = kThreads / CPR;                     // key rows per copy pass
     constexpr int PASSES = kF32Keys / KPP;
-    __shared__ __attribute__((aligned(16))) float ks[kF32Keys * LD];
-    __shared__ __attribute__((aligned(16))) float vs[kF32Keys * LD];
+    // Up to head size 128 the next tile is fetched into registers during the compute and the LDS
+    // holds two stages (one barrier per tile); at 256 the registers are taken, and one stage is
+    // refilled after the compute.
+    constexpr bool PREFETCH = D <= 128;
+    constexpr int STAGES = PREFETCH ? 2 : 1;
+    constexpr int STAGE = kF32Keys * LD;                    // floats per stage
+    __shared__ __attribute__((aligned(16))) float ks[STAGES * STAGE];
+    __shared__ __attribute__((aligned(16))) float vs[STAGES * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -1105,12 +1111,12 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(
             vr[ps] = *reinterpret_cast<const float4 *>(vp + 4 * (tid % CPR));
         }
     };
-    auto commit = [&]() __attribute__((always_inline)) {
+    auto commit = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             const int r = tid / CPR + KPP * ps;
-            *reinterpret_cast<float4 *>(ks + r * LD + 4 * (tid % CPR)) = kr[ps];
-            *reinterpret_cast<float4 *>(vs + r * LD + 4 * (tid % CPR)) = vr[ps];
+            *reinterpret_cast<float4 *>(ks + st * STAGE + r * LD + 4 * (tid % CPR)) = kr[ps];
+            *reinterpret_cast<float4 *>(vs + st * STAGE + r * LD + 4 * (tid % CPR)) = vr[ps];
         }
     };
 
@@ -1121,7 +1127,9 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(
 #pragma unroll
         for (int b = 0; b < DB; ++b) o[qbk][b] = floatx4_v{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int kt) __attribute__((always_inline)) {
+    auto compute = [&](int kt, int st) __attribute__((always_inline)) {
+        const float *kst = ks + st * STAGE;
+        const float *vst = vs + st * STAGE;
         const int k0 = kt * kF32Keys;
         // tiles no row of this wavefront sees
         if (!active || k0 > wpos_hi || (p.window > 0 && k0 + kF32Keys - 1 <= wpos_lo - p.window)) return;
@@ -1135,7 +1143,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(
         for (int b = 0; b < DB; ++b) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const float4 kv = *reinterpret_cast<const float4 *>(ks + (16 * kk + l16) * LD + 16 * b + 4 * lg);
+                const float4 kv = *reinterpret_cast<const float4 *>(kst + (16 * kk + l16) * LD + 16 * b + 4 * lg);
                 const float ka[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -1187,7 +1195,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(
             for (int v = 0; v < 4; ++v) {
                 // (at head size 256 the V reads are held back to one key ahead: registers)
                 if constexpr (D > 128) __builtin_amdgcn_sched_barrier(0);
-                const float *vrow = vs + (16 * kk + 4 * lg + v) * LD + l16;
+                const float *vrow = vst + (16 * kk + 4 * lg + v) * LD + l16;
 #pragma unroll
                 for (int b = 0; b < DB; ++b) {
                     const float a = vrow[16 * b];
@@ -1198,20 +1206,28 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_f32_kernel(
             }
     };
 
-    // ---- pipeline: tile kt is computed from LDS while tile kt - 1 is fetched into registers (up
-    // to head size 128; at 256 the registers are taken and the fetch follows the compute)
-    constexpr bool PREFETCH = D <= 128;
+    // ---- pipeline.  Two stages: tile kt is computed from stage st while tile kt - 1 goes into the
+    // other one (last read by the previous tile's compute, which every wavefront finished before
+    // the previous barrier); one stage: the fetch and the refill follow the compute.
     fetch(kt_hi);
-    commit();
+    commit(0);
     __syncthreads();
+    int st = 0;
     for (int kt = kt_hi; kt >= kt_lo; --kt) {
-        if (PREFETCH && kt > kt_lo) fetch(kt - 1);
-        compute(kt);
-        __syncthreads();
-        if (kt > kt_lo) {
-            if (!PREFETCH) fetch(kt - 1);
-            commit();
+        if constexpr (PREFETCH) {
+            if (kt > kt_lo) fetch(kt - 1);
+            compute(kt, st);
+            if (kt > kt_lo) commit(st ^ 1);
             __syncthreads();
+            st ^= 1;
+        } else {
+            compute(kt, 0);
+            __syncthreads();
+            if (kt > kt_lo) {
+                fetch(kt - 1);
+                commit(0);
+                __syncthreads();
+            }
         }
     }
 
