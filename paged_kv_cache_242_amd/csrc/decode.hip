@@ -1296,10 +1296,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
     for (int k = 0; k < PER; ++k) store_out<T>(out_row + lane + 64 * k, num[k] * inv);
 }
 
-// KV heads per work unit: 2 for head groups of 1 or 2 (whole 512-byte runs of two adjacent head
-// rows per token instead of 256-byte slices), 4 for 16-bit head groups of 4 (1 KB runs: one token's
-// four head rows per load instruction, 2.8% faster than two on workload 3), when the KV head count
-// divides by it; never more than the rows of one load instruction.
+// KV heads per work unit: 2 for head groups of 1, 2 or 8 (whole 512-byte runs of two adjacent head
+// rows per token instead of 256-byte slices; 2.7% faster for the 8 virtual heads of workload 3's
+// two-row decode), 4 for 16-bit head groups of 4 (1 KB runs: one token's four head rows per load
+// instruction, 1.3-2.8% faster than two on workload 3), when the KV head count divides by it;
+// never more than the rows of one load instruction.
 #ifndef PA_DECODE_KVH_S
 #define PA_DECODE_KVH_S 2
 #endif
@@ -1310,7 +1311,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
 #define PA_DECODE_KVH_M8 2
 #endif
 #ifndef PA_DECODE_KVH_B
-#define PA_DECODE_KVH_B 1
+#define PA_DECODE_KVH_B 2
 #endif
 template <typename T, int GP, int D>
 constexpr int kvh_max() {
