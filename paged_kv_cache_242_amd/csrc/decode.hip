@@ -1417,10 +1417,19 @@ hipError_t launch_mfma(const DecodeParams &p, const DecodeShape &s, hipStream_t 
     return hipGetLastError();
 }
 
+// KV heads per unit actually used: kvh_max when the KV head count divides by it, else 2 (when
+// kvh_max is 4 and the count is even), else 1.
+template <typename T, int GP, int D>
+constexpr int kvh_mid() { return kvh_max<T, GP, D>() >= 4 ? 2 : 1; }
+
 template <typename T, int D, int GP>
 hipError_t launch_kvh(const DecodeParams &p, const DecodeShape &s, hipStream_t stream) {
-    if constexpr (kvh_max<T, GP, D>() > 1) {
-        if (s.kvh == kvh_max<T, GP, D>()) return launch_typed<T, D, GP, kvh_max<T, GP, D>()>(p, s, stream);
+    constexpr int K1 = kvh_max<T, GP, D>(), K2 = kvh_mid<T, GP, D>();
+    if constexpr (K1 > 1) {
+        if (s.kvh == K1) return launch_typed<T, D, GP, K1>(p, s, stream);
+    }
+    if constexpr (K2 > 1) {
+        if (s.kvh == K2) return launch_typed<T, D, GP, K2>(p, s, stream);
     }
     return launch_typed<T, D, GP, 1>(p, s, stream);
 }
@@ -1438,11 +1447,17 @@ hipError_t launch_group(const DecodeParams &p, const DecodeShape &s, int padded_
 
 template <typename T, int D, int GP>
 void instance_info_gp(int num_kv_heads, int block_shift, int &kvh, int &tile, int &waves) {
-    kvh = (kvh_max<T, GP, D>() > 1 && num_kv_heads % kvh_max<T, GP, D>() == 0) ? kvh_max<T, GP, D>() : 1;
-    if (kvh > 1) {
-        tile = tile_keys<T, D, GP, kvh_max<T, GP, D>()>();
-        waves = split_waves<T, D, GP, kvh_max<T, GP, D>()>(block_shift);
+    constexpr int K1 = kvh_max<T, GP, D>(), K2 = kvh_mid<T, GP, D>();
+    if (K1 > 1 && num_kv_heads % K1 == 0) {
+        kvh = K1;
+        tile = tile_keys<T, D, GP, K1>();
+        waves = split_waves<T, D, GP, K1>(block_shift);
+    } else if (K2 > 1 && num_kv_heads % K2 == 0) {
+        kvh = K2;
+        tile = tile_keys<T, D, GP, K2>();
+        waves = split_waves<T, D, GP, K2>(block_shift);
     } else {
+        kvh = 1;
         tile = tile_keys<T, D, GP, 1>();
         waves = split_waves<T, D, GP, 1>(block_shift);
     }

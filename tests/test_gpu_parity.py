@@ -221,6 +221,13 @@ DECODE_LAYERS = [
     _layer(8, 8, 256, 16, wl.F16, alibi=True, window=300),
     _layer(16, 4, 256, 32, fp8=True, softcap=30.0, scale=0.15),
     _layer(4, 2, 256, 16, wl.F32, sinks=True),
+    # KV heads per work unit: 4 (groups of 4, KV heads divisible by 4), 2 (groups of 4 over 2 or 6 KV
+    # heads; groups of 8 over an even count), 1 (an odd KV head count)
+    _layer(16, 4, 128, 16, alibi=True),
+    _layer(24, 6, 128, 16, window=700),
+    _layer(12, 3, 128, 32),
+    _layer(16, 2, 128, 16, wl.F16, sinks=True),
+    _layer(24, 3, 128, 16),
 ]
 DECODE_LENS = [1, 2, 31, 32, 33, 127, 129, 511, 512, 513, 1000, 1025, 2049, 0, 4100]
 
