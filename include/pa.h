@@ -168,9 +168,11 @@ size_t pa_decode_workspace_size(const pa_layer *layer, int32_t num_seqs, int32_t
  *                    and to max_blocks_per_seq * block_size)
  *   workspace        device scratch of pa_decode_workspace_size() bytes, 256-byte aligned,
  *                    overwritten; calls that share one workspace must not overlap
- * The key tiles of all (sequence, KV head) pairs are split evenly over as many wavefronts as
- * the device holds at once (each wavefront finds its share from seq_lens on the device; above
- * 2048 sequences a small planning kernel does it first); a pair cut between wavefronts leaves
+ * The key tiles of all (sequence, KV head group) pairs are split evenly over as many wavefronts
+ * as the device holds at once; a group is one KV head, or (VALU path, 16-bit or FP8 cache) 2 or
+ * 4 adjacent KV heads read as one run per token where that count divides num_kv_heads and the
+ * rows fit the wavefront's registers.  Each wavefront finds its share from seq_lens on the
+ * device (above 2048 sequences a small planning kernel does it first); a pair cut between wavefronts leaves
  * (max, sum, weighted-V) partials that a second kernel merges with the log-sum-exp rule.  The
  * dot products run on the VALU, or on the matrix unit at head size 128 (block size >= 16) with
  * an FP8 cache and 5 to 32 query heads per KV head, or 9 to 32 query heads per KV head.
