@@ -38,8 +38,8 @@
  * Numerics: products and softmax in fp32; for bf16 and fp16 layers the softmax weights are
  * rounded to the element type (nearest even) before they multiply V, and outputs are rounded to
  * nearest even.  Over an fp8 cache the codes enter the products exactly and the scales are
- * applied in fp32, except in prefill at head size 256, where cached V rows are staged as
- * code * v_scale rounded to the element type.
+ * applied in fp32, except in prefill at head size 256 with both ALiBi and a soft-cap, where
+ * cached V rows are staged as code * v_scale rounded to the element type.
  *
  * Errors: every entry point returns a pa_status and launches nothing when it fails.  Only
  * host-visible scalars and pointers are validated.  Device contents (slots, block ids,

@@ -270,13 +270,13 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // FP8 cache: cached K rows sit in the tile as exact code values (k_scale not applied); the
     // score FMA (or the soft-cap's input scale) of a cached key multiplies by k_scale as well.
     const float qk_scale_c = C8 ? qk_scale * p.k_scale : qk_scale;     // cached keys
-    // FP8 cache up to head size 128 (EXACT_V): cached V rows sit in the tile as exact code values
-    // too; a cached key's weight carries v_scale instead (log2 v_scale joins its exponent, so the
-    // weight is rounded once, as any weight is) and its row-sum share, kept apart, is divided by
-    // v_scale at the end.  At head size 256 V rows are staged as code * v_scale rounded to the
-    // element type: there this form came out of the compiler wrong with ALiBi and a soft-cap (its
-    // outputs differed from the identical arithmetic of the rounded form even with no cached key).
-    constexpr bool EXACT_V = C8 && D <= 128;
+    // FP8 cache (EXACT_V): cached V rows sit in the tile as exact code values too; a cached key's
+    // weight carries v_scale instead (log2 v_scale joins its exponent, so the weight is rounded
+    // once, as any weight is) and its row-sum share, kept apart, is divided by v_scale at the end.
+    // At head size 256 with both ALiBi and a soft-cap, V rows are staged as code * v_scale rounded
+    // to the element type: there this form came out of the compiler wrong (its outputs differed
+    // from the identical arithmetic of the rounded form even with no cached key).
+    constexpr bool EXACT_V = C8 && (D <= 128 || !(ALIBI && SOFTCAP));
     const float lvs = EXACT_V ? __log2f(p.v_scale) : 0.f;
     // PRE multipliers of new and cached keys (with start values and a zero scale, 1: Q is zero)
     const float mul_n = KB_INIT && qk_scale == 0.f ? 1.f : qk_scale;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
     // path, which copies bytes unchanged.  Each lane instead loads 16 codes of a row (one 16-byte
     // load per slot, slot s = lane + 64 j: tile row 16 w + s / (D / 16), codes 16 (s % (D / 16)) ..
     // + 15) for K and for V when the tile's copies are issued, and a tile later, when they have
-    // long arrived, turns them into 16-bit values (the codes exactly; V at head size 256 as
+    // long arrived, turns them into 16-bit values (the codes exactly; V without EXACT_V as
     // code * v_scale) and writes them into the same swizzled places the copies would have filled.
     // New-token rows still use the copies.
     // Rows past key_hi (the last key any row of the workgroup sees) stand in for the row key_hi in
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kThreads, D > 128 ? 1 : 2) void prefill_mfma_kernel
 #pragma unroll
                     for (int o = 0; o < 2; ++o) {
                         // K codes exactly (every E4M3 value is a 16-bit value); V likewise, or
-                        // (head size 256) as code * v_scale rounded to the element type
+                        // (without EXACT_V) as code * v_scale rounded to the element type
                         uint32_t w[8];
                         if constexpr (EXACT_V) {
                             const uint4 w0 = widen_e4m3<T>(make_uint2(raw8[o][j].x, raw8[o][j].y));

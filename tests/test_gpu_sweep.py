@@ -115,3 +115,41 @@ def test_head256_fp8_alibi_prefill(seed):
     pool = gh.oracle_pool(batch)
     assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8)), "cache differs"
     gh.assert_close(gh.to_f64(pre), gh.oracle_prefill(batch, pool), batch.layer, f"head-256 fp8 case {seed}")
+
+
+# Head size 256 over an fp8 cache at 2.5 times the default logit scale, with many short contexts:
+# the cases where staging V as code * v_scale rounded to bf16 had pushed outputs near 4 past the
+# bf16 bound, and which exact V codes keep inside it.  ALiBi with a soft-cap still stages rounded V
+# at this head size, so those draws run without the cap here (that pair is covered above).
+HEAD256_EXACT_V_SEEDS = list(range(32)) + [147, 248]
+
+
+@pytest.mark.parametrize("seed", HEAD256_EXACT_V_SEEDS)
+def test_head256_fp8_exact_v_prefill(seed):
+    rng = np.random.default_rng([seed, 2561])
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    Hkv = int(rng.choice([1, 2]))
+    bs = int(rng.choice([8, 16, 32]))
+    cap = float(rng.choice([0.0, 0.0, 5.0, 30.0]))
+    alibi = rng.random() < 0.5
+    if alibi:
+        cap = 0.0
+    window = int(rng.integers(1, 500)) if rng.random() < 0.3 else 0
+    scale = (1.0 / 16.0) * float(rng.choice([1.0, 2.5, 2.5, -1.0]))
+    dtype = wl.BF16 if rng.random() < 0.7 else wl.F16
+    H = G * Hkv
+    layer = wl.LayerSpec(H, Hkv, 256, bs, 0, dtype, wl.fp32(scale),
+                         alibi_slopes=wl.alibi_slopes_geometric(H) if alibi else None, sliding_window=window,
+                         logits_soft_cap=wl.fp32(cap), kv_cache_dtype="fp8_e4m3", k_scale=wl.fp32(0.02),
+                         v_scale=wl.fp32(0.015))
+    n = int(rng.integers(1, 40))
+    ctx_max = int(rng.choice([25, 400]))
+    prefill = [(int(rng.integers(0, ctx_max)), int(rng.integers(1, 60))) for _ in range(n)]
+    print(f"head-256 fp8 exact-V case {seed}: {H}/{Hkv} heads bs={bs} {dtype} alibi={alibi} cap={cap} "
+          f"window={window} scale={scale:.4f}; prefill {prefill}", flush=True)
+    batch = wl.make_batch(layer, seed=seed, prefill=prefill, decode=[], device=gh.device())
+    cache, pre, _ = gh.gpu_run(batch)
+    torch.cuda.synchronize()
+    pool = gh.oracle_pool(batch)
+    assert np.array_equal(wl.host_bits(cache).view(np.uint8), pool.view(np.uint8)), "cache differs"
+    gh.assert_close(gh.to_f64(pre), gh.oracle_prefill(batch, pool), batch.layer, f"head-256 fp8 exact-V case {seed}")
