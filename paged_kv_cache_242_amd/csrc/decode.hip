@@ -1297,9 +1297,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p, Decode
 }
 
 // KV heads per work unit: 2 for head groups of 1, 2 or 8 (whole 512-byte runs of two adjacent head
-// rows per token instead of 256-byte slices; 2.7% faster for the 8 virtual heads of workload 3's
-// two-row decode), 4 for 16-bit head groups of 4 (1 KB runs: one token's four head rows per load
-// instruction, 1.3-2.8% faster than two on workload 3), when the KV head count divides by it;
+// rows per token instead of 256-byte slices; 2.7% faster for the 8 virtual heads of a two-row
+// decode over 256 bf16 sequences of 512-8192 tokens with 32/8 heads), 4 for 16-bit head groups of 4
+// (1 KB runs: one token's four head rows per load instruction, 1.3-2.8% faster than two on that
+// single-row decode), when the KV head count divides by it;
 // never more than the rows of one load instruction.
 #ifndef PA_DECODE_KVH_S
 #define PA_DECODE_KVH_S 2
